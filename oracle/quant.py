@@ -1,0 +1,175 @@
+"""Oracle: rotate -> clip -> INT2 quantise -> pack (test infrastructure only).
+
+Follows the demotion step of the serving pipeline in [ZAKER]: the oldest
+recent token is rotated, clipped, quantised and packed, four 2-bit values per
+byte, and moved into INT2 history.  The step order matches [CSDN] 3.1
+("multiply by R, clip, INT2-quantise, store").  The rotation and the
+per-layer threshold come from [GIST] 2.2A.  The scale/zero-point form is the
+one [ZAKER] names for dequantisation.
+
+Readings where the pages leave the step open:
+
+* rotation convention: row vectors, y = x R;
+* quantisation group: the d channels of one (token, KV head);
+* clipping: symmetric clamp to [-tau, tau] before the group min/max;
+* quantiser: asymmetric min-max with zero = fp16(min) and
+  scale = fp16((max - min) / 3), code = clamp(rint((y - zero) / scale), 0, 3),
+  round half to even, dequantised as zero + code * scale;
+* degenerate group (scale rounds to 0): all codes 0;
+* pack order: byte i of a token's row holds channels 4i..4i+3, with channel
+  4i+j in bits 2j..2j+1;
+* in-page layout (64-token pages, one block per (page, KV head)):
+  K codes are 4 planes; plane p holds bytes [p*d/16, (p+1)*d/16) of every
+  token's row, token-major.  V codes are byte-column-major: byte i of token o
+  sits at i*64 + o.  scale/zero are fp16 pairs (scale, zero) per token.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+PAGE = 64
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns -> float64 (exact)."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def f16_bits_to_f64(bits) -> np.ndarray:
+    """IEEE fp16 bit patterns -> float64 (exact)."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def rotate_round_f32(x_bits: np.ndarray, rot: np.ndarray) -> np.ndarray:
+    """y = x R for row vectors, accumulated in float64 and rounded once to
+    float32.  x_bits: bf16 [..., d]; rot: fp32 [d, d]."""
+    return (bf16_to_f64(x_bits) @ np.asarray(rot, dtype=np.float32).astype(np.float64)).astype(np.float32)
+
+
+def quantize_group(y: np.ndarray, clip):
+    """Clip and INT2-quantise the rows of y (float32 [n, d]); one group per row.
+
+    Returns (codes uint8 [n, d], scale16 uint16 [n], zero16 uint16 [n], info)
+    where info holds the float32 clipped values, group min/max and the fp32
+    value (max - min) / 3 before fp16 rounding, for the parity checker."""
+    y = np.asarray(y, dtype=np.float32)
+    tau = np.float32(clip)
+    yc = np.minimum(np.maximum(y, -tau), tau)
+    mn = yc.min(axis=1)
+    mx = yc.max(axis=1)
+    rng3 = (mx - mn) / np.float32(3.0)             # float32 subtract, float32 divide
+    zero16 = mn.astype(np.float16)                 # round to nearest even
+    scale16 = rng3.astype(np.float16)
+    z = zero16.astype(np.float32)[:, None]
+    s = scale16.astype(np.float32)[:, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = (yc - z) / s                           # float32 subtract, float32 divide
+        codes = np.clip(np.rint(t), 0.0, 3.0)
+    codes = np.where(s == 0, 0.0, codes).astype(np.uint8)
+    info = dict(yc=yc, mn=mn, mx=mx, range3=rng3)
+    return codes, scale16.view(np.uint16), zero16.view(np.uint16), info
+
+
+def pack_codes_row(codes: np.ndarray) -> np.ndarray:
+    """[..., d] codes in 0..3 -> [..., d/4] bytes, channel 4i+j in bits 2j."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::4] | (c[..., 1::4] << 2) | (c[..., 2::4] << 4) | (c[..., 3::4] << 6)).astype(np.uint8)
+
+
+def unpack_codes_row(row: np.ndarray) -> np.ndarray:
+    """Inverse of :func:`pack_codes_row`."""
+    r = np.asarray(row, dtype=np.uint8)
+    out = np.stack([(r >> (2 * j)) & 3 for j in range(4)], axis=-1)
+    return out.reshape(r.shape[:-1] + (r.shape[-1] * 4,)).astype(np.uint8)
+
+
+def page_block_bytes(d: int) -> int:
+    """Bytes of codes per (page, KV head)."""
+    return PAGE * d // 4
+
+
+def k_byte_offsets(offset, d: int) -> np.ndarray:
+    """Positions inside a (page, head) K block of the d/4 row bytes of the
+    token at page offset ``offset`` (scalar or array -> [..., d/4])."""
+    w = d // 16
+    i = np.arange(d // 4)
+    o = np.asarray(offset)[..., None]
+    return (i // w) * (PAGE * w) + o * w + (i % w)
+
+
+def v_byte_offsets(offset, d: int) -> np.ndarray:
+    """Positions inside a (page, head) V block of the d/4 row bytes of the
+    token at page offset ``offset`` (byte-column-major)."""
+    i = np.arange(d // 4)
+    o = np.asarray(offset)[..., None]
+    return i * PAGE + o
+
+
+def _offsets(kind: str, offset, d: int):
+    if kind == "k":
+        return k_byte_offsets(offset, d)
+    if kind == "v":
+        return v_byte_offsets(offset, d)
+    raise ValueError("kind must be 'k' or 'v'")
+
+
+def quantize_pack_ref(kind: str, x_bits: np.ndarray, rot: np.ndarray, clip, dst_slot: np.ndarray,
+                      codes_pool: np.ndarray, sz_pool: np.ndarray, src_idx: np.ndarray | None = None,
+                      chunk: int = 16384):
+    """Demote tokens of one tensor (K or V) of one layer into INT2 pages, in place.
+
+    x_bits   bf16 [n_src][n_kv][d]
+    rot      fp32 [n_kv][d][d]   (y = x R per head)
+    clip     tau > 0, finite, <= 65504
+    dst_slot int32 [n_tok]: physical page * 64 + offset; slots outside
+             [0, n_pages*64) are skipped
+    src_idx  int32 [n_tok] rows of x, or None for rows 0..n_tok-1; rows
+             outside [0, n_src) are skipped
+    codes_pool uint8 [n_pages][n_kv][64*d/4]; sz_pool uint16 [n_pages][n_kv][64][2]
+
+    Returns a dict of per-(token, head) diagnostics for the written tokens
+    (arrays [n_written][n_kv]...) used by the parity checker."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    n_src, n_kv, d = x_bits.shape
+    tau = np.float32(clip)
+    if not (np.isfinite(tau) and 0 < tau <= 65504):
+        raise ValueError("clip must be finite, > 0 and <= 65504")
+    if d % 16:
+        raise ValueError("head_dim must be a multiple of 16")
+    n_pages = codes_pool.shape[0]
+    dst = np.asarray(dst_slot, dtype=np.int64).ravel()
+    src = np.arange(dst.size) if src_idx is None else np.asarray(src_idx, dtype=np.int64).ravel()
+    if src.size != dst.size:
+        raise ValueError("src_idx and dst_slot lengths differ")
+    keep = (dst >= 0) & (dst < n_pages * PAGE) & (src >= 0) & (src < n_src)
+    dst, src = dst[keep], src[keep]
+    diag = {k: [] for k in ("slot", "yc", "mn", "mx", "range3", "codes", "scale16", "zero16")}
+    for c0 in range(0, dst.size, chunk):
+        dd, ss = dst[c0:c0 + chunk], src[c0:c0 + chunk]
+        page, off = dd // PAGE, dd % PAGE
+        pos = _offsets(kind, off, d)                         # [n, d/4]
+        yc_h, mn_h, mx_h, r3_h, cd_h, sc_h, zr_h = ([] for _ in range(7))
+        for g in range(n_kv):
+            y = rotate_round_f32(x_bits[ss, g, :], rot[g])
+            codes, s16, z16, info = quantize_group(y, tau)
+            codes_pool[page[:, None], g, pos] = pack_codes_row(codes)
+            sz_pool[page, g, off, 0] = s16
+            sz_pool[page, g, off, 1] = z16
+            yc_h.append(info["yc"]); mn_h.append(info["mn"]); mx_h.append(info["mx"])
+            r3_h.append(info["range3"]); cd_h.append(codes); sc_h.append(s16); zr_h.append(z16)
+        diag["slot"].append(dd)
+        diag["yc"].append(np.stack(yc_h, 1)); diag["mn"].append(np.stack(mn_h, 1))
+        diag["mx"].append(np.stack(mx_h, 1)); diag["range3"].append(np.stack(r3_h, 1))
+        diag["codes"].append(np.stack(cd_h, 1)); diag["scale16"].append(np.stack(sc_h, 1))
+        diag["zero16"].append(np.stack(zr_h, 1))
+    return {k: (np.concatenate(v) if v else np.zeros(0)) for k, v in diag.items()}
+
+
+def read_history_codes(kind: str, codes_pool: np.ndarray, sz_pool: np.ndarray, pages: np.ndarray,
+                       offsets: np.ndarray, g: int, d: int):
+    """Codes [n][d] and fp16 (scale, zero) bits [n] of the tokens at the given
+    (physical page, offset) pairs of KV head g."""
+    pos = _offsets(kind, offsets, d)
+    rows = codes_pool[np.asarray(pages)[:, None], g, pos]
+    return unpack_codes_row(rows), sz_pool[pages, g, offsets, 0], sz_pool[pages, g, offsets, 1]
