@@ -1,0 +1,129 @@
+// Internal helpers shared by the liboscar kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "oscar.h"
+
+namespace oscar {
+
+constexpr int kPage = OSCAR_PAGE_TOKENS;  // tokens per page
+constexpr int kWave = 64;                 // CDNA wavefront width
+constexpr int kBlock = 256;               // threads per block (4 waves)
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
+  return __half2float(__ushort_as_half(static_cast<unsigned short>(bits16)));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// exp2 that maps a -inf difference to 0 (empty partials carry m = -inf)
+__device__ __forceinline__ float exp2_or_zero(float m, float ref) {
+  return (m == -INFINITY) ? 0.0f : exp2f(m - ref);
+}
+
+// ---------------------------------------------------------------------------
+// decode plan: splits and workspace layout (host and device agree on it)
+// ---------------------------------------------------------------------------
+struct DecodePlan {
+  int hist_pages;    // ceil(max_hist_len / 64)
+  int splits;        // history splits per (request, KV head)
+  int pages_per_split;
+  int chunks;        // BF16 64-token chunks per (request, KV head)
+  int sink_chunks;   // the first sink_chunks chunks cover the sink window
+  size_t off_qrot, off_qsum, off_hpart, off_bpart, total;
+};
+
+constexpr int kTargetBlocks = 1024;  // history blocks per launch the split policy aims for
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline DecodePlan make_decode_plan(int B, int Hq, int n_kv, int d, int max_hist_len, int sink_cap,
+                                   int recent_cap) {
+  DecodePlan p{};
+  const int G = Hq / n_kv;
+  p.hist_pages = (max_hist_len + kPage - 1) / kPage;
+  if (p.hist_pages > 0) {
+    const long units = (long)(B > 0 ? B : 1) * n_kv;
+    long s0 = (kTargetBlocks + units - 1) / units;
+    if (s0 < 1) s0 = 1;
+    if (s0 > p.hist_pages) s0 = p.hist_pages;
+    p.pages_per_split = (int)((p.hist_pages + s0 - 1) / s0);
+    p.splits = (p.hist_pages + p.pages_per_split - 1) / p.pages_per_split;
+  }
+  p.sink_chunks = (sink_cap + kPage - 1) / kPage;
+  p.chunks = p.sink_chunks + (recent_cap + kPage - 1) / kPage;
+  const size_t part = (size_t)G * (d + 2) * sizeof(float);
+  size_t off = 0;
+  p.off_qrot = off;  off = align256(off + (size_t)B * Hq * d * sizeof(float));
+  p.off_qsum = off;  off = align256(off + (size_t)B * Hq * sizeof(float));
+  p.off_hpart = off; off = align256(off + (size_t)B * n_kv * p.splits * part);
+  p.off_bpart = off; off = align256(off + (size_t)B * n_kv * p.chunks * part);
+  p.total = off;
+  return p;
+}
+
+struct Bf16Plan {
+  int ctx_pages, splits, pages_per_split;
+  size_t off_part, total;
+};
+
+inline Bf16Plan make_bf16_plan(int B, int Hq, int n_kv, int d, int max_ctx_len) {
+  Bf16Plan p{};
+  const int G = Hq / n_kv;
+  p.ctx_pages = (max_ctx_len + kPage - 1) / kPage;
+  if (p.ctx_pages > 0) {
+    const long units = (long)(B > 0 ? B : 1) * n_kv;
+    long s0 = (kTargetBlocks + units - 1) / units;
+    if (s0 < 1) s0 = 1;
+    if (s0 > p.ctx_pages) s0 = p.ctx_pages;
+    p.pages_per_split = (int)((p.ctx_pages + s0 - 1) / s0);
+    p.splits = (p.ctx_pages + p.pages_per_split - 1) / p.pages_per_split;
+  }
+  p.off_part = 0;
+  p.total = align256((size_t)B * n_kv * p.splits * G * (d + 2) * sizeof(float));
+  return p;
+}
+
+// ---------------------------------------------------------------------------
+// launchers (defined in quantize.hip / decode.hip); arguments already validated
+// ---------------------------------------------------------------------------
+hipError_t launch_quantize_pack(int kind, const uint16_t* x, int64_t n_src, int64_t tok_stride,
+                                int64_t head_stride, const int32_t* src_idx, int64_t n_tok, int n_kv,
+                                int d, const float* rot, float clip, const int32_t* dst_slot,
+                                uint8_t* codes, uint16_t* scale_zero, int64_t n_pages,
+                                hipStream_t stream);
+
+// decode phases: rotate the query, scan history and BF16 windows, merge
+constexpr int kPhaseRotate = 0, kPhaseScan = 1, kPhaseMerge = 2;
+hipError_t launch_decode_phase(int phase, const oscar_decode_args& a, const DecodePlan& plan, char* ws,
+                               hipStream_t stream);
+
+hipError_t launch_decode_bf16(const oscar_bf16_decode_args& a, const Bf16Plan& plan, char* ws,
+                              hipStream_t stream);
+
+}  // namespace oscar

@@ -1,0 +1,154 @@
+// oscar_quantize_pack kernel: rotate -> clip -> INT2 quantise -> pack.
+//
+// Demotes tokens of one tensor (K or V) into 64-token INT2 pages.  The step
+// order (rotate by the fixed R, clip with the per-layer threshold, quantise
+// with a per-group scale/zero point, pack four 2-bit codes per byte) is the
+// demotion step of the serving pipeline in the myzaker.com article on OSCAR;
+// R and the threshold are the offline artefacts of the gist.science OSCAR
+// technical summary, section 2.2A.
+//
+// Block = (tile of 32 tokens, one KV head).  R[g] columns are read once per
+// block and reused for the tile.  The rotation accumulates in fp64 (the
+// bf16 x fp32 products are exact in fp64) and rounds once to fp32, so every
+// later decision (clip, min/max, fp16 rounding of scale/zero, the code) is
+// taken on the correctly rounded fp32 rotated value.
+#include "common.hpp"
+
+namespace oscar {
+namespace {
+
+constexpr int kQTok = 32;  // tokens per block
+
+template <int D>
+__global__ __launch_bounds__(kBlock) void quantize_pack_kernel(
+    int kind, const uint16_t* __restrict__ x, int64_t n_src, int64_t tok_stride,
+    int64_t head_stride, const int32_t* __restrict__ src_idx, int64_t n_tok, int n_kv,
+    const float* __restrict__ rot, float clip, const int32_t* __restrict__ dst_slot,
+    uint8_t* __restrict__ codes, uint32_t* __restrict__ sz, int64_t n_pages) {
+  constexpr int kParts = kBlock / D;     // token groups (2 for d=128, 4 for d=64)
+  constexpr int kPerThr = kQTok / kParts;
+  constexpr int kRowBytes = D / 4;       // code bytes per token
+  constexpr int kPlane = D / 16;         // bytes per token in one K plane
+  __shared__ float xs[D][kQTok];         // x tile, channel-major (broadcast reads)
+  __shared__ float ys[kQTok][D + 1];     // clipped rotated values
+  __shared__ int64_t src_s[kQTok];
+  __shared__ int64_t dst_s[kQTok];       // -1: skip this token
+  __shared__ float zf[kQTok], sf[kQTok];
+
+  const int g = blockIdx.y;
+  const int64_t t0 = (int64_t)blockIdx.x * kQTok;
+  const int tid = threadIdx.x;
+
+  if (tid < kQTok) {
+    const int64_t t = t0 + tid;
+    int64_t s = -1, slot = -1;
+    if (t < n_tok) {
+      s = src_idx ? (int64_t)src_idx[t] : t;
+      slot = dst_slot[t];
+      if (s < 0 || s >= n_src || slot < 0 || slot >= n_pages * kPage) {
+        s = -1;
+        slot = -1;
+      }
+    }
+    src_s[tid] = s;
+    dst_s[tid] = slot;
+  }
+  __syncthreads();
+
+  for (int e = tid; e < kQTok * D; e += kBlock) {
+    const int t = e / D, c = e % D;
+    const int64_t s = src_s[t];
+    xs[c][t] = (s >= 0) ? bf16_to_f32(x[s * tok_stride + (int64_t)g * head_stride + c]) : 0.0f;
+  }
+  __syncthreads();
+
+  // y[t][j] = sum_i x[t][i] * R[i][j]
+  const int j = tid % D, part = tid / D;
+  const float* R = rot + (size_t)g * D * D;
+  double acc[kPerThr];
+#pragma unroll
+  for (int k = 0; k < kPerThr; ++k) acc[k] = 0.0;
+  for (int i = 0; i < D; ++i) {
+    const double r = (double)R[i * D + j];
+#pragma unroll
+    for (int k = 0; k < kPerThr; ++k) acc[k] = fma((double)xs[i][part * kPerThr + k], r, acc[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < kPerThr; ++k) {
+    const float y = (float)acc[k];
+    ys[part * kPerThr + k][j] = fminf(fmaxf(y, -clip), clip);
+  }
+  __syncthreads();
+
+  // per-token group statistics: zero = fp16(min), scale = fp16((max - min) / 3)
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  for (int t = wave; t < kQTok; t += kBlock / kWave) {
+    float mn = INFINITY, mx = -INFINITY;
+    for (int c = lane; c < D; c += kWave) {
+      mn = fminf(mn, ys[t][c]);
+      mx = fmaxf(mx, ys[t][c]);
+    }
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    if (lane == 0) {
+      const __half z = __float2half_rn(mn);
+      const __half s = __float2half_rn(__fdiv_rn(mx - mn, 3.0f));
+      zf[t] = __half2float(z);
+      sf[t] = __half2float(s);
+      const int64_t slot = dst_s[t];
+      if (slot >= 0) {
+        const int64_t page = slot / kPage;
+        const int o = (int)(slot % kPage);
+        sz[(page * n_kv + g) * kPage + o] =
+            (uint32_t)__half_as_ushort(s) | ((uint32_t)__half_as_ushort(z) << 16);
+      }
+    }
+  }
+  __syncthreads();
+
+  // codes: rint((y - zero) / scale) clamped to [0, 3], 4 per byte, LSB first
+  for (int e = tid; e < kQTok * kRowBytes; e += kBlock) {
+    const int t = e / kRowBytes, i = e % kRowBytes;
+    const int64_t slot = dst_s[t];
+    if (slot < 0) continue;
+    const float z = zf[t], s = sf[t];
+    uint32_t byte = 0;
+    if (s != 0.0f) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float v = rintf(__fdiv_rn(ys[t][4 * i + q] - z, s));
+        v = fminf(fmaxf(v, 0.0f), 3.0f);
+        byte |= (uint32_t)v << (2 * q);
+      }
+    }
+    const int64_t page = slot / kPage;
+    const int o = (int)(slot % kPage);
+    uint8_t* blk = codes + (page * n_kv + g) * (int64_t)(kPage * kRowBytes);
+    const int pos = (kind == OSCAR_KIND_K) ? (i / kPlane) * (kPage * kPlane) + o * kPlane + (i % kPlane)
+                                           : i * kPage + o;
+    blk[pos] = (uint8_t)byte;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_pack(int kind, const uint16_t* x, int64_t n_src, int64_t tok_stride,
+                                int64_t head_stride, const int32_t* src_idx, int64_t n_tok, int n_kv,
+                                int d, const float* rot, float clip, const int32_t* dst_slot,
+                                uint8_t* codes, uint16_t* scale_zero, int64_t n_pages,
+                                hipStream_t stream) {
+  if (n_tok == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n_tok + kQTok - 1) / kQTok), (unsigned)n_kv);
+  uint32_t* sz = reinterpret_cast<uint32_t*>(scale_zero);
+  if (d == 128)
+    quantize_pack_kernel<128><<<grid, kBlock, 0, stream>>>(kind, x, n_src, tok_stride, head_stride,
+                                                          src_idx, n_tok, n_kv, rot, clip, dst_slot,
+                                                          codes, sz, n_pages);
+  else
+    quantize_pack_kernel<64><<<grid, kBlock, 0, stream>>>(kind, x, n_src, tok_stride, head_stride,
+                                                         src_idx, n_tok, n_kv, rot, clip, dst_slot,
+                                                         codes, sz, n_pages);
+  return hipGetLastError();
+}
+
+}  // namespace oscar

@@ -1,0 +1,216 @@
+/*
+ * oscar.h - C ABI of liboscar: INT2 three-segment decode attention and the
+ * INT2 demotion (rotate -> clip -> quantise -> pack) kernel, for AMD gfx950.
+ *
+ * Method sources (cited by page title and section):
+ *  - gist.science, "OSCAR: Offline Spectral Covariance-Aware Rotation for
+ *    2-bit KV Cache Quantization", technical summary section 2.2A (fixed
+ *    per-head rotations R_K = U_Q H P_br, R_V = U_S H P_br and per-layer clip
+ *    thresholds, computed offline) and section 2.2B (paged hybrid-precision
+ *    cache; INT2 history is unpacked, dequantised and inverse-rotated inside
+ *    the attention kernel).
+ *  - myzaker.com article on OSCAR, serving-pipeline paragraphs: a token pool
+ *    of BF16 sink (64 tokens) | INT2 history | BF16 recent (256 tokens); the
+ *    oldest recent token is rotated, clipped, quantised and packed (four
+ *    2-bit values per byte) into history; decode runs an INT2 part (unpack,
+ *    scale/zero-point dequantisation, float accumulation) and a BF16 part
+ *    and merges them with an online softmax.
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers named in a signature are DEVICE pointers owned by the caller,
+ *    unless documented as host.  The library allocates, frees and
+ *    synchronises nothing and keeps no mutable global state.  Work is
+ *    enqueued on `stream` (NULL = the default stream); results are valid
+ *    after the caller synchronises that stream.
+ *  - All argument checks run on the host BEFORE any HIP call.  A failed
+ *    check returns OSCAR_EINVAL / OSCAR_EUNSUPPORTED / OSCAR_EWORKSPACE
+ *    and enqueues nothing.  A kernel launch failure returns OSCAR_EHIP.
+ *  - Rotations use row vectors: a rotated vector is y = x R; its inverse is
+ *    x = y R^T.  R is fp32 [n_kv][d][d] row-major, one matrix per KV head.
+ *  - bf16 and fp16 values are passed as their 16-bit patterns.
+ *  - Pages hold 64 tokens.  One (page, KV head) block of an INT2 pool is:
+ *      K codes : d/4*64 bytes in 4 planes.  Plane p (p = 0..3) holds bytes
+ *                [p*d/16, (p+1)*d/16) of every token's code row, token-major:
+ *                byte i of token o is at (i/(d/16))*64*(d/16) + o*(d/16) + i%(d/16).
+ *      V codes : byte-column-major: byte i of token o is at i*64 + o.
+ *      A token's code row has d/4 bytes; byte i holds rotated channels
+ *      4i..4i+3, channel 4i+j in bits 2j..2j+1.
+ *      scale/zero: fp16 pairs (scale, zero) per token: [64][2].
+ *    Pools: codes uint8 [n_pages][n_kv][64*d/4]; scale_zero uint16
+ *    [n_pages][n_kv][64][2].  A K pool and a V pool are separate buffers.
+ *  - Dequantisation of a code c is zero + c*scale (rotated space).
+ */
+#ifndef OSCAR_H
+#define OSCAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OSCAR_ABI_VERSION 1
+#define OSCAR_PAGE_TOKENS 64
+
+#ifndef OSCAR_API
+#define OSCAR_API __attribute__((visibility("default")))
+#endif
+
+typedef enum oscar_status {
+  OSCAR_OK = 0,
+  OSCAR_EINVAL = 1,        /* a pointer, size or scalar argument is invalid */
+  OSCAR_EUNSUPPORTED = 2,  /* a valid shape this build has no kernel for   */
+  OSCAR_EWORKSPACE = 3,    /* workspace missing, misaligned or too small    */
+  OSCAR_EHIP = 4           /* the HIP runtime reported an error             */
+} oscar_status;
+
+typedef enum oscar_kind { OSCAR_KIND_K = 0, OSCAR_KIND_V = 1 } oscar_kind;
+
+/* ABI version of the loaded library (OSCAR_ABI_VERSION). */
+OSCAR_API int oscar_abi_version(void);
+
+/* Static, human-readable text for a status code (never NULL). */
+OSCAR_API const char* oscar_status_str(int status);
+
+/*
+ * oscar_quantize_pack - demote tokens of ONE tensor (K or V) of one layer
+ * into INT2 history pages.  Follows the demotion step of the serving pipeline
+ * (myzaker.com article) with the rotation and clip threshold of the
+ * gist.science technical summary, section 2.2A:
+ *   y = x R (fp32, accumulated exactly and rounded once); y_c = clamp(y, -clip, clip);
+ *   over the d channels of each (token, head): zero = fp16(min y_c),
+ *   scale = fp16((max y_c - min y_c) / 3) (fp32 subtract and divide);
+ *   code = clamp(rint((y_c - zero) / scale), 0, 3) in fp32, round half to
+ *   even, all codes 0 when scale is 0; pack 4 codes per byte; write the code
+ *   row and (scale, zero) into slot dst_slot = page*64 + offset.
+ *
+ *  kind          OSCAR_KIND_K or OSCAR_KIND_V (selects the in-page layout)
+ *  x             bf16; element (token s, head g, channel c) is at
+ *                x[s*x_tok_stride + g*x_head_stride + c]; the caller
+ *                guarantees that address is valid for every s in [0, n_src)
+ *  src_idx       int32 [n_tok] source token of each demoted token, or NULL
+ *                for tokens 0..n_tok-1; entries outside [0, n_src) are skipped
+ *  n_tok         tokens to demote (0 is a no-op)
+ *  n_kv, head_dim  head_dim in {64, 128}; n_kv >= 1
+ *  rot           fp32 [n_kv][head_dim][head_dim] (R_K or R_V)
+ *  clip          per-layer threshold, finite, 0 < clip <= 65504 (host scalar)
+ *  dst_slot      int32 [n_tok]; slots outside [0, n_pages*64) are skipped
+ *  codes         uint8 pool [n_pages][n_kv][64*head_dim/4]
+ *  scale_zero    uint16 pool [n_pages][n_kv][64][2]
+ *  Two demoted tokens must not share a slot (the result would be unspecified).
+ */
+OSCAR_API oscar_status oscar_quantize_pack(int32_t kind, const uint16_t* x, int64_t n_src,
+                                 int64_t x_tok_stride, int64_t x_head_stride,
+                                 const int32_t* src_idx, int64_t n_tok, int32_t n_kv,
+                                 int32_t head_dim, const float* rot, float clip,
+                                 const int32_t* dst_slot, uint8_t* codes,
+                                 uint16_t* scale_zero, int64_t n_pages, hipStream_t stream);
+
+/*
+ * Decode attention over a three-segment cache (one new query per request).
+ * Context of request b, in order: sink tokens [0, sink_len[b]) (BF16,
+ * unrotated), history tokens [0, hist_len[b]) (INT2, stored rotated; history
+ * token t is in page block_table[b][t/64] at offset t%64), recent tokens
+ * [0, recent_len[b]) (BF16, unrotated, any ring order).  Query head h uses KV
+ * head h / (n_q_heads / n_kv_heads).  Every query attends to its whole
+ * context: out = softmax(sm_scale * q.k) . v, with INT2 history keys and
+ * values inverse-rotated (x = (zero + c*scale) R^T).  The rotation is applied
+ * once per query head (q R_K before the history scan, accumulated values times
+ * R_V^T after it).  The INT2 and BF16 parts merge through an online softmax.
+ * A request whose segments are all empty gets a zero output row.  Device
+ * lengths outside [0, cap] / [0, max_hist_len], or a block-table entry outside
+ * [0, n_pages) for a used page, make that request's output rows NaN (no
+ * out-of-bounds access happens).
+ */
+typedef struct oscar_decode_args {
+  int32_t batch;            /* B >= 0 (0 is a no-op)                               */
+  int32_t n_q_heads;        /* multiple of n_kv_heads; G = n_q_heads/n_kv_heads in {1,2,4,8,16} */
+  int32_t n_kv_heads;       /* >= 1                                                */
+  int32_t head_dim;         /* 64 or 128                                           */
+  float sm_scale;           /* finite, > 0 (normally 1/sqrt(head_dim))             */
+  const uint16_t* q;        /* bf16 [B][n_q_heads][head_dim]                       */
+  const uint16_t* sink_k;   /* bf16 [B][n_kv][sink_cap][head_dim]                  */
+  const uint16_t* sink_v;
+  const uint16_t* recent_k; /* bf16 [B][n_kv][recent_cap][head_dim]                */
+  const uint16_t* recent_v;
+  int32_t sink_cap;         /* 0..4096 (64 in OSCAR)                               */
+  int32_t recent_cap;       /* 0..4096 (256 in OSCAR)                              */
+  const int32_t* sink_len;  /* int32 [B]                                           */
+  const int32_t* recent_len;/* int32 [B]                                           */
+  const int32_t* hist_len;  /* int32 [B]                                           */
+  int32_t max_hist_len;     /* host upper bound on hist_len[b]; sizes the grid     */
+  const uint8_t* k_codes;   /* INT2 K pool (layout above)                          */
+  const uint8_t* v_codes;   /* INT2 V pool                                         */
+  const uint16_t* k_sz;     /* fp16 (scale, zero) pools                            */
+  const uint16_t* v_sz;
+  int64_t n_pages;          /* pages in each pool                                  */
+  const int32_t* block_table; /* int32 [B][max_pages]                              */
+  int32_t max_pages;        /* >= ceil(max_hist_len/64)                            */
+  const float* r_k;         /* fp32 [n_kv][d][d], the R used to quantise K         */
+  const float* r_v;         /* fp32 [n_kv][d][d], the R used to quantise V         */
+  float* out;               /* fp32 [B][n_q_heads][head_dim]                       */
+} oscar_decode_args;
+
+/* Workspace bytes oscar_decode_attn needs for these sizes (0 on invalid sizes).
+ * Depends only on its arguments, so results do not depend on the device. */
+OSCAR_API size_t oscar_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                    int32_t head_dim, int32_t max_hist_len, int32_t sink_cap,
+                                    int32_t recent_cap);
+
+/* Enqueue decode attention.  workspace: device buffer of at least
+ * oscar_decode_workspace_bytes(...) bytes, 256-byte aligned; its contents on
+ * entry do not matter and are overwritten. */
+OSCAR_API oscar_status oscar_decode_attn(const oscar_decode_args* args, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The three phases oscar_decode_attn runs, in this order, on one stream; a
+ * caller may enqueue them separately (to time or overlap a phase).  The
+ * workspace carries the state between phases, so the same args and
+ * workspace must be passed to all three.
+ *   oscar_decode_rotate_query  q_rot = q R_K (and its channel sum) per query head
+ *   oscar_decode_scan          INT2 history split-K scan and BF16 sink/recent
+ *                              tiles; one online-softmax partial per split/tile
+ *   oscar_decode_merge         log-sum-exp merge of the history partials, times
+ *                              R_V^T, merge with the BF16 partials, normalise
+ * Same validation and status codes as oscar_decode_attn.
+ */
+OSCAR_API oscar_status oscar_decode_rotate_query(const oscar_decode_args* args, void* workspace,
+                                                 size_t workspace_bytes, hipStream_t stream);
+OSCAR_API oscar_status oscar_decode_scan(const oscar_decode_args* args, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream);
+OSCAR_API oscar_status oscar_decode_merge(const oscar_decode_args* args, void* workspace,
+                                          size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * BF16 comparator: plain decode attention with the whole context held in
+ * BF16 pages (no rotation, no quantisation), same GQA mapping and output
+ * rules.  Used to measure the INT2 path against a BF16 cache of the same
+ * shape.  Context token t of request b is in page block_table[b][t/64] at
+ * offset t%64 of k_pages/v_pages bf16 [n_pages][n_kv][64][head_dim].
+ */
+typedef struct oscar_bf16_decode_args {
+  int32_t batch, n_q_heads, n_kv_heads, head_dim;
+  float sm_scale;
+  const uint16_t* q;          /* bf16 [B][n_q_heads][head_dim] */
+  const uint16_t* k_pages;    /* bf16 [n_pages][n_kv][64][head_dim] */
+  const uint16_t* v_pages;
+  int64_t n_pages;
+  const int32_t* block_table; /* int32 [B][max_pages] */
+  int32_t max_pages;
+  const int32_t* ctx_len;     /* int32 [B], each in [0, max_ctx_len] */
+  int32_t max_ctx_len;        /* host bound, <= max_pages*64 */
+  float* out;                 /* fp32 [B][n_q_heads][head_dim] */
+} oscar_bf16_decode_args;
+
+OSCAR_API size_t oscar_decode_bf16_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                         int32_t head_dim, int32_t max_ctx_len);
+OSCAR_API oscar_status oscar_decode_attn_bf16(const oscar_bf16_decode_args* args, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* OSCAR_H */

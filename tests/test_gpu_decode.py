@@ -1,0 +1,172 @@
+"""GPU parity of oscar_decode_attn (and the BF16 comparator) against the oracle.
+
+Decode inputs never come from the HIP path: history pages are written by the
+oracle quantiser or by the brute-force page writer of tests/pins.py, or drawn
+directly (28-request workload)."""
+import numpy as np
+import pytest
+import torch
+
+import bit_rotated_kv_attn_amd as hip
+import oracle
+import pins
+import synth
+from gpu_util import compare_out, dev, gpu_decode, host, oracle_pools
+
+pytestmark = pytest.mark.gpu
+PAGE = 64
+
+
+def ragged_cache(seed, B, n_kv, G, d, sink, hist, recent, sink_cap=64, recent_cap=256):
+    rng = np.random.default_rng(seed)
+    cfg, pools, _ = pins.make_small_cache(seed=seed, B=B, Hq=n_kv * G, nkv=n_kv, d=d, sink=sink,
+                                          hist=hist, recent=recent, sink_cap=sink_cap,
+                                          recent_cap=recent_cap)
+    return cfg, pools
+
+
+def test_tiny_config():
+    cfg = synth.make_decode_config(0)
+    pools = oracle_pools(cfg)
+    ref = oracle.decode_attn_ref(cfg, *pools)
+    got = gpu_decode(cfg, pools)
+    compare_out(got, ref, what="tiny config")
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("d", [64, 128])
+def test_ragged_segments(G, d):
+    """Partial pages, partial windows, empty history, empty windows."""
+    cfg, pools = ragged_cache(10 + G, B=3, n_kv=2, G=G, d=d, sink=(64, 5, 0), hist=(0, 37, 200),
+                              recent=(256, 1, 100))
+    ref = oracle.decode_attn_ref(cfg, *pools)
+    got = gpu_decode(cfg, pools)
+    compare_out(got, ref, what=f"ragged G={G} d={d}")
+
+
+def test_empty_context_rows_are_zero():
+    cfg, pools = ragged_cache(3, B=2, n_kv=1, G=4, d=64, sink=(0, 3), hist=(0, 70), recent=(0, 2))
+    got = gpu_decode(cfg, pools)
+    assert not got[0].any()
+    compare_out(got, oracle.decode_attn_ref(cfg, *pools), what="empty context")
+
+
+def test_bad_inputs_poison_only_their_request():
+    cfg, pools = ragged_cache(4, B=3, n_kv=2, G=4, d=128, sink=(64, 64, 64), hist=(130, 130, 130),
+                              recent=(256, 256, 256))
+    ref = oracle.decode_attn_ref(cfg, *pools)
+    table = cfg["block_table"].copy()
+    table[1, 1] = pools[0].shape[0] + 5          # outside the pool
+    hl = cfg["hist_len"].copy()
+    hl[2] = 10_000                               # above max_hist_len
+    got = gpu_decode(cfg, pools, block_table=table, hist_len=hl, max_hist_len=130)
+    assert np.all(np.isnan(got[1])) and np.all(np.isnan(got[2]))
+    compare_out(got[:1], ref[:1], what="unaffected request")
+    sl = cfg["sink_len"].copy()
+    sl[0] = 65                                   # above sink_cap
+    got = gpu_decode(cfg, pools, sink_len=sl)
+    assert np.all(np.isnan(got[0]))
+    compare_out(got[1:], ref[1:], what="unaffected requests")
+
+
+def test_split_partition_and_page_order_invariance():
+    cfg, pools = ragged_cache(6, B=2, n_kv=2, G=8, d=128, sink=(64, 64), hist=(1000, 999),
+                              recent=(256, 256))
+    ref = oracle.decode_attn_ref(cfg, *pools)
+    base = gpu_decode(cfg, pools)
+    compare_out(base, ref, what="base")
+    # a larger max_hist_len changes pages per split (a different partition)
+    wide = np.full((2, 125), -1, np.int32)
+    wide[:, : cfg["block_table"].shape[1]] = cfg["block_table"]
+    other = gpu_decode(cfg, pools, block_table=wide, max_hist_len=8000)
+    compare_out(other, ref, what="other split count")
+    # physical page order: same logical pages -> bit-identical
+    n_pages = pools[0].shape[0]
+    perm = np.random.default_rng(1).permutation(n_pages)
+    inv = np.argsort(perm)
+    t2 = cfg["block_table"].copy()
+    t2[t2 >= 0] = perm[t2[t2 >= 0]]
+    moved = gpu_decode(cfg, tuple(p[inv] for p in pools), block_table=t2)
+    assert np.array_equal(moved, base)
+
+
+def test_deterministic():
+    cfg = synth.make_decode_config(0)
+    pools = oracle_pools(cfg)
+    a = gpu_decode(cfg, pools)
+    b = gpu_decode(cfg, pools, reps=3)
+    assert np.array_equal(a, b)
+
+
+def test_qwen3_8b_layer_32k():
+    cfg = synth.make_decode_config(1)
+    pools = oracle_pools(cfg)
+    ref = oracle.decode_attn_ref(cfg, *pools)
+    got = gpu_decode(cfg, pools)
+    compare_out(got, ref, what="Qwen3-8B layer, 32k")
+
+
+def test_qwen3_32b_layer_100k():
+    cfg = synth.make_decode_config(3)
+    pools = oracle_pools(cfg)
+    ref = oracle.decode_attn_ref(cfg, *pools)
+    got = gpu_decode(cfg, pools)
+    compare_out(got, ref, what="Qwen3-32B layer, 100k")
+
+
+def test_batch28_shared_prefix_100k_sampled():
+    """28 requests x 100k context, 1406 shared history pages; pages are drawn
+    directly (uniform codes, realistic fp16 scale/zero).  The oracle computes a
+    seeded sample of (request, head) rows; the rest are checked finite."""
+    cfg = synth.make_decode_config(4, materialize_history=False)
+    rng = np.random.default_rng(2024)
+    sigma = float(np.sqrt((128 - 3 + 3 * 400) / 128))
+    kc, ks = synth.random_pages(rng, cfg["n_pages"], cfg["n_kv"], cfg["head_dim"], sigma)
+    vc, vs = synth.random_pages(rng, cfg["n_pages"], cfg["n_kv"], cfg["head_dim"], sigma)
+    pools = (kc, vc, ks, vs)
+    got = gpu_decode(cfg, pools)
+    heads = [(0, 0), (5, 13), (27, 31), (14, 8), (27, 2)]
+    ref = oracle.decode_attn_ref(cfg, *pools, heads=heads)
+    idx = tuple(np.array(heads).T)
+    compare_out(got[idx], ref[idx], what="28x100k sampled rows")
+    assert np.all(np.isfinite(got))
+
+
+# ---- BF16 comparator ------------------------------------------------------
+def _gpu_bf16(q, kp, vp, table, ctx, sm):
+    B, Hq, d = q.shape
+    ws = torch.empty(max(1, hip.oscar_decode_bf16_workspace_bytes(B, Hq, kp.shape[1], d, int(ctx.max()))),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    hip.oscar_decode_attn_bf16(q=dev(q), k_pages=dev(kp), v_pages=dev(vp), block_table=dev(table),
+                               ctx_len=dev(ctx), max_ctx_len=int(ctx.max()), out=out, workspace=ws,
+                               sm_scale=float(sm))
+    torch.cuda.synchronize()
+    return host(out)
+
+
+@pytest.mark.parametrize("cfg_index", [0, 1])
+def test_bf16_comparator(cfg_index):
+    cfg = synth.make_decode_config(cfg_index)
+    bf = synth.bf16_context_pages(cfg)
+    ref = oracle.bf16_paged_attn_ref(cfg["q"], bf["k_pages"], bf["v_pages"], bf["block_table"], bf["ctx_len"],
+                                     cfg["sm_scale"])
+    got = _gpu_bf16(cfg["q"], bf["k_pages"], bf["v_pages"], bf["block_table"], bf["ctx_len"], cfg["sm_scale"])
+    compare_out(got, ref, what=f"bf16 comparator config {cfg_index}")
+
+
+def test_bf16_comparator_ragged():
+    rng = np.random.default_rng(9)
+    B, Hq, nkv, d = 3, 16, 2, 128
+    ctx = np.array([0, 65, 700], np.int32)
+    n_pages = 14
+    table = np.full((B, 11), -1, np.int32)
+    perm = rng.permutation(n_pages)
+    table[1, :2] = perm[:2]
+    table[2, :11] = perm[2:13]
+    kp = synth.f32_to_bf16_bits(rng.standard_normal((n_pages, nkv, PAGE, d)).astype(np.float32) * 2)
+    vp = synth.f32_to_bf16_bits(rng.standard_normal((n_pages, nkv, PAGE, d)).astype(np.float32))
+    q = synth.f32_to_bf16_bits(rng.standard_normal((B, Hq, d)).astype(np.float32))
+    ref = oracle.bf16_paged_attn_ref(q, kp, vp, table, ctx, 1 / np.sqrt(d))
+    got = _gpu_bf16(q, kp, vp, table, ctx, 1 / np.sqrt(d))
+    compare_out(got, ref, what="bf16 ragged")
