@@ -18,7 +18,7 @@ import os
 PAGE = 64
 KIND_K, KIND_V = 0, 1
 # arithmetic the kernels of this build compute in (reported by bench.py)
-COMPUTE_DTYPE = "f32 (fp64 rotation in demotion)"
+COMPUTE_DTYPE = "i8 MFMA (exact integer digits) + f32 softmax; f64 rotation in demotion"
 OSCAR_OK, OSCAR_EINVAL, OSCAR_EUNSUPPORTED, OSCAR_EWORKSPACE, OSCAR_EHIP = range(5)
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liboscar.so")
 

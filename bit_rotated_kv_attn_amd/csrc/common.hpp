@@ -55,10 +55,14 @@ struct DecodePlan {
   int pages_per_split;
   int chunks;        // BF16 64-token chunks per (request, KV head)
   int sink_chunks;   // the first sink_chunks chunks cover the sink window
-  size_t off_qrot, off_qsum, off_hpart, off_bpart, total;
+  size_t off_qdig, off_qa, off_qb, off_hpart, off_bpart, total;
 };
 
-constexpr int kTargetBlocks = 1024;  // history blocks per launch the split policy aims for
+#ifndef OSCAR_TARGET_BLOCKS
+#define OSCAR_TARGET_BLOCKS 1024
+#endif
+constexpr int kTargetBlocks = OSCAR_TARGET_BLOCKS;  // history blocks per launch the split policy aims for
+constexpr int kMaxPagesPerSplit = 4096;   // keeps the int32 PV accumulators far from overflow
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -66,11 +70,13 @@ inline DecodePlan make_decode_plan(int B, int Hq, int n_kv, int d, int max_hist_
                                    int recent_cap) {
   DecodePlan p{};
   const int G = Hq / n_kv;
+  const int NB = (G + 3) / 4;
   p.hist_pages = (max_hist_len + kPage - 1) / kPage;
   if (p.hist_pages > 0) {
     const long units = (long)(B > 0 ? B : 1) * n_kv;
     long s0 = (kTargetBlocks + units - 1) / units;
-    if (s0 < 1) s0 = 1;
+    const long s_min = (p.hist_pages + kMaxPagesPerSplit - 1) / kMaxPagesPerSplit;
+    if (s0 < s_min) s0 = s_min;
     if (s0 > p.hist_pages) s0 = p.hist_pages;
     p.pages_per_split = (int)((p.hist_pages + s0 - 1) / s0);
     p.splits = (p.hist_pages + p.pages_per_split - 1) / p.pages_per_split;
@@ -79,8 +85,9 @@ inline DecodePlan make_decode_plan(int B, int Hq, int n_kv, int d, int max_hist_
   p.chunks = p.sink_chunks + (recent_cap + kPage - 1) / kPage;
   const size_t part = (size_t)G * (d + 2) * sizeof(float);
   size_t off = 0;
-  p.off_qrot = off;  off = align256(off + (size_t)B * Hq * d * sizeof(float));
-  p.off_qsum = off;  off = align256(off + (size_t)B * Hq * sizeof(float));
+  p.off_qdig = off;  off = align256(off + (size_t)B * n_kv * NB * (d / 64) * 64 * 16);
+  p.off_qa = off;    off = align256(off + (size_t)B * Hq * sizeof(float));
+  p.off_qb = off;    off = align256(off + (size_t)B * Hq * sizeof(float));
   p.off_hpart = off; off = align256(off + (size_t)B * n_kv * p.splits * part);
   p.off_bpart = off; off = align256(off + (size_t)B * n_kv * p.chunks * part);
   p.total = off;

@@ -10,23 +10,44 @@
 //     q . (x_hat R^T) = (q R) . x_hat   and   sum_t p_t x_hat_t R^T = (sum_t p_t x_hat_t) R^T,
 // so the rotation is applied once per query head: to q before the history
 // scan and to the accumulated history output after the split merge.  With
-// x_hat = zero + c*scale, a history logit is scale*(q_rot . c) + zero*sum(q_rot).
+// x_hat = zero + c*scale, a history logit is scale*(q_rot . c) + zero*sum(q_rot)
+// and a history output is sum_t p_t*scale_t*c_t + sum_t p_t*zero_t.
+//
+// History scan on the matrix cores, in exact integer arithmetic
+// (v_mfma_i32_16x16x64_i8): the 2-bit codes become int8 operands by masking
+// (no conversion), the rotated query and the softmax weights become 30-bit
+// fixed-point integers split into four balanced 8-bit digits, one MFMA row per
+// (head, digit), so 4 heads fill the 16 rows.  Products and sums are exact;
+// the only roundings are the fixed-point conversions (relative 2^-24) and the
+// fp32 combination of the digit results.  PV accumulates in int32 across a
+// split's pages; the softmax reference maximum is only raised when a logit
+// exceeds it by 2^8 (then the integer accumulator is folded into fp32).
 //
 // Launches (all on the caller's stream):
-//   1. qrot_kernel    q_rot = q R_K[g], qsum = sum_j q_rot[j]
-//   2. decode_main    one grid: history splits (split-K over pages) and
-//                     BF16 64-token chunks; each writes an (m, l, acc) partial
-//   3. merge_kernel   LSE merge of the history partials, * R_V^T, LSE merge
-//                     with the BF16 partials, normalise
+//   1. rotate_query_kernel  q_rot = q R_K[g] per query head -> MFMA digit operands
+//   2. decode_main_kernel   one grid: BF16 sink/recent chunks (first) and INT2
+//                           history splits; each writes an (m, l, acc) partial
+//   3. merge_kernel         LSE merge of the history partials, * R_V^T, LSE merge
+//                           with the BF16 partials, normalise
 // Softmax state uses base-2 exponents (logits pre-scaled by log2 e).
 #include "common.hpp"
 
 namespace oscar {
 namespace {
 
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kMask0 = 0x03030303u;  // code field 0 of each byte (x1)
+constexpr uint32_t kMask1 = 0x0C0C0C0Cu;  // field 1 (x4)
+constexpr uint32_t kMask2 = 0x30303030u;  // field 2 (x16); field 3 is shifted into it
+constexpr float kLazyThr = 8.0f;          // raise the reference max only past +2^8
+constexpr float kScaleSlack = 1.75f;      // refold when a V scale exceeds 1.75x the running max
+constexpr float kFix = 1073741824.0f;     // 2^30: fixed-point range of digits
+constexpr int kPlanePad = 80;             // bytes per LDS digit plane (64 tokens + pad, 16-aligned)
+
 struct DecodeDev {
-  int B, Hq, n_kv, G, sink_cap, recent_cap, max_hist_len, max_pages;
-  int splits, pps, chunks, sink_chunks;
+  int B, Hq, n_kv, G, NB, sink_cap, recent_cap, max_hist_len, max_pages;
+  int splits, pps, chunks, sink_chunks, bf_blocks;
   float sm_log2;
   int64_t n_pages;
   const uint16_t *q, *sink_k, *sink_v, *recent_k, *recent_v;
@@ -34,7 +55,10 @@ struct DecodeDev {
   const uint8_t *k_codes, *v_codes;
   const uint32_t *k_sz, *v_sz;
   const float *r_k, *r_v;
-  float *out, *qrot, *qsum, *hpart, *bpart;
+  float* out;
+  uint8_t* qdig;     // [B][n_kv][NB][D/64][64 lanes][16 bytes] QK A operands
+  float *qa, *qb;    // [B][Hq] logit constants: sm_log2/(16 kq), sm_log2*sum(q_rot)
+  float *hpart, *bpart;
 };
 
 struct Bf16Dev {
@@ -46,10 +70,42 @@ struct Bf16Dev {
   float *out, *part;
 };
 
-// per-wave online-softmax state for G query heads; lane owns channels lane + 64k
+__device__ __forceinline__ float group16_max(float v) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float group16_sum(float v) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// operand mask p of a raw code word: bytes hold field p of each byte (x1, x4, x16, x16)
+__device__ __forceinline__ int code_mask(uint32_t w, int p) {
+  return (int)(p == 0 ? (w & kMask0) : p == 1 ? (w & kMask1) : p == 2 ? (w & kMask2) : ((w >> 2) & kMask2));
+}
+
+__device__ __forceinline__ float code_scale_inv(int p) {  // 1 / (x1, x4, x16, x16)
+  return p == 0 ? 1.0f : p == 1 ? 0.25f : 0.0625f;
+}
+
+// fp32 value of a 4-digit (base 256, balanced) integer held in one MFMA result column
+__device__ __forceinline__ float digits_to_f32(v4i d) {
+  return fmaf((float)d.w, 16777216.0f, fmaf((float)d.z, 65536.0f, fmaf((float)d.y, 256.0f, (float)d.x)));
+}
+
+__device__ __forceinline__ uint32_t balanced_digits(uint32_t x) {  // x in [-2^30, 2^30] two's complement
+  return (x + 0x80808080u) ^ 0x80808080u;
+}
+
+// ---------------------------------------------------------------------------
+// VALU path for BF16 tiles (sink / recent windows and the BF16 comparator)
+// ---------------------------------------------------------------------------
 template <int D, int G>
 struct WaveAcc {
-  float m[G], l[G], z[G];
+  float m[G], l[G];
   float a[G][D / kWave];
 };
 
@@ -59,98 +115,13 @@ __device__ __forceinline__ void acc_init(WaveAcc<D, G>& s) {
   for (int h = 0; h < G; ++h) {
     s.m[h] = -INFINITY;
     s.l[h] = 0.0f;
-    s.z[h] = 0.0f;
 #pragma unroll
     for (int k = 0; k < D / kWave; ++k) s.a[h][k] = 0.0f;
   }
 }
 
-// Softmax update for one 64-token tile: lane = token.  lg: base-2 logits
-// (-inf for invalid lanes).  Writes each token's weight p (times wscale) to
-// wbuf[lane*G + h] and returns via st the rescaled state; zterm is the value
-// added to every channel per unit weight (the history zero point), 0 for BF16.
-template <int D, int G>
-__device__ __forceinline__ void softmax_tile(WaveAcc<D, G>& st, const float (&lg)[G], bool valid,
-                                             float wscale, float zterm, float* wbuf, int lane) {
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float mt = wave_max(lg[h]);
-    const float mn = fmaxf(st.m[h], mt);
-    const float alpha = exp2_or_zero(st.m[h], mn);
-    const float pr = valid ? exp2f(lg[h] - mn) : 0.0f;
-    st.l[h] = st.l[h] * alpha + wave_sum(pr);
-    st.z[h] = st.z[h] * alpha + wave_sum(pr * zterm);
-#pragma unroll
-    for (int k = 0; k < D / kWave; ++k) st.a[h][k] *= alpha;
-    st.m[h] = mn;
-    wbuf[lane * G + h] = pr * wscale;
-  }
-  __builtin_amdgcn_wave_barrier();
-}
-
-// One INT2 history page (64 tokens, n_valid of them used) for KV head g.
-template <int D, int G>
-__device__ __forceinline__ void int2_page(WaveAcc<D, G>& st, const float* qr, const float* qs,
-                                          float sm_log2, const uint8_t* __restrict__ kblk,
-                                          const uint8_t* __restrict__ vblk,
-                                          const uint32_t* __restrict__ ksz,
-                                          const uint32_t* __restrict__ vsz, int n_valid,
-                                          float* wbuf, int lane) {
-  constexpr int kPlane = D / 16;   // bytes per token per K plane
-  constexpr int kWords = D / 16;   // 32-bit words per token code row
-  const bool valid = lane < n_valid;
-  uint32_t w[kWords];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(kblk + p * kPage * kPlane + lane * kPlane);
-#pragma unroll
-    for (int u = 0; u < kPlane / 4; ++u) w[p * (kPlane / 4) + u] = src[u];
-  }
-  const uint32_t szk = ksz[lane], szv = vsz[lane];
-  const float sk = f16_to_f32(szk & 0xffffu), zk = f16_to_f32(szk >> 16);
-  const float sv = f16_to_f32(szv & 0xffffu), zv = f16_to_f32(szv >> 16);
-
-  // code field k of row word u is rotated channel 16u + k
-  float dot[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) dot[h] = 0.0f;
-#pragma unroll
-  for (int u = 0; u < kWords; ++u) {
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const float c = (float)((w[u] >> (2 * k)) & 3u);
-#pragma unroll
-      for (int h = 0; h < G; ++h) dot[h] = fmaf(qr[h * D + 16 * u + k], c, dot[h]);
-    }
-  }
-  float lg[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) lg[h] = valid ? sm_log2 * fmaf(sk, dot[h], zk * qs[h]) : -INFINITY;
-  softmax_tile<D, G>(st, lg, valid, sv, zv, wbuf, lane);
-
-  // PV in rotated space: a[h][c] += sum_t p_t * scale_t * code_t[c]; the zero
-  // point's share sum_t p_t * zero_t is kept in st.z and added at the merge.
-#pragma unroll
-  for (int k = 0; k < D / kWave; ++k) {
-    const int c = lane + kWave * k;
-    const uint4* col = reinterpret_cast<const uint4*>(vblk + (c >> 2) * kPage);
-    uint32_t bw[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 v = col[q];
-      bw[4 * q] = v.x; bw[4 * q + 1] = v.y; bw[4 * q + 2] = v.z; bw[4 * q + 3] = v.w;
-    }
-    const int sh = 2 * (c & 3);
-    for (int t = 0; t < n_valid; ++t) {
-      const float cv = (float)((bw[t >> 2] >> (8 * (t & 3) + sh)) & 3u);
-#pragma unroll
-      for (int h = 0; h < G; ++h) st.a[h][k] = fmaf(wbuf[t * G + h], cv, st.a[h][k]);
-    }
-  }
-  __builtin_amdgcn_wave_barrier();
-}
-
-// One tile of up to 64 BF16 tokens; token t's row at kbase + t*D.
+// One tile of up to 64 BF16 tokens (lane = token for QK, lane = channel for
+// PV); token t's row at kbase + t*D.
 template <int D, int G>
 __device__ __forceinline__ void bf16_tile(WaveAcc<D, G>& st, const float* qu, float sm_log2,
                                           const uint16_t* __restrict__ kbase,
@@ -175,10 +146,20 @@ __device__ __forceinline__ void bf16_tile(WaveAcc<D, G>& st, const float* qu, fl
       }
     }
   }
-  float lg[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) lg[h] = valid ? sm_log2 * dot[h] : -INFINITY;
-  softmax_tile<D, G>(st, lg, valid, 1.0f, 0.0f, wbuf, lane);
+  for (int h = 0; h < G; ++h) {
+    const float lg = valid ? sm_log2 * dot[h] : -INFINITY;
+    const float mt = wave_max(lg);
+    const float mn = fmaxf(st.m[h], mt);
+    const float alpha = exp2_or_zero(st.m[h], mn);
+    const float pr = valid ? exp2f(lg - mn) : 0.0f;
+    st.l[h] = st.l[h] * alpha + wave_sum(pr);
+#pragma unroll
+    for (int k = 0; k < D / kWave; ++k) st.a[h][k] *= alpha;
+    st.m[h] = mn;
+    wbuf[lane * G + h] = pr;
+  }
+  __builtin_amdgcn_wave_barrier();
 #pragma unroll
   for (int k = 0; k < D / kWave; ++k) {
     const int c = lane + kWave * k;
@@ -191,28 +172,9 @@ __device__ __forceinline__ void bf16_tile(WaveAcc<D, G>& st, const float* qu, fl
   __builtin_amdgcn_wave_barrier();
 }
 
-// Wave-level partial: [G][D+2] = (m, l, acc[D]) per head; acc includes z.
+// Wave state -> this wave's slot of the block merge area [G][D+2] = (m, l, acc).
 template <int D, int G>
-__device__ __forceinline__ void write_wave_partial(const WaveAcc<D, G>& st, bool poison, float* dst,
-                                                   int lane) {
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float* ph = dst + h * (D + 2);
-    if (lane == 0) {
-      ph[0] = st.m[h];
-      ph[1] = poison ? NAN : st.l[h];
-    }
-#pragma unroll
-    for (int k = 0; k < D / kWave; ++k) ph[2 + lane + kWave * k] = st.a[h][k] + st.z[h];
-  }
-}
-
-// Merge the 4 waves' states of a block and write one partial.
-template <int D, int G>
-__device__ __forceinline__ void block_merge_write(const WaveAcc<D, G>& st, bool poison, float* mrg,
-                                                  int* flags, float* dst, int tid) {
-  const int lane = tid & (kWave - 1), wave = tid / kWave;
-  float* mw = mrg + wave * G * (D + 2);
+__device__ __forceinline__ void store_wave_state(const WaveAcc<D, G>& st, float* mw, int lane) {
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     if (lane == 0) {
@@ -220,36 +182,336 @@ __device__ __forceinline__ void block_merge_write(const WaveAcc<D, G>& st, bool 
       mw[h * (D + 2) + 1] = st.l[h];
     }
 #pragma unroll
-    for (int k = 0; k < D / kWave; ++k) mw[h * (D + 2) + 2 + lane + kWave * k] = st.a[h][k] + st.z[h];
+    for (int k = 0; k < D / kWave; ++k) mw[h * (D + 2) + 2 + lane + kWave * k] = st.a[h][k];
   }
-  if (lane == 0) flags[wave] = poison ? 1 : 0;
-  __syncthreads();
+}
+
+// Merge the 4 wave slots of a block (after a barrier; slot v starts at
+// mrg + v*slot floats) into one partial.
+__device__ __forceinline__ void combine_block(const float* mrg, int slot, const int* flags, float* dst, int G,
+                                              int D, int tid) {
   const bool bad = flags[0] | flags[1] | flags[2] | flags[3];
-  constexpr int kW = kBlock / kWave;
   for (int e = tid; e < G * (D + 2); e += kBlock) {
     const int h = e / (D + 2), r = e % (D + 2);
     float M = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < kW; ++v) M = fmaxf(M, mrg[v * G * (D + 2) + h * (D + 2)]);
+    for (int v = 0; v < 4; ++v) M = fmaxf(M, mrg[v * slot + h * (D + 2)]);
     float s = 0.0f;
+    if (r != 0) {
 #pragma unroll
-    for (int v = 0; v < kW; ++v) {
-      const float f = exp2_or_zero(mrg[v * G * (D + 2) + h * (D + 2)], M);
-      s += (r == 0) ? 0.0f : f * mrg[v * G * (D + 2) + e];
+      for (int v = 0; v < 4; ++v) s += exp2_or_zero(mrg[v * slot + h * (D + 2)], M) * mrg[v * slot + e];
     }
-    if (r == 0) dst[e] = M;
-    else if (r == 1) dst[e] = bad ? NAN : s;
-    else dst[e] = s;
+    dst[e] = (r == 0) ? M : (r == 1 && bad) ? NAN : s;
   }
 }
 
 // ---------------------------------------------------------------------------
+// INT2 history on the matrix cores
+// ---------------------------------------------------------------------------
+// Lane roles (lane = 16*grp + n):
+//  * QK:  D[(head, digit)][token] = sum_ch Qdigit[(head,digit)][ch] * code'[ch][token].
+//         A (q digits) comes from the workspace; B lane (n, grp) holds, for token
+//         block tb, token 4n+tb and the 16 channels of one code word of K plane grp.
+//         The result lane holds the 4 digit sums of head (4nb+grp) for token 4n+tb.
+//  * PV:  D[(head, digit)][channel] = sum_t Wdigit[(head,digit)][t] * code'[t][channel].
+//         A (weight digits) is read back from LDS planes; B lane (n, grp) holds
+//         tokens 16grp..16grp+15 of one channel of V byte column D/64*n + bs.
+//         The result lane holds the 4 digit sums of head (4nb+grp), channel D/16*n + u.
+// ---- asynchronous page staging: global -> LDS copies (no VGPRs), one ring of
+// stages per wave.  The copies are issued from inline assembly so that their
+// completion is awaited explicitly (s_waitcnt vmcnt(n) before a stage is read)
+// and pages ahead of the one being consumed stay in flight.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p);
+}
+
+__device__ __forceinline__ void copy16_to_lds(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_base) : "memory");
+}
+
+__device__ __forceinline__ void copy4_to_lds(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_base) : "memory");
+}
+
+// wait until at most n vector-memory operations of this wave are outstanding
+__device__ __forceinline__ void wait_vmem(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+    case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+    case 18: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+
+// Stage layout (one page of one KV head): K codes (16*D bytes, the pool's
+// plane layout), V codes (16*D bytes, byte-column-major), K (scale, zero)
+// [64] u32, V (scale, zero) [64] u32.
 template <int D>
-__global__ __launch_bounds__(128) void qrot_kernel(DecodeDev p) {
+struct Stage {
+  static constexpr int kK = 0, kV = 16 * D, kKsz = 32 * D, kVsz = 32 * D + 256, kBytes = 32 * D + 512;
+  static constexpr int kCopies = 2 * (D / 64) + 2;   // copy instructions per page
+};
+
+template <int D>
+__device__ __forceinline__ void stage_page(const DecodeDev& p, size_t blk, uint32_t stage_lds, int lane) {
+  using S = Stage<D>;
+  const uint8_t* kblk = p.k_codes + blk * (16 * D);
+  const uint8_t* vblk = p.v_codes + blk * (16 * D);
+#pragma unroll
+  for (int c = 0; c < D / 64; ++c) copy16_to_lds(kblk + 1024 * c + 16 * lane, stage_lds + S::kK + 1024 * c);
+#pragma unroll
+  for (int c = 0; c < D / 64; ++c) copy16_to_lds(vblk + 1024 * c + 16 * lane, stage_lds + S::kV + 1024 * c);
+  copy4_to_lds(p.k_sz + blk * kPage + lane, stage_lds + S::kKsz);
+  copy4_to_lds(p.v_sz + blk * kPage + lane, stage_lds + S::kVsz);
+}
+
+// Ring stages per wave and where the weight-digit planes live, chosen so two
+// blocks of 4 waves fit a CU's 160 KB of LDS.
+template <int D, int NB>
+struct Ring {
+  static constexpr bool kPlanesInK = NB * 1024 <= 16 * D;   // planes reuse the consumed K codes
+  static constexpr int kStages = (D == 128 && NB > 2) ? 3 : 4;
+  static constexpr int kPlaneBytes = kPlanesInK ? 0 : NB * 1024;
+  static constexpr int kWaveBytes = kStages * Stage<D>::kBytes + kPlaneBytes;
+};
+
+// Lane roles (lane = 16*grp + n):
+//  * QK:  D[(head, digit)][token] = sum_ch Qdigit[(head,digit)][ch] * code'[ch][token].
+//         A (q digits) comes from the workspace; B lane (n, grp) holds, for token
+//         block tb, token 4n+tb and the 16 channels of one code word of K plane grp.
+//         The result lane holds the 4 digit sums of head (4nb+grp) for token 4n+tb.
+//  * PV:  D[(head, digit)][channel] = sum_t Wdigit[(head,digit)][t] * code'[t][channel].
+//         A (weight digits) is read back from LDS planes; B lane (n, grp) holds
+//         tokens 16grp..16grp+15 of one channel of V byte column D/64*n + bs.
+//         The result lane holds the 4 digit sums of head (4nb+grp), channel D/16*n + u.
+template <int D, int NB>
+__device__ __forceinline__ void hist_wave(const DecodeDev& p, int b, int g, int pg_begin, int pg_end, int hl,
+                                          uint8_t* ring, float* mw, bool& poison, int lane) {
+  constexpr int NCH = D / 64;   // code words per token per K plane; V byte columns per lane
+  constexpr int NU = 4 * NCH;   // PV result column blocks per head block
+  constexpr int PLANE = D / 16; // bytes per token in one K plane
+  using S = Stage<D>;
+  using RG = Ring<D, NB>;
+  constexpr int NS = RG::kStages;
+  const int n = lane & 15, grp = lane >> 4;
+  const int G = p.G;
+  const int h_base = b * p.Hq + g * G;
+
+  v4i qa[NB][NCH];
+  float ca[NB], cb[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int hout = 4 * nb + grp;        // head whose results this lane holds
+    ca[nb] = hout < G ? p.qa[h_base + hout] : 0.0f;
+    cb[nb] = hout < G ? p.qb[h_base + hout] : 0.0f;
+    const bool row_ok = 4 * nb + (n >> 2) < G;   // head of the A row this lane supplies
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const v4i* src = reinterpret_cast<const v4i*>(p.qdig) +
+                       ((((size_t)b * p.n_kv + g) * NB + nb) * NCH + c) * kWave + lane;
+      qa[nb][c] = row_ok ? *src : v4i{0, 0, 0, 0};
+    }
+  }
+  wait_vmem(0);   // operands loaded before the page copies start counting
+
+  v4i pv[NB][NU];
+  float facc[NB][NU], mref[NB], lsum[NB], zsum[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    mref[nb] = -INFINITY;
+    lsum[nb] = 0.0f;
+    zsum[nb] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      pv[nb][u] = v4i{0, 0, 0, 0};
+      facc[nb][u] = 0.0f;
+    }
+  }
+  float smax = 0.0f, kw = 0.0f;
+
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_offset(ring));
+  uint8_t* planes = RG::kPlanesInK ? nullptr : ring + NS * S::kBytes;
+  const int count = pg_end - pg_begin;
+  // page ids (validated; an invalid page is staged from page 0 and skipped)
+  auto page_blk = [&](int pg) -> size_t {
+    const int pid = p.block_table[(size_t)b * p.max_pages + pg];
+    return (pid >= 0 && (int64_t)pid < p.n_pages) ? (size_t)pid * p.n_kv + g : (size_t)g;
+  };
+  auto page_ok = [&](int pg) -> bool {
+    const int pid = p.block_table[(size_t)b * p.max_pages + pg];
+    return pid >= 0 && (int64_t)pid < p.n_pages;
+  };
+  const int pre = count < NS - 1 ? count : NS - 1;
+  for (int i = 0; i < pre; ++i) stage_page<D>(p, page_blk(pg_begin + i), ring_lds + i * S::kBytes, lane);
+
+  for (int i = 0; i < count; ++i) {
+    const int pg = pg_begin + i;
+    if (i + NS - 1 < count)
+      stage_page<D>(p, page_blk(pg + NS - 1), ring_lds + ((i + NS - 1) % NS) * S::kBytes, lane);
+    const int ahead = min(NS - 1, count - 1 - i);
+    wait_vmem(ahead * S::kCopies);
+    if (!page_ok(pg)) {
+      poison = true;
+      continue;
+    }
+    const uint8_t* st = ring + (i % NS) * S::kBytes;
+    const int nv = min(kPage, hl - pg * kPage);
+
+    uint32_t kword[4 * NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const uint4 k4 = *reinterpret_cast<const uint4*>(st + S::kK + grp * kPage * PLANE + 4 * n * PLANE + 16 * c);
+      kword[4 * c] = k4.x; kword[4 * c + 1] = k4.y; kword[4 * c + 2] = k4.z; kword[4 * c + 3] = k4.w;
+    }
+    const uint4 ksz = *reinterpret_cast<const uint4*>(st + S::kKsz + 16 * n);
+    const uint4 vsz = *reinterpret_cast<const uint4*>(st + S::kVsz + 16 * n);
+    const uint32_t kw4[4] = {ksz.x, ksz.y, ksz.z, ksz.w};
+    const uint32_t vw4[4] = {vsz.x, vsz.y, vsz.z, vsz.w};
+    float sk[4], zk[4], sv[4], zv[4];
+    bool tv[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      tv[tb] = 4 * n + tb < nv;
+      sk[tb] = f16_to_f32(kw4[tb] & 0xffffu);
+      zk[tb] = f16_to_f32(kw4[tb] >> 16);
+      sv[tb] = tv[tb] ? f16_to_f32(vw4[tb] & 0xffffu) : 0.0f;
+      zv[tb] = tv[tb] ? f16_to_f32(vw4[tb] >> 16) : 0.0f;
+    }
+
+    // ---- QK, one head block at a time: token block tb holds token 4n+tb
+    float lg[NB][4];
+    bool need = false;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const bool hok = 4 * nb + grp < G;
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        v4i dq;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          const uint32_t w = kword[tb * NCH + c];
+          const v4i bop = v4i{code_mask(w, 0), code_mask(w, 1), code_mask(w, 2), code_mask(w, 3)};
+          dq = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[nb][c], bop, c == 0 ? v4i{0, 0, 0, 0} : dq, 0, 0, 0);
+        }
+        // digits: d0 + 2^8 d1 and d2 + 2^8 d3 are exact in int32
+        const int lo = dq.x + dq.y * 256, hi = dq.z + dq.w * 256;
+        const float dot = fmaf((float)hi, 65536.0f, (float)lo);
+        lg[nb][tb] = (tv[tb] && hok) ? fmaf(sk[tb] * ca[nb], dot, zk[tb] * cb[nb]) : -INFINITY;
+        need |= lg[nb][tb] > mref[nb] + kLazyThr;
+      }
+    }
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) need |= sv[tb] > kScaleSlack * smax;
+
+    if (__any(need)) {
+      // raise the reference maxima and the V-scale bound; fold the integer
+      // accumulators into fp32 under the old ones first
+      float s_new = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      s_new = fmaxf(smax, group16_max(s_new));
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const float t = fmaxf(fmaxf(lg[nb][0], lg[nb][1]), fmaxf(lg[nb][2], lg[nb][3]));
+        const float nm = fmaxf(mref[nb], group16_max(t));
+        const float alpha = exp2_or_zero(mref[nb], nm);
+        if (kw > 0.0f) {
+#pragma unroll
+          for (int u = 0; u < NU; ++u) {
+            facc[nb][u] = (facc[nb][u] + digits_to_f32(pv[nb][u]) * (code_scale_inv(u & 3) / kw)) * alpha;
+            pv[nb][u] = v4i{0, 0, 0, 0};
+          }
+        }
+        lsum[nb] *= alpha;
+        zsum[nb] *= alpha;
+        mref[nb] = nm;
+      }
+      smax = s_new;
+      kw = smax > 0.0f ? kFix / (exp2f(kLazyThr) * smax) : kFix / exp2f(kLazyThr);
+    }
+
+    // ---- weights p*scale_V as 30-bit fixed point, balanced digits,
+    // transposed into LDS planes [nb][head][digit][64 tokens]
+    uint8_t* pl = RG::kPlanesInK ? const_cast<uint8_t*>(st) + S::kK : planes;
+    __builtin_amdgcn_wave_barrier();   // every lane has read its K words
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      uint32_t dg[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const float pr = __builtin_amdgcn_exp2f(lg[nb][tb] - mref[nb]);   // exp2(-inf) = 0
+        lsum[nb] += pr;
+        zsum[nb] = fmaf(pr, zv[tb], zsum[nb]);
+        dg[tb] = balanced_digits((uint32_t)fmaf(pr * sv[tb], kw, 0.5f));
+      }
+      // 4x4 byte transpose: t_j byte tb = digit j of token 4n+tb
+      const uint32_t x01l = __builtin_amdgcn_perm(dg[1], dg[0], 0x05010400u);
+      const uint32_t x01h = __builtin_amdgcn_perm(dg[1], dg[0], 0x07030602u);
+      const uint32_t x23l = __builtin_amdgcn_perm(dg[3], dg[2], 0x05010400u);
+      const uint32_t x23h = __builtin_amdgcn_perm(dg[3], dg[2], 0x07030602u);
+      uint8_t* plane = pl + ((nb * 4 + grp) * 4) * kPage + 4 * n;
+      *reinterpret_cast<uint32_t*>(plane) = __builtin_amdgcn_perm(x23l, x01l, 0x05040100u);
+      *reinterpret_cast<uint32_t*>(plane + kPage) = __builtin_amdgcn_perm(x23l, x01l, 0x07060302u);
+      *reinterpret_cast<uint32_t*>(plane + 2 * kPage) = __builtin_amdgcn_perm(x23h, x01h, 0x05040100u);
+      *reinterpret_cast<uint32_t*>(plane + 3 * kPage) = __builtin_amdgcn_perm(x23h, x01h, 0x07060302u);
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- PV
+#pragma unroll
+    for (int bs = 0; bs < NCH; ++bs) {
+      const uint4 v4 = *reinterpret_cast<const uint4*>(st + S::kV + (NCH * n + bs) * kPage + 16 * grp);
+      const uint32_t r[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const v4i wa = *reinterpret_cast<const v4i*>(pl + ((nb * 4 + (n >> 2)) * 4 + (n & 3)) * kPage + 16 * grp);
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          const v4i bop = v4i{code_mask(r[0], pp), code_mask(r[1], pp), code_mask(r[2], pp), code_mask(r[3], pp)};
+          pv[nb][4 * bs + pp] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa, bop, pv[nb][4 * bs + pp], 0, 0, 0);
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  wait_vmem(0);
+
+  // ---- fold, reduce over the 16 lanes of each head, store (m, l, acc) per head
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const float l = group16_sum(lsum[nb]);
+    const float z = group16_sum(zsum[nb]);
+    const int h = 4 * nb + grp;
+    if (h < G) {
+      float* mh = mw + h * (D + 2);
+      if (n == 0) {
+        mh[0] = mref[nb];
+        mh[1] = l;
+      }
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const float part = kw > 0.0f ? digits_to_f32(pv[nb][u]) * (code_scale_inv(u & 3) / kw) : 0.0f;
+        mh[2 + NU * n + u] = facc[nb][u] + part + z;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 1. rotate the query: q_rot = q R_K[g]; MFMA digit operands and constants
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(128) void rotate_query_kernel(DecodeDev p) {
+  constexpr int NCH = D / 64, PLANE = D / 16;
   __shared__ float qs[D];
-  __shared__ float red[2];
+  __shared__ float red[2][2];
   const int bh = blockIdx.x;
-  const int h = bh % p.Hq, g = h / p.G;
+  const int b = bh / p.Hq, h = bh % p.Hq, g = h / p.G, hl = h % p.G;
   const int j = threadIdx.x;
   if (j < D) qs[j] = bf16_to_f32(p.q[(size_t)bh * D + j]);
   __syncthreads();
@@ -257,63 +519,75 @@ __global__ __launch_bounds__(128) void qrot_kernel(DecodeDev p) {
   if (j < D) {
     const float* R = p.r_k + (size_t)g * D * D;
     for (int i = 0; i < D; ++i) acc = fmaf(qs[i], R[i * D + j], acc);
-    p.qrot[(size_t)bh * D + j] = acc;
   }
-  const float s = wave_sum(j < D ? acc : 0.0f);
-  if ((j & (kWave - 1)) == 0) red[j / kWave] = s;
+  const float amax = wave_max(j < D ? fabsf(acc) : 0.0f);
+  const float asum = wave_sum(j < D ? acc : 0.0f);
+  if ((j & (kWave - 1)) == 0) {
+    red[0][j / kWave] = amax;
+    red[1][j / kWave] = asum;
+  }
   __syncthreads();
-  if (j == 0) p.qsum[bh] = red[0] + red[1];
+  const float maxabs = fmaxf(red[0][0], red[0][1]);
+  const float qsum = red[1][0] + red[1][1];
+  // kq: power of two with 16 * maxabs * kq <= 2^30
+  float kq = 1.0f;
+  if (maxabs > 0.0f) {
+    kq = exp2f(floorf(log2f(kFix / (16.0f * maxabs))));
+    if (16.0f * maxabs * kq > kFix) kq *= 0.5f;
+  }
+  if (j < D) {
+    const int pp = j & 3;                       // mask index of channel j
+    const float scale = kq * (pp == 0 ? 16.0f : pp == 1 ? 4.0f : 1.0f);
+    const uint32_t U = balanced_digits((uint32_t)(int)rintf(acc * scale));
+    const int ib = j >> 2;                      // code-row byte of channel j
+    const int kb = ib / PLANE, rem = ib % PLANE, c = rem >> 2, bb = rem & 3;
+    const int nb = hl >> 2, hr = hl & 3;
+    uint8_t* base = p.qdig + ((((size_t)b * p.n_kv + g) * p.NB + nb) * NCH + c) * kWave * 16;
+#pragma unroll
+    for (int dj = 0; dj < 4; ++dj) {
+      const int lane = 16 * kb + 4 * hr + dj;
+      base[lane * 16 + 4 * pp + bb] = (uint8_t)(U >> (8 * dj));
+    }
+  }
+  if (j == 0) {
+    p.qa[bh] = p.sm_log2 / (16.0f * kq);
+    p.qb[bh] = p.sm_log2 * qsum;
+  }
 }
 
+// ---------------------------------------------------------------------------
+// 2. scan: BF16 chunk blocks first (4 chunks per block), then history splits
+// ---------------------------------------------------------------------------
+#ifndef OSCAR_SCAN_WAVES_PER_SIMD
+#define OSCAR_SCAN_WAVES_PER_SIMD 2
+#endif
 template <int D, int G>
-__global__ __launch_bounds__(kBlock) void decode_main_kernel(DecodeDev p) {
-  constexpr int kMrg = 4 * G * (D + 2);
-  constexpr int kWbuf = 4 * kWave * G;
-  __shared__ float q_s[G * D];
-  __shared__ float qsum_s[G];
-  __shared__ float scratch[kMrg > kWbuf ? kMrg : kWbuf];
+__global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) void decode_main_kernel(DecodeDev p) {
+  constexpr int NB = (G + 3) / 4;
+  using RG = Ring<D, NB>;
+  constexpr int kHistBytes = 4 * RG::kWaveBytes;
+  constexpr int kBf16Bytes = (G * D + 4 * kWave * G) * 4;
+  constexpr int kSmem = kHistBytes > kBf16Bytes ? kHistBytes : kBf16Bytes;
+  static_assert(G * (D + 2) * 4 <= RG::kWaveBytes, "merge slot must fit the wave's ring");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
   __shared__ int flags[4];
-  const int b = blockIdx.z, g = blockIdx.y, x = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int h0 = g * G;
-  const size_t part = (size_t)G * (D + 2);
-  WaveAcc<D, G> st;
-  acc_init(st);
+  const int units = p.B * p.n_kv;
+  const int id = blockIdx.x;
   bool poison = false;
-  float* wbuf = scratch + wave * kWave * G;
 
-  if (x < p.splits) {  // ---- INT2 history split (block-uniform branch)
-    for (int e = tid; e < G * D; e += kBlock) q_s[e] = p.qrot[((size_t)b * p.Hq + h0) * D + e];
-    if (tid < G) qsum_s[tid] = p.qsum[(size_t)b * p.Hq + h0 + tid];
+  if (id < units * p.bf_blocks) {  // ---- BF16 sink / recent chunks (block-uniform)
+    float* q_s = reinterpret_cast<float*>(smem);
+    float* wbuf = q_s + G * D;
+    const int unit = id % units, cb = id / units;
+    const int b = unit / p.n_kv, g = unit % p.n_kv;
+    const size_t part = (size_t)G * (D + 2);
+    for (int e = tid; e < G * D; e += kBlock) q_s[e] = bf16_to_f32(p.q[((size_t)b * p.Hq + g * G) * D + e]);
     __syncthreads();
-    int hl = p.hist_len[b];
-    if (hl < 0 || hl > p.max_hist_len) {
-      poison = true;
-      hl = 0;
-    }
-    const int hp = (hl + kPage - 1) / kPage;
-    const int pb = x * p.pps;
-    const int pe = min(pb + p.pps, hp);
-    for (int pg = pb + wave; pg < pe; pg += kBlock / kWave) {
-      const int pid = p.block_table[(size_t)b * p.max_pages + pg];
-      if (pid < 0 || (int64_t)pid >= p.n_pages) {
-        poison = true;
-        continue;
-      }
-      const int nv = min(kPage, hl - pg * kPage);
-      const size_t blk = (size_t)pid * p.n_kv + g;
-      int2_page<D, G>(st, q_s, qsum_s, p.sm_log2, p.k_codes + blk * (kPage * D / 4),
-                      p.v_codes + blk * (kPage * D / 4), p.k_sz + blk * kPage, p.v_sz + blk * kPage,
-                      nv, wbuf, lane);
-    }
-    __syncthreads();  // wbuf and the merge area share scratch
-    block_merge_write<D, G>(st, poison, scratch, flags,
-                            p.hpart + (((size_t)b * p.n_kv + g) * p.splits + x) * part, tid);
-  } else {  // ---- BF16 sink / recent chunks, one per wave
-    for (int e = tid; e < G * D; e += kBlock) q_s[e] = bf16_to_f32(p.q[((size_t)b * p.Hq + h0) * D + e]);
-    __syncthreads();
-    const int c = (x - p.splits) * (kBlock / kWave) + wave;
+    const int c = cb * (kBlock / kWave) + wave;
     if (c < p.chunks) {
+      WaveAcc<D, G> st;
+      acc_init(st);
       const uint16_t *kb, *vb;
       int nv;
       if (c < p.sink_chunks) {
@@ -339,63 +613,140 @@ __global__ __launch_bounds__(kBlock) void decode_main_kernel(DecodeDev p) {
         kb = p.recent_k + off;
         vb = p.recent_v + off;
       }
-      if (nv > 0) bf16_tile<D, G>(st, q_s, p.sm_log2, kb, vb, nv, wbuf, lane);
-      write_wave_partial<D, G>(st, poison, p.bpart + (((size_t)b * p.n_kv + g) * p.chunks + c) * part,
-                               lane);
+      if (nv > 0) bf16_tile<D, G>(st, q_s, p.sm_log2, kb, vb, nv, wbuf + wave * kWave * G, lane);
+      float* dst = p.bpart + (((size_t)b * p.n_kv + g) * p.chunks + c) * part;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        if (lane == 0) {
+          dst[h * (D + 2)] = st.m[h];
+          dst[h * (D + 2) + 1] = poison ? NAN : st.l[h];
+        }
+#pragma unroll
+        for (int k = 0; k < D / kWave; ++k) dst[h * (D + 2) + 2 + lane + kWave * k] = st.a[h][k];
+      }
     }
+    return;
   }
+
+  // ---- INT2 history split: waves take contiguous page ranges
+  const int hid = id - units * p.bf_blocks;
+  const int unit = hid % units, split = hid / units;
+  const int b = unit / p.n_kv, g = unit % p.n_kv;
+  int hl = p.hist_len[b];
+  if (hl < 0 || hl > p.max_hist_len) {
+    poison = true;
+    hl = 0;
+  }
+  const int hp = (hl + kPage - 1) / kPage;
+  const int pb = split * p.pps;
+  const int pe = min(pb + p.pps, hp);
+  const int per_wave = (p.pps + 3) / 4;
+  const int wb = min(pb + wave * per_wave, pe);
+  const int we = min(wb + per_wave, pe);
+  uint8_t* ring = smem + wave * RG::kWaveBytes;
+  // the wave's merge slot [G][D+2] = (m, l, acc) overlays its own ring once the scan is done
+  hist_wave<D, NB>(p, b, g, wb, we, hl, ring, reinterpret_cast<float*>(ring), poison, lane);
+  if (lane == 0) flags[wave] = poison ? 1 : 0;
+  __syncthreads();
+  combine_block(reinterpret_cast<const float*>(smem), RG::kWaveBytes / 4, flags,
+                p.hpart + (((size_t)b * p.n_kv + g) * p.splits + split) * (size_t)G * (D + 2), G, D, tid);
+}
+
+// ---------------------------------------------------------------------------
+// 3. merge: LSE over history splits, * R_V^T, LSE with BF16 chunks, normalise
+// ---------------------------------------------------------------------------
+// Block-wide LSE merge of n partials (stride floats apart) into acc[D] (LDS);
+// returns (M, L) with L = sum exp2(m_i - M) l_i.
+template <int D>
+__device__ __forceinline__ float2 lse_merge(const float* __restrict__ parts, int n, size_t stride, float* w_s,
+                                            float* acc_s, float* red, int tid) {
+  constexpr int TPC = kBlock / D;   // threads per channel
+  float m = -INFINITY;
+  for (int s = tid; s < n; s += kBlock) m = fmaxf(m, parts[s * stride]);
+  m = wave_max(m);
+  if ((tid & (kWave - 1)) == 0) red[tid / kWave] = m;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float l = 0.0f;
+  for (int s = tid; s < n; s += kBlock) {
+    const float f = exp2_or_zero(parts[s * stride], M);
+    w_s[s] = f;
+    l += f * parts[s * stride + 1];
+  }
+  l = wave_sum(l);
+  if ((tid & (kWave - 1)) == 0) red[tid / kWave] = l;
+  __syncthreads();
+  const float L = red[0] + red[1] + red[2] + red[3];
+  const int c = tid % D, part = tid / D;
+  float a = 0.0f;
+  for (int s = part; s < n; s += TPC) a = fmaf(w_s[s], parts[s * stride + 2 + c], a);
+  acc_s[part * D + c] = a;
+  __syncthreads();
+  if (part == 0) {
+#pragma unroll
+    for (int k = 1; k < TPC; ++k) a += acc_s[k * D + c];
+    acc_s[c] = a;
+  }
+  __syncthreads();
+  return make_float2(M, L);
 }
 
 template <int D>
-__global__ __launch_bounds__(128) void merge_kernel(DecodeDev p) {
+__global__ __launch_bounds__(kBlock) void merge_kernel(DecodeDev p, int max_parts) {
+  constexpr int TPC = kBlock / D;
+  extern __shared__ float w_s[];   // max_parts weights
+  __shared__ float acc_s[kBlock];
   __shared__ float arot[D];
+  __shared__ float red[4];
   const int bh = blockIdx.x;
   const int b = bh / p.Hq, h = bh % p.Hq, g = h / p.G, kh = h % p.G;
-  const int c = threadIdx.x;
+  const int tid = threadIdx.x;
   const size_t stride = (size_t)p.G * (D + 2);
-  // history partials (rotated space)
-  const float* hp = p.hpart + ((size_t)b * p.n_kv + g) * p.splits * stride + (size_t)kh * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < p.splits; ++s) M = fmaxf(M, hp[s * stride]);
-  float L = 0.0f, A = 0.0f;
-  for (int s = 0; s < p.splits; ++s) {
-    const float f = exp2_or_zero(hp[s * stride], M);
-    L += f * hp[s * stride + 1];
-    if (c < D) A += f * hp[s * stride + 2 + c];
-  }
-  if (c < D) arot[c] = A;
-  __syncthreads();
+  float2 mh = make_float2(-INFINITY, 0.0f);
   float oh = 0.0f;
-  if (c < D && p.splits > 0) {
-    const float* Rrow = p.r_v + ((size_t)g * D + c) * D;  // out[c] = sum_j arot[j] * R_V[c][j]
-    for (int j2 = 0; j2 < D; ++j2) oh = fmaf(arot[j2], Rrow[j2], oh);
+  if (p.splits > 0) {
+    const float* hp = p.hpart + ((size_t)b * p.n_kv + g) * p.splits * stride + (size_t)kh * (D + 2);
+    mh = lse_merge<D>(hp, p.splits, stride, w_s, acc_s, red, tid);
+    if (tid < D) arot[tid] = acc_s[tid];
+    __syncthreads();
+    // out_hist[i] = sum_j arot[j] * R_V[g][i][j]: TPC threads per row, contiguous segments
+    const int i = tid / TPC, seg = tid % TPC;
+    const float* Rrow = p.r_v + ((size_t)g * D + i) * D + seg * (D / TPC);
+    float s = 0.0f;
+#pragma unroll 8
+    for (int k = 0; k < D / TPC; ++k) s = fmaf(arot[seg * (D / TPC) + k], Rrow[k], s);
+#pragma unroll
+    for (int o = 1; o < TPC; o <<= 1) s += __shfl_xor(s, o, kWave);
+    oh = s;
+    __syncthreads();
   }
-  // BF16 partials (unrotated)
-  const float* bp = p.bpart + ((size_t)b * p.n_kv + g) * p.chunks * stride + (size_t)kh * (D + 2);
-  float Mb = -INFINITY;
-  for (int s = 0; s < p.chunks; ++s) Mb = fmaxf(Mb, bp[s * stride]);
-  float Lb = 0.0f, Ab = 0.0f;
-  for (int s = 0; s < p.chunks; ++s) {
-    const float f = exp2_or_zero(bp[s * stride], Mb);
-    Lb += f * bp[s * stride + 1];
-    if (c < D) Ab += f * bp[s * stride + 2 + c];
+  float2 mb = make_float2(-INFINITY, 0.0f);
+  float ob = 0.0f;
+  if (p.chunks > 0) {
+    const float* bp = p.bpart + ((size_t)b * p.n_kv + g) * p.chunks * stride + (size_t)kh * (D + 2);
+    mb = lse_merge<D>(bp, p.chunks, stride, w_s, acc_s, red, tid);
   }
-  const float Mt = fmaxf(M, Mb);
-  const float fh = exp2_or_zero(M, Mt), fb = exp2_or_zero(Mb, Mt);
-  const float den = fh * L + fb * Lb;
-  float o;
-  if (isnan(den)) o = NAN;
-  else o = (den > 0.0f) ? (fh * oh + fb * Ab) / den : 0.0f;
-  if (c < D) p.out[(size_t)bh * D + c] = o;
+  const int i = tid / TPC;
+  if (tid % TPC == 0) {
+    if (p.chunks > 0) ob = acc_s[i];
+    const float Mt = fmaxf(mh.x, mb.x);
+    const float fh = exp2_or_zero(mh.x, Mt), fb = exp2_or_zero(mb.x, Mt);
+    const float den = fh * mh.y + fb * mb.y;
+    float o;
+    if (isnan(den)) o = NAN;
+    else o = (den > 0.0f) ? (fh * oh + fb * ob) / den : 0.0f;
+    p.out[(size_t)bh * D + i] = o;
+  }
 }
 
 // ---- BF16 paged comparator ---------------------------------------------
 template <int D, int G>
 __global__ __launch_bounds__(kBlock) void bf16_paged_kernel(Bf16Dev p) {
-  constexpr int kMrg = 4 * G * (D + 2);
   constexpr int kWbuf = 4 * kWave * G;
   __shared__ float q_s[G * D];
-  __shared__ float scratch[kMrg > kWbuf ? kMrg : kWbuf];
+  __shared__ float mrg[4 * G * (D + 2)];
+  __shared__ float wbuf[kWbuf];
   __shared__ int flags[4];
   const int b = blockIdx.z, g = blockIdx.y, x = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -403,7 +754,6 @@ __global__ __launch_bounds__(kBlock) void bf16_paged_kernel(Bf16Dev p) {
   WaveAcc<D, G> st;
   acc_init(st);
   bool poison = false;
-  float* wbuf = scratch + wave * kWave * G;
   for (int e = tid; e < G * D; e += kBlock) q_s[e] = bf16_to_f32(p.q[((size_t)b * p.Hq + h0) * D + e]);
   __syncthreads();
   int cl = p.ctx_len[b];
@@ -421,11 +771,13 @@ __global__ __launch_bounds__(kBlock) void bf16_paged_kernel(Bf16Dev p) {
     }
     const size_t off = ((size_t)pid * p.n_kv + g) * kPage * D;
     bf16_tile<D, G>(st, q_s, p.sm_log2, p.k_pages + off, p.v_pages + off, min(kPage, cl - pg * kPage),
-                    wbuf, lane);
+                    wbuf + wave * kWave * G, lane);
   }
+  store_wave_state<D, G>(st, mrg + wave * G * (D + 2), lane);
+  if (lane == 0) flags[wave] = poison ? 1 : 0;
   __syncthreads();
-  block_merge_write<D, G>(st, poison, scratch, flags,
-                          p.part + (((size_t)b * p.n_kv + g) * p.splits + x) * (size_t)G * (D + 2), tid);
+  combine_block(mrg, G * (D + 2), flags, p.part + (((size_t)b * p.n_kv + g) * p.splits + x) * (size_t)G * (D + 2),
+                G, D, tid);
 }
 
 template <int D>
@@ -451,10 +803,9 @@ __global__ __launch_bounds__(128) void merge_plain_kernel(Bf16Dev p) {
 
 template <int D, int G>
 void launch_main(const DecodeDev& dv, hipStream_t stream) {
-  const unsigned nbf = (unsigned)((dv.chunks + 3) / 4);
-  const dim3 grid((unsigned)dv.splits + nbf, (unsigned)dv.n_kv, (unsigned)dv.B);
-  if (grid.x == 0) return;
-  decode_main_kernel<D, G><<<grid, kBlock, 0, stream>>>(dv);
+  const long blocks = (long)dv.B * dv.n_kv * (dv.bf_blocks + dv.splits);
+  if (blocks == 0) return;
+  decode_main_kernel<D, G><<<dim3((unsigned)blocks), kBlock, 0, stream>>>(dv);
 }
 
 template <int D>
@@ -485,16 +836,15 @@ void launch_bf16_g(const Bf16Dev& dv, hipStream_t stream) {
   }
 }
 
-}  // namespace
-
-namespace {
 DecodeDev make_dev(const oscar_decode_args& a, const DecodePlan& plan, char* ws) {
   DecodeDev dv{};
   dv.B = a.batch; dv.Hq = a.n_q_heads; dv.n_kv = a.n_kv_heads; dv.G = a.n_q_heads / a.n_kv_heads;
+  dv.NB = (dv.G + 3) / 4;
   dv.sink_cap = a.sink_cap; dv.recent_cap = a.recent_cap;
   dv.max_hist_len = a.max_hist_len; dv.max_pages = a.max_pages;
   dv.splits = plan.splits; dv.pps = plan.pages_per_split;
   dv.chunks = plan.chunks; dv.sink_chunks = plan.sink_chunks;
+  dv.bf_blocks = (plan.chunks + 3) / 4;
   dv.sm_log2 = a.sm_scale * kLog2e;
   dv.n_pages = a.n_pages;
   dv.q = a.q; dv.sink_k = a.sink_k; dv.sink_v = a.sink_v; dv.recent_k = a.recent_k; dv.recent_v = a.recent_v;
@@ -504,12 +854,14 @@ DecodeDev make_dev(const oscar_decode_args& a, const DecodePlan& plan, char* ws)
   dv.k_sz = reinterpret_cast<const uint32_t*>(a.k_sz);
   dv.v_sz = reinterpret_cast<const uint32_t*>(a.v_sz);
   dv.r_k = a.r_k; dv.r_v = a.r_v; dv.out = a.out;
-  dv.qrot = reinterpret_cast<float*>(ws + plan.off_qrot);
-  dv.qsum = reinterpret_cast<float*>(ws + plan.off_qsum);
+  dv.qdig = reinterpret_cast<uint8_t*>(ws + plan.off_qdig);
+  dv.qa = reinterpret_cast<float*>(ws + plan.off_qa);
+  dv.qb = reinterpret_cast<float*>(ws + plan.off_qb);
   dv.hpart = reinterpret_cast<float*>(ws + plan.off_hpart);
   dv.bpart = reinterpret_cast<float*>(ws + plan.off_bpart);
   return dv;
 }
+
 }  // namespace
 
 hipError_t launch_decode_phase(int phase, const oscar_decode_args& a, const DecodePlan& plan, char* ws,
@@ -520,15 +872,17 @@ hipError_t launch_decode_phase(int phase, const oscar_decode_args& a, const Deco
   const bool d128 = a.head_dim == 128;
   if (phase == kPhaseRotate) {
     if (plan.splits > 0) {
-      if (d128) qrot_kernel<128><<<nbh, 128, 0, stream>>>(dv);
-      else qrot_kernel<64><<<nbh, 128, 0, stream>>>(dv);
+      if (d128) rotate_query_kernel<128><<<nbh, 128, 0, stream>>>(dv);
+      else rotate_query_kernel<64><<<nbh, 128, 0, stream>>>(dv);
     }
   } else if (phase == kPhaseScan) {
     if (d128) launch_main_g<128>(dv, stream);
     else launch_main_g<64>(dv, stream);
   } else {
-    if (d128) merge_kernel<128><<<nbh, 128, 0, stream>>>(dv);
-    else merge_kernel<64><<<nbh, 128, 0, stream>>>(dv);
+    const int maxp = plan.splits > plan.chunks ? plan.splits : plan.chunks;
+    const size_t lds = (size_t)(maxp > 0 ? maxp : 1) * sizeof(float);
+    if (d128) merge_kernel<128><<<nbh, kBlock, lds, stream>>>(dv, maxp);
+    else merge_kernel<64><<<nbh, kBlock, lds, stream>>>(dv, maxp);
   }
   return hipGetLastError();
 }

@@ -170,3 +170,29 @@ def test_bf16_comparator_ragged():
     ref = oracle.bf16_paged_attn_ref(q, kp, vp, table, ctx, 1 / np.sqrt(d))
     got = _gpu_bf16(q, kp, vp, table, ctx, 1 / np.sqrt(d))
     compare_out(got, ref, what="bf16 ragged")
+
+
+def test_writes_stay_inside_workspace_and_output():
+    """Canary bytes around the workspace and the output must survive a call."""
+    cfg, pools = ragged_cache(21, B=2, n_kv=2, G=8, d=128, sink=(64, 3), hist=(300, 65), recent=(256, 9))
+    B, Hq, d = cfg["q"].shape
+    mh = int(cfg["hist_len"].max())
+    need = hip.oscar_decode_workspace_bytes(B, Hq, 2, d, mh, 64, 256)
+    guard = 1 << 16
+    ws_full = torch.full((need + 2 * guard,), 0xAB, dtype=torch.uint8, device="cuda")
+    ws = ws_full[guard:guard + need]
+    out_full = torch.full((B * Hq * d + 2 * 4096,), 12345.0, dtype=torch.float32, device="cuda")
+    out = out_full[4096:4096 + B * Hq * d].view(B, Hq, d)
+    kc, vc, ks, vs = (dev(p) for p in pools)
+    hip.oscar_decode_attn(q=dev(cfg["q"]), sink_k=dev(cfg["sink_k"]), sink_v=dev(cfg["sink_v"]),
+                          recent_k=dev(cfg["recent_k"]), recent_v=dev(cfg["recent_v"]),
+                          sink_len=dev(cfg["sink_len"]), recent_len=dev(cfg["recent_len"]),
+                          hist_len=dev(cfg["hist_len"]), max_hist_len=mh, k_codes=kc, v_codes=vc, k_sz=ks, v_sz=vs,
+                          block_table=dev(cfg["block_table"]), r_k=dev(cfg["r_k"]), r_v=dev(cfg["r_v"]), out=out,
+                          workspace=ws, sm_scale=float(cfg["sm_scale"]))
+    torch.cuda.synchronize()
+    wsh = host(ws_full)
+    assert np.all(wsh[:guard] == 0xAB) and np.all(wsh[guard + need:] == 0xAB), "write outside the workspace"
+    oh = host(out_full)
+    assert np.all(oh[:4096] == 12345.0) and np.all(oh[4096 + B * Hq * d:] == 12345.0), "write outside out"
+    compare_out(host(out), oracle.decode_attn_ref(cfg, *pools), what="canary run")
