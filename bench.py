@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB device copy (torch.neg) 3 times: the known-size "
+                         "kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
 
 
@@ -180,6 +183,17 @@ def main():
     ms_per_step = sec * 1e3 / K
     log(f"step: {ms_per_step * 1e3:.2f} us (wall {wall * 1e3 / K:.2f} us)")
 
+    if args.copy_probe:
+        n = (256 << 20) // 4
+        src = torch.randn(n, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"copy probe: 3 x torch.neg over {n * 4} bytes read + {n * 4} bytes written")
+        del src, dst
+
     # ---- dominant kernel: the scan, R launches back to back per graph replay
     g_scan = capture(lambda r: hip.oscar_decode_scan(args=dargs[r]), range(R))
     n_scan = max(1, K // R)
@@ -204,7 +218,7 @@ def main():
                    "history": hl, "recent": int(cfg["recent_len"][0]), "page_tokens": 64,
                    "cache_replicas": R, "step": "demote K,V of 1 token/request + decode attention"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload),
                      "kernel": "decode_main_kernel (oscar_decode_scan)", "kernel_us": scan_us,
                      "bytes_per_launch": scan_bytes},
         "kv_tokens_per_s": float(cfg["hist_len"].sum() + cfg["sink_len"].sum() + cfg["recent_len"].sum())
@@ -247,6 +261,40 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+SCAN_SOURCES = ("bit_rotated_kv_attn_amd/csrc/decode.hip", "bit_rotated_kv_attn_amd/csrc/common.hpp")
+
+
+def scan_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in SCAN_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per scan launch from the committed counter summary of this
+    workload (FETCH_SIZE + WRITE_SIZE, each scaled by the copy-kernel
+    calibration), or None when the summary is missing or was taken on other
+    kernel sources than the ones built now."""
+    path = os.path.join(ROOT, "profiles", f"traffic_decode_main_kernel_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256_16") != scan_source_hash():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def ensure_free_slot(cfg):

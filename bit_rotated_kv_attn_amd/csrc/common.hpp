@@ -58,11 +58,18 @@ struct DecodePlan {
   size_t off_qdig, off_qa, off_qb, off_hpart, off_bpart, total;
 };
 
-#ifndef OSCAR_TARGET_BLOCKS
-#define OSCAR_TARGET_BLOCKS 1024
+#ifndef OSCAR_RESIDENT_BLOCKS
+#define OSCAR_RESIDENT_BLOCKS 512
 #endif
-constexpr int kTargetBlocks = OSCAR_TARGET_BLOCKS;  // history blocks per launch the split policy aims for
-constexpr int kMaxPagesPerSplit = 4096;   // keeps the int32 PV accumulators far from overflow
+// Blocks of the scan launch that are resident at once on MI355X (256 CUs,
+// two 4-wave scan blocks per CU).  The split policy sizes the history splits
+// so that history and BF16 blocks together fill them in one round: every wave
+// then pays the latency of its first page once, and no second round of
+// blocks runs on a partly idle chip.
+constexpr int kResidentBlocks = OSCAR_RESIDENT_BLOCKS;
+// at most 64 pages per wave (one page id per lane), which also keeps the int32
+// PV accumulators far from overflow
+constexpr int kMaxPagesPerSplit = 4 * 64;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -72,17 +79,19 @@ inline DecodePlan make_decode_plan(int B, int Hq, int n_kv, int d, int max_hist_
   const int G = Hq / n_kv;
   const int NB = (G + 3) / 4;
   p.hist_pages = (max_hist_len + kPage - 1) / kPage;
+  p.sink_chunks = (sink_cap + kPage - 1) / kPage;
+  p.chunks = p.sink_chunks + (recent_cap + kPage - 1) / kPage;
   if (p.hist_pages > 0) {
     const long units = (long)(B > 0 ? B : 1) * n_kv;
-    long s0 = (kTargetBlocks + units - 1) / units;
+    long target = kResidentBlocks - units * ((p.chunks + 3) / 4);   // blocks left for history
+    if (target < units) target = units;
+    long s0 = (target + units - 1) / units;
     const long s_min = (p.hist_pages + kMaxPagesPerSplit - 1) / kMaxPagesPerSplit;
     if (s0 < s_min) s0 = s_min;
     if (s0 > p.hist_pages) s0 = p.hist_pages;
     p.pages_per_split = (int)((p.hist_pages + s0 - 1) / s0);
     p.splits = (p.hist_pages + p.pages_per_split - 1) / p.pages_per_split;
   }
-  p.sink_chunks = (sink_cap + kPage - 1) / kPage;
-  p.chunks = p.sink_chunks + (recent_cap + kPage - 1) / kPage;
   const size_t part = (size_t)G * (d + 2) * sizeof(float);
   size_t off = 0;
   p.off_qdig = off;  off = align256(off + (size_t)B * n_kv * NB * (d / 64) * 64 * 16);
@@ -105,7 +114,7 @@ inline Bf16Plan make_bf16_plan(int B, int Hq, int n_kv, int d, int max_ctx_len) 
   p.ctx_pages = (max_ctx_len + kPage - 1) / kPage;
   if (p.ctx_pages > 0) {
     const long units = (long)(B > 0 ? B : 1) * n_kv;
-    long s0 = (kTargetBlocks + units - 1) / units;
+    long s0 = (kResidentBlocks + units - 1) / units;
     if (s0 < 1) s0 = 1;
     if (s0 > p.ctx_pages) s0 = p.ctx_pages;
     p.pages_per_split = (int)((p.ctx_pages + s0 - 1) / s0);

@@ -43,7 +43,6 @@ constexpr uint32_t kMask2 = 0x30303030u;  // field 2 (x16); field 3 is shifted i
 constexpr float kLazyThr = 8.0f;          // raise the reference max only past +2^8
 constexpr float kScaleSlack = 1.75f;      // refold when a V scale exceeds 1.75x the running max
 constexpr float kFix = 1073741824.0f;     // 2^30: fixed-point range of digits
-constexpr int kPlanePad = 80;             // bytes per LDS digit plane (64 tokens + pad, 16-aligned)
 
 struct DecodeDev {
   int B, Hq, n_kv, G, NB, sink_cap, recent_cap, max_hist_len, max_pages;
@@ -96,17 +95,36 @@ __device__ __forceinline__ float digits_to_f32(v4i d) {
   return fmaf((float)d.w, 16777216.0f, fmaf((float)d.z, 65536.0f, fmaf((float)d.y, 256.0f, (float)d.x)));
 }
 
+// Zero an accumulator in its own registers.  A plain assignment of 0 in the
+// rarely taken rescale branch makes the compiler materialise zeros and copy
+// the accumulators on every page at the branch join.
+__device__ __forceinline__ void clear_in_place(v4i& a) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    int x = a[k];
+    asm volatile("v_mov_b32 %0, 0" : "+v"(x));
+    a[k] = x;
+  }
+}
+
 __device__ __forceinline__ uint32_t balanced_digits(uint32_t x) {  // x in [-2^30, 2^30] two's complement
   return (x + 0x80808080u) ^ 0x80808080u;
 }
 
 // ---------------------------------------------------------------------------
-// VALU path for BF16 tiles (sink / recent windows and the BF16 comparator)
+// BF16 tiles (sink / recent windows and the BF16 comparator): 64 tokens of one
+// KV head.  QK runs on the matrix cores (v_mfma_f32_16x16x32_bf16: q and K are
+// bf16 already, so products are exact and sums fp32); PV runs on the VALU in
+// fp32 from a V tile staged in LDS.  All global loads of a tile are issued
+// together (bf16_load) before any is used.
 // ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
 template <int D, int G>
-struct WaveAcc {
+struct WaveAcc {            // online-softmax state, replicated in every lane
   float m[G], l[G];
-  float a[G][D / kWave];
+  float a[G][D / kWave];    // channels (D/64)*lane + k
 };
 
 template <int D, int G>
@@ -120,53 +138,137 @@ __device__ __forceinline__ void acc_init(WaveAcc<D, G>& s) {
   }
 }
 
-// One tile of up to 64 BF16 tokens (lane = token for QK, lane = channel for
-// PV); token t's row at kbase + t*D.
+template <int D>
+struct Bf16Tile {
+  static constexpr int KK = D / 32;   // MFMA k-steps per token block
+  static constexpr int VC = D / 8;    // 16-byte V chunks per lane
+  uint4 k[4][KK];                     // B operands: token 16*tb + lane%16, channels 32kk + 8*(lane/16) ..+7
+  uint4 v[VC];                        // V chunk lane + 64j of the [64][D] tile
+};
+
+// LDS bytes per wave for one BF16 tile: V tile, weights [64][G], reductions
 template <int D, int G>
-__device__ __forceinline__ void bf16_tile(WaveAcc<D, G>& st, const float* qu, float sm_log2,
-                                          const uint16_t* __restrict__ kbase,
-                                          const uint16_t* __restrict__ vbase, int n_valid,
-                                          float* wbuf, int lane) {
-  const bool valid = lane < n_valid;
-  float dot[G];
+constexpr int bf16_lds_bytes() { return 64 * D * 2 + 64 * G * 4 + 3 * 16 * 4; }
+
+// q rows of the G heads as MFMA A operands (rows >= G are zero)
+template <int D, int G>
+__device__ __forceinline__ void bf16_q_operands(bf16x8* qa, const uint16_t* __restrict__ qrows, int lane) {
+  const int r = lane & 15, kg = lane >> 4;
 #pragma unroll
-  for (int h = 0; h < G; ++h) dot[h] = 0.0f;
-  if (valid) {
-    const uint16_t* krow = kbase + (size_t)lane * D;
-#pragma unroll 4
-    for (int c8 = 0; c8 < D; c8 += 8) {
-      const uint4 v = *reinterpret_cast<const uint4*>(krow + c8);
-      const uint32_t e[4] = {v.x, v.y, v.z, v.w};
+  for (int kk = 0; kk < D / 32; ++kk) {
+    const uint4 x = r < G ? *reinterpret_cast<const uint4*>(qrows + (size_t)r * D + 32 * kk + 8 * kg)
+                          : make_uint4(0, 0, 0, 0);
+    qa[kk] = __builtin_bit_cast(bf16x8, x);
+  }
+}
+
+// Tokens at or past nv are neither read nor used.
+template <int D>
+__device__ __forceinline__ void bf16_load(Bf16Tile<D>& t, const uint16_t* __restrict__ kbase,
+                                          const uint16_t* __restrict__ vbase, int nv, int lane) {
+  const int r = lane & 15, kg = lane >> 4;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float k0 = __uint_as_float(e[q] << 16), k1 = __uint_as_float(e[q] & 0xffff0000u);
+  for (int tb = 0; tb < 4; ++tb) {
+    const int tok = 16 * tb + r;
 #pragma unroll
-        for (int h = 0; h < G; ++h)
-          dot[h] = fmaf(qu[h * D + c8 + 2 * q + 1], k1, fmaf(qu[h * D + c8 + 2 * q], k0, dot[h]));
-      }
+    for (int kk = 0; kk < D / 32; ++kk)
+      t.k[tb][kk] = tok < nv ? *reinterpret_cast<const uint4*>(kbase + (size_t)tok * D + 32 * kk + 8 * kg)
+                             : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < D / 8; ++j) {
+    const int ch = lane + kWave * j, tok = ch / (D / 8);
+    t.v[j] = tok < nv ? *reinterpret_cast<const uint4*>(vbase + (size_t)tok * D + 8 * (ch % (D / 8)))
+                      : make_uint4(0, 0, 0, 0);
+  }
+}
+
+template <int D, int G>
+__device__ __forceinline__ void bf16_compute(WaveAcc<D, G>& st, const Bf16Tile<D>& t, const bf16x8* qa,
+                                             float sm_log2, int nv, uint8_t* lds, int lane) {
+  constexpr int CPL = D / kWave;
+  uint16_t* vt = reinterpret_cast<uint16_t*>(lds);            // [64][D]
+  float* w = reinterpret_cast<float*>(lds + 64 * D * 2);     // [64][G]
+  float* red = w + 64 * G;                                    // [3][16]
+  const int r = lane & 15, kg = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < D / 8; ++j) *reinterpret_cast<uint4*>(vt + 8 * (lane + kWave * j)) = t.v[j];
+
+  // QK: lane (r, kg) holds heads 4kg+i of token 16tb + r
+  float lg[4][4], mloc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mloc[i] = -INFINITY;
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    v4f s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], __builtin_bit_cast(bf16x8, t.k[tb][kk]), s, 0, 0, 0);
+    const bool ok = 16 * tb + r < nv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lg[tb][i] = ok ? sm_log2 * s[i] : -INFINITY;
+      mloc[i] = fmaxf(mloc[i], lg[tb][i]);
     }
   }
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float lg = valid ? sm_log2 * dot[h] : -INFINITY;
-    const float mt = wave_max(lg);
-    const float mn = fmaxf(st.m[h], mt);
-    const float alpha = exp2_or_zero(st.m[h], mn);
-    const float pr = valid ? exp2f(lg - mn) : 0.0f;
-    st.l[h] = st.l[h] * alpha + wave_sum(pr);
+  for (int i = 0; i < 4; ++i) {
+    mloc[i] = group16_max(mloc[i]);
+    if (r == 0 && 4 * kg + i < G) red[4 * kg + i] = mloc[i];
+  }
+  __builtin_amdgcn_wave_barrier();
+  float mnew[G], alpha[G];
 #pragma unroll
-    for (int k = 0; k < D / kWave; ++k) st.a[h][k] *= alpha;
-    st.m[h] = mn;
-    wbuf[lane * G + h] = pr;
+  for (int h = 0; h < G; ++h) {
+    mnew[h] = fmaxf(st.m[h], red[h]);
+    alpha[h] = exp2_or_zero(st.m[h], mnew[h]);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) red[16 + h] = mnew[h];
+  }
+  __builtin_amdgcn_wave_barrier();
+  // weights p = exp2(logit - m) into w[token][head]; row sums per head
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * kg + i;
+    if (4 * kg < G) {   // lane groups past the last head hold no rows
+      const float m = red[16 + (h < G ? h : 0)];
+      float ls = 0.0f;
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const float pr = exp2_or_zero(lg[tb][i], m);
+        ls += pr;
+        if (h < G) w[(16 * tb + r) * G + h] = pr;
+      }
+      ls = group16_sum(ls);
+      if (r == 0 && h < G) red[32 + h] = ls;
+    }
   }
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
-  for (int k = 0; k < D / kWave; ++k) {
-    const int c = lane + kWave * k;
-    for (int t = 0; t < n_valid; ++t) {
-      const float v = bf16_to_f32(vbase[(size_t)t * D + c]);
+  for (int h = 0; h < G; ++h) {
+    st.l[h] = st.l[h] * alpha[h] + red[32 + h];
+    st.m[h] = mnew[h];
 #pragma unroll
-      for (int h = 0; h < G; ++h) st.a[h][k] = fmaf(wbuf[t * G + h], v, st.a[h][k]);
+    for (int k = 0; k < CPL; ++k) st.a[h][k] *= alpha[h];
+  }
+  // PV: lane holds channels CPL*lane .. CPL*lane + CPL-1
+#pragma unroll 4
+  for (int tok = 0; tok < nv; ++tok) {
+    float v[CPL];
+    if constexpr (CPL == 2) {
+      const uint32_t x = *reinterpret_cast<const uint32_t*>(vt + tok * D + 2 * lane);
+      v[0] = bf16_to_f32(x & 0xffffu);
+      v[1] = bf16_to_f32(x >> 16);
+    } else {
+      v[0] = bf16_to_f32(vt[tok * D + lane]);
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float pr = w[tok * G + h];
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) st.a[h][k] = fmaf(pr, v[k], st.a[h][k]);
     }
   }
   __builtin_amdgcn_wave_barrier();
@@ -174,15 +276,15 @@ __device__ __forceinline__ void bf16_tile(WaveAcc<D, G>& st, const float* qu, fl
 
 // Wave state -> this wave's slot of the block merge area [G][D+2] = (m, l, acc).
 template <int D, int G>
-__device__ __forceinline__ void store_wave_state(const WaveAcc<D, G>& st, float* mw, int lane) {
+__device__ __forceinline__ void store_wave_state(const WaveAcc<D, G>& st, float* mw, int lane, bool poison) {
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     if (lane == 0) {
       mw[h * (D + 2)] = st.m[h];
-      mw[h * (D + 2) + 1] = st.l[h];
+      mw[h * (D + 2) + 1] = poison ? NAN : st.l[h];
     }
 #pragma unroll
-    for (int k = 0; k < D / kWave; ++k) mw[h * (D + 2) + 2 + lane + kWave * k] = st.a[h][k];
+    for (int k = 0; k < D / kWave; ++k) mw[h * (D + 2) + 2 + (D / kWave) * lane + k] = st.a[h][k];
   }
 }
 
@@ -208,15 +310,6 @@ __device__ __forceinline__ void combine_block(const float* mrg, int slot, const 
 // ---------------------------------------------------------------------------
 // INT2 history on the matrix cores
 // ---------------------------------------------------------------------------
-// Lane roles (lane = 16*grp + n):
-//  * QK:  D[(head, digit)][token] = sum_ch Qdigit[(head,digit)][ch] * code'[ch][token].
-//         A (q digits) comes from the workspace; B lane (n, grp) holds, for token
-//         block tb, token 4n+tb and the 16 channels of one code word of K plane grp.
-//         The result lane holds the 4 digit sums of head (4nb+grp) for token 4n+tb.
-//  * PV:  D[(head, digit)][channel] = sum_t Wdigit[(head,digit)][t] * code'[t][channel].
-//         A (weight digits) is read back from LDS planes; B lane (n, grp) holds
-//         tokens 16grp..16grp+15 of one channel of V byte column D/64*n + bs.
-//         The result lane holds the 4 digit sums of head (4nb+grp), channel D/16*n + u.
 // ---- asynchronous page staging: global -> LDS copies (no VGPRs), one ring of
 // stages per wave.  The copies are issued from inline assembly so that their
 // completion is awaited explicitly (s_waitcnt vmcnt(n) before a stage is read)
@@ -250,9 +343,13 @@ __device__ __forceinline__ void wait_vmem(int n) {
   }
 }
 
-// Stage layout (one page of one KV head): K codes (16*D bytes, the pool's
-// plane layout), V codes (16*D bytes, byte-column-major), K (scale, zero)
-// [64] u32, V (scale, zero) [64] u32.
+// Stage layout (one page of one KV head): K codes (16*D bytes), V codes
+// (16*D bytes), K (scale, zero) [64] u32, V (scale, zero) [64] u32.  Each copy
+// instruction moves 1 KB, lane l's 16 bytes landing at 16*l; every lane fetches
+// exactly the 16 bytes that the same lane reads back as an MFMA operand, so the
+// reads (16*l + 1024*c) are free of LDS bank conflicts:
+//   K copy c, lane (q = l/16, n = l%16): plane q, tokens 4n..4n+3, bytes 16c..16c+15
+//   V copy c, lane (q, n): byte column (D/64)*n + c, tokens 16q..16q+15
 template <int D>
 struct Stage {
   static constexpr int kK = 0, kV = 16 * D, kKsz = 32 * D, kVsz = 32 * D + 256, kBytes = 32 * D + 512;
@@ -262,24 +359,34 @@ struct Stage {
 template <int D>
 __device__ __forceinline__ void stage_page(const DecodeDev& p, size_t blk, uint32_t stage_lds, int lane) {
   using S = Stage<D>;
-  const uint8_t* kblk = p.k_codes + blk * (16 * D);
-  const uint8_t* vblk = p.v_codes + blk * (16 * D);
+  constexpr int NCH = D / 64, PLANE = D / 16;
+  const int q = lane >> 4, n = lane & 15;
+  const uint8_t* kblk = p.k_codes + blk * (16 * D) + q * kPage * PLANE + 4 * n * PLANE;
+  const uint8_t* vblk = p.v_codes + blk * (16 * D) + NCH * n * kPage + 16 * q;
 #pragma unroll
-  for (int c = 0; c < D / 64; ++c) copy16_to_lds(kblk + 1024 * c + 16 * lane, stage_lds + S::kK + 1024 * c);
+  for (int c = 0; c < NCH; ++c) copy16_to_lds(kblk + 16 * c, stage_lds + S::kK + 1024 * c);
 #pragma unroll
-  for (int c = 0; c < D / 64; ++c) copy16_to_lds(vblk + 1024 * c + 16 * lane, stage_lds + S::kV + 1024 * c);
+  for (int c = 0; c < NCH; ++c) copy16_to_lds(vblk + kPage * c, stage_lds + S::kV + 1024 * c);
   copy4_to_lds(p.k_sz + blk * kPage + lane, stage_lds + S::kKsz);
   copy4_to_lds(p.v_sz + blk * kPage + lane, stage_lds + S::kVsz);
 }
 
-// Ring stages per wave and where the weight-digit planes live, chosen so two
-// blocks of 4 waves fit a CU's 160 KB of LDS.
+// Per-wave LDS: a ring of page stages, the weight-digit planes (unless they
+// reuse the consumed K codes) and the fp32 PV accumulators, which are only
+// touched when the softmax reference is raised.  Sized so two blocks of 4
+// waves fit a CU's 160 KB of LDS.
 template <int D, int NB>
 struct Ring {
   static constexpr bool kPlanesInK = NB * 1024 <= 16 * D;   // planes reuse the consumed K codes
-  static constexpr int kStages = (D == 128 && NB > 2) ? 3 : 4;
+#ifdef OSCAR_SCAN_STAGES
+  static constexpr int kStages = OSCAR_SCAN_STAGES;
+#else
+  static constexpr int kStages = D == 128 ? 3 : 4;
+#endif
   static constexpr int kPlaneBytes = kPlanesInK ? 0 : NB * 1024;
-  static constexpr int kWaveBytes = kStages * Stage<D>::kBytes + kPlaneBytes;
+  static constexpr int kFaccOff = kStages * Stage<D>::kBytes + kPlaneBytes;
+  static constexpr int kFaccBytes = NB * 4 * (D / 64) * kWave * 4;   // [nb][u][lane] fp32
+  static constexpr int kWaveBytes = kFaccOff + kFaccBytes;
 };
 
 // Lane roles (lane = 16*grp + n):
@@ -291,18 +398,22 @@ struct Ring {
 //         A (weight digits) is read back from LDS planes; B lane (n, grp) holds
 //         tokens 16grp..16grp+15 of one channel of V byte column D/64*n + bs.
 //         The result lane holds the 4 digit sums of head (4nb+grp), channel D/16*n + u.
-template <int D, int NB>
+template <int D, int G>
 __device__ __forceinline__ void hist_wave(const DecodeDev& p, int b, int g, int pg_begin, int pg_end, int hl,
                                           uint8_t* ring, float* mw, bool& poison, int lane) {
+  constexpr int NB = (G + 3) / 4;
   constexpr int NCH = D / 64;   // code words per token per K plane; V byte columns per lane
   constexpr int NU = 4 * NCH;   // PV result column blocks per head block
-  constexpr int PLANE = D / 16; // bytes per token in one K plane
   using S = Stage<D>;
   using RG = Ring<D, NB>;
   constexpr int NS = RG::kStages;
   const int n = lane & 15, grp = lane >> 4;
-  const int G = p.G;
   const int h_base = b * p.Hq + g * G;
+  const int count = pg_end - pg_begin;   // wave-uniform, at most kWave pages
+
+  // the wave's page ids, one per lane, read once: a vector load inside the
+  // page loop would have to wait for every page copy in flight
+  const int pid_lane = lane < count ? p.block_table[(size_t)b * p.max_pages + pg_begin + lane] : -1;
 
   v4i qa[NB][NCH];
   float ca[NB], cb[NB];
@@ -319,61 +430,71 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int b, int g, int 
       qa[nb][c] = row_ok ? *src : v4i{0, 0, 0, 0};
     }
   }
-  wait_vmem(0);   // operands loaded before the page copies start counting
+  wait_vmem(0);   // operands and page ids loaded before the page copies start counting
+  const uint64_t page_ok = __ballot(pid_lane >= 0 && (int64_t)pid_lane < p.n_pages);
 
   v4i pv[NB][NU];
-  float facc[NB][NU], mref[NB], lsum[NB], zsum[NB];
+  // mref: reference maximum (log2 units) of each head block; logits are kept
+  // relative to it.  thr: rescale when a relative logit exceeds it (-inf until
+  // the first page has set the references).
+  float mref[NB], lsum[NB], zsum[NB];
+  float* facc = reinterpret_cast<float*>(ring + RG::kFaccOff) + lane;   // [nb][u], stride kWave
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    mref[nb] = -INFINITY;
+    mref[nb] = 0.0f;
     lsum[nb] = 0.0f;
     zsum[nb] = 0.0f;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       pv[nb][u] = v4i{0, 0, 0, 0};
-      facc[nb][u] = 0.0f;
+      facc[(nb * NU + u) * kWave] = 0.0f;
     }
   }
-  float smax = 0.0f, kw = 0.0f;
+  float thr = -INFINITY, smax = 0.0f, sthr = 0.0f, kw = 0.0f, kw_inv = 0.0f;
 
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_offset(ring));
   uint8_t* planes = RG::kPlanesInK ? nullptr : ring + NS * S::kBytes;
-  const int count = pg_end - pg_begin;
-  // page ids (validated; an invalid page is staged from page 0 and skipped)
-  auto page_blk = [&](int pg) -> size_t {
-    const int pid = p.block_table[(size_t)b * p.max_pages + pg];
-    return (pid >= 0 && (int64_t)pid < p.n_pages) ? (size_t)pid * p.n_kv + g : (size_t)g;
-  };
-  auto page_ok = [&](int pg) -> bool {
-    const int pid = p.block_table[(size_t)b * p.max_pages + pg];
-    return pid >= 0 && (int64_t)pid < p.n_pages;
+  // (page, head) block of page i of the range; an invalid page id is staged
+  // from page 0 and skipped
+  auto page_blk = [&](int i) -> size_t {
+    const int pid = __builtin_amdgcn_readlane(pid_lane, i);
+    return ((page_ok >> i) & 1) ? (size_t)pid * p.n_kv + g : (size_t)g;
   };
   const int pre = count < NS - 1 ? count : NS - 1;
-  for (int i = 0; i < pre; ++i) stage_page<D>(p, page_blk(pg_begin + i), ring_lds + i * S::kBytes, lane);
+  for (int i = 0; i < pre; ++i) stage_page<D>(p, page_blk(i), ring_lds + i * S::kBytes, lane);
 
   for (int i = 0; i < count; ++i) {
     const int pg = pg_begin + i;
-    if (i + NS - 1 < count)
-      stage_page<D>(p, page_blk(pg + NS - 1), ring_lds + ((i + NS - 1) % NS) * S::kBytes, lane);
+    if (i + NS - 1 < count) stage_page<D>(p, page_blk(i + NS - 1), ring_lds + ((i + NS - 1) % NS) * S::kBytes, lane);
     const int ahead = min(NS - 1, count - 1 - i);
     wait_vmem(ahead * S::kCopies);
-    if (!page_ok(pg)) {
+    if (!((page_ok >> i) & 1)) {
       poison = true;
       continue;
     }
-    const uint8_t* st = ring + (i % NS) * S::kBytes;
+    uint8_t* st = ring + (i % NS) * S::kBytes;
     const int nv = min(kPage, hl - pg * kPage);
+    if (nv < kPage) {
+      // slots past the history end hold undefined bytes: give them zero
+      // scales and zeros, so only the logit mask below has to exclude them
+      if (lane >= nv) {
+        reinterpret_cast<uint32_t*>(st + S::kKsz)[lane] = 0u;
+        reinterpret_cast<uint32_t*>(st + S::kVsz)[lane] = 0u;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
 
     uint32_t kword[4 * NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const uint4 k4 = *reinterpret_cast<const uint4*>(st + S::kK + grp * kPage * PLANE + 4 * n * PLANE + 16 * c);
+      const uint4 k4 = *reinterpret_cast<const uint4*>(st + S::kK + 1024 * c + 16 * lane);
       kword[4 * c] = k4.x; kword[4 * c + 1] = k4.y; kword[4 * c + 2] = k4.z; kword[4 * c + 3] = k4.w;
     }
     const uint4 ksz = *reinterpret_cast<const uint4*>(st + S::kKsz + 16 * n);
     const uint4 vsz = *reinterpret_cast<const uint4*>(st + S::kVsz + 16 * n);
     const uint32_t kw4[4] = {ksz.x, ksz.y, ksz.z, ksz.w};
     const uint32_t vw4[4] = {vsz.x, vsz.y, vsz.z, vsz.w};
+    // token 4n+tb
     float sk[4], zk[4], sv[4], zv[4];
     bool tv[4];
 #pragma unroll
@@ -381,12 +502,13 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int b, int g, int 
       tv[tb] = 4 * n + tb < nv;
       sk[tb] = f16_to_f32(kw4[tb] & 0xffffu);
       zk[tb] = f16_to_f32(kw4[tb] >> 16);
-      sv[tb] = tv[tb] ? f16_to_f32(vw4[tb] & 0xffffu) : 0.0f;
-      zv[tb] = tv[tb] ? f16_to_f32(vw4[tb] >> 16) : 0.0f;
+      sv[tb] = f16_to_f32(vw4[tb] & 0xffffu);
+      zv[tb] = f16_to_f32(vw4[tb] >> 16);
     }
 
-    // ---- QK, one head block at a time: token block tb holds token 4n+tb
-    float lg[NB][4];
+    // ---- QK, one head block at a time: token block tb holds token 4n+tb.
+    // Relative logit (log2 units): scale*ca*dot + (zero*cb - mref).
+    float lg[NB][4], lmax[NB];
     bool need = false;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -403,73 +525,96 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int b, int g, int 
         // digits: d0 + 2^8 d1 and d2 + 2^8 d3 are exact in int32
         const int lo = dq.x + dq.y * 256, hi = dq.z + dq.w * 256;
         const float dot = fmaf((float)hi, 65536.0f, (float)lo);
-        lg[nb][tb] = (tv[tb] && hok) ? fmaf(sk[tb] * ca[nb], dot, zk[tb] * cb[nb]) : -INFINITY;
-        need |= lg[nb][tb] > mref[nb] + kLazyThr;
+        // an invalid token or head gets fma(0, dot, -inf) = -inf (dot is finite)
+        const float off = (tv[tb] & hok) ? fmaf(zk[tb], cb[nb], -mref[nb]) : -INFINITY;
+        lg[nb][tb] = fmaf(sk[tb] * ca[nb], dot, off);
       }
+      lmax[nb] = fmaxf(fmaxf(lg[nb][0], lg[nb][1]), fmaxf(lg[nb][2], lg[nb][3]));
+      need |= lmax[nb] > thr;
+      __builtin_amdgcn_sched_barrier(0);   // bounds the live MFMA operands (register pressure)
     }
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) need |= sv[tb] > kScaleSlack * smax;
+    need |= fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])) > sthr;
 
+    __builtin_amdgcn_sched_barrier(0);
     if (__any(need)) {
-      // raise the reference maxima and the V-scale bound; fold the integer
+      // raise the references and the V-scale bound; fold the integer
       // accumulators into fp32 under the old ones first
+      const bool first = !(kw_inv > 0.0f);   // nothing accumulated yet
       float s_new = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
       s_new = fmaxf(smax, group16_max(s_new));
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const float t = fmaxf(fmaxf(lg[nb][0], lg[nb][1]), fmaxf(lg[nb][2], lg[nb][3]));
-        const float nm = fmaxf(mref[nb], group16_max(t));
-        const float alpha = exp2_or_zero(mref[nb], nm);
-        if (kw > 0.0f) {
+        const float t = group16_max(lmax[nb]);
+        // raise of the reference; the first page sets it (all -inf: head has no rows)
+        const float delta = first ? (t == -INFINITY ? 0.0f : t) : fmaxf(t, 0.0f);
+        if (!first) {
+          const float alpha = exp2f(-delta);
 #pragma unroll
           for (int u = 0; u < NU; ++u) {
-            facc[nb][u] = (facc[nb][u] + digits_to_f32(pv[nb][u]) * (code_scale_inv(u & 3) / kw)) * alpha;
-            pv[nb][u] = v4i{0, 0, 0, 0};
+            float& f = facc[(nb * NU + u) * kWave];
+            f = (f + digits_to_f32(pv[nb][u]) * (code_scale_inv(u & 3) * kw_inv)) * alpha;
+            clear_in_place(pv[nb][u]);
           }
+          lsum[nb] *= alpha;
+          zsum[nb] *= alpha;
         }
-        lsum[nb] *= alpha;
-        zsum[nb] *= alpha;
-        mref[nb] = nm;
+        mref[nb] += delta;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) lg[nb][tb] -= delta;
       }
+      thr = kLazyThr;
       smax = s_new;
-      kw = smax > 0.0f ? kFix / (exp2f(kLazyThr) * smax) : kFix / exp2f(kLazyThr);
+      sthr = kScaleSlack * smax;
+      // weights p*scale_V*kw stay below 2^30 * kScaleSlack < 2^31
+      const float denom = exp2f(kLazyThr) * (smax > 0.0f ? smax : 1.0f);
+      kw = kFix / denom;
+      kw_inv = denom / kFix;
     }
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- weights p*scale_V as 30-bit fixed point, balanced digits,
-    // transposed into LDS planes [nb][head][digit][64 tokens]
-    uint8_t* pl = RG::kPlanesInK ? const_cast<uint8_t*>(st) + S::kK : planes;
+    // transposed into the LDS digit planes of the PV A operands
+    uint8_t* pl = RG::kPlanesInK ? st + S::kK : planes;
+    float svk[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) svk[tb] = sv[tb] * kw;
     __builtin_amdgcn_wave_barrier();   // every lane has read its K words
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       uint32_t dg[4];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        const float pr = __builtin_amdgcn_exp2f(lg[nb][tb] - mref[nb]);   // exp2(-inf) = 0
+        const float pr = __builtin_amdgcn_exp2f(lg[nb][tb]);   // exp2(-inf) = 0
         lsum[nb] += pr;
         zsum[nb] = fmaf(pr, zv[tb], zsum[nb]);
-        dg[tb] = balanced_digits((uint32_t)fmaf(pr * sv[tb], kw, 0.5f));
+        dg[tb] = balanced_digits((uint32_t)fmaf(pr, svk[tb], 0.5f));
       }
       // 4x4 byte transpose: t_j byte tb = digit j of token 4n+tb
       const uint32_t x01l = __builtin_amdgcn_perm(dg[1], dg[0], 0x05010400u);
       const uint32_t x01h = __builtin_amdgcn_perm(dg[1], dg[0], 0x07030602u);
       const uint32_t x23l = __builtin_amdgcn_perm(dg[3], dg[2], 0x05010400u);
       const uint32_t x23h = __builtin_amdgcn_perm(dg[3], dg[2], 0x07030602u);
-      uint8_t* plane = pl + ((nb * 4 + grp) * 4) * kPage + 4 * n;
-      *reinterpret_cast<uint32_t*>(plane) = __builtin_amdgcn_perm(x23l, x01l, 0x05040100u);
-      *reinterpret_cast<uint32_t*>(plane + kPage) = __builtin_amdgcn_perm(x23l, x01l, 0x07060302u);
-      *reinterpret_cast<uint32_t*>(plane + 2 * kPage) = __builtin_amdgcn_perm(x23h, x01h, 0x05040100u);
-      *reinterpret_cast<uint32_t*>(plane + 3 * kPage) = __builtin_amdgcn_perm(x23h, x01h, 0x07060302u);
+      // word j is row (head 4nb+grp, digit j), tokens 4n..4n+3: it goes to the
+      // chunk the PV reader lane (4grp+j, n/4) loads (see plane_chunk)
+      uint8_t* plane = pl + nb * 1024 + 256 * (n >> 2) + 4 * (n & 3);
+      const int sw = 4 * (n >> 2);
+      *reinterpret_cast<uint32_t*>(plane + 16 * ((4 * grp + 0) ^ sw)) = __builtin_amdgcn_perm(x23l, x01l, 0x05040100u);
+      *reinterpret_cast<uint32_t*>(plane + 16 * ((4 * grp + 1) ^ sw)) = __builtin_amdgcn_perm(x23l, x01l, 0x07060302u);
+      *reinterpret_cast<uint32_t*>(plane + 16 * ((4 * grp + 2) ^ sw)) = __builtin_amdgcn_perm(x23h, x01h, 0x05040100u);
+      *reinterpret_cast<uint32_t*>(plane + 16 * ((4 * grp + 3) ^ sw)) = __builtin_amdgcn_perm(x23h, x01h, 0x07060302u);
     }
     __builtin_amdgcn_wave_barrier();
 
     // ---- PV
 #pragma unroll
     for (int bs = 0; bs < NCH; ++bs) {
-      const uint4 v4 = *reinterpret_cast<const uint4*>(st + S::kV + (NCH * n + bs) * kPage + 16 * grp);
+      const uint4 v4 = *reinterpret_cast<const uint4*>(st + S::kV + 1024 * bs + 16 * lane);
       const uint32_t r[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const v4i wa = *reinterpret_cast<const v4i*>(pl + ((nb * 4 + (n >> 2)) * 4 + (n & 3)) * kPage + 16 * grp);
+        // A lane (n, grp): row (head 4nb + n/4, digit n%4), tokens 16grp..16grp+15;
+        // plane nb holds 4 token blocks of 256 bytes, chunk n ^ 4grp of block grp
+        const v4i wa = *reinterpret_cast<const v4i*>(pl + nb * 1024 + 256 * grp + 16 * (n ^ (4 * grp)));
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) {
           const v4i bop = v4i{code_mask(r[0], pp), code_mask(r[1], pp), code_mask(r[2], pp), code_mask(r[3], pp)};
@@ -481,23 +626,28 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int b, int g, int 
   }
   wait_vmem(0);
 
-  // ---- fold, reduce over the 16 lanes of each head, store (m, l, acc) per head
+  // ---- fold, reduce over the 16 lanes of each head; each head's (m, l, acc)
+  // slot overlays the start of the ring, below the fp32 accumulators
+  float acc[NB][NU], lz[NB][2];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const float l = group16_sum(lsum[nb]);
-    const float z = group16_sum(zsum[nb]);
+    lz[nb][0] = group16_sum(lsum[nb]);
+    lz[nb][1] = group16_sum(zsum[nb]);
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+      acc[nb][u] = facc[(nb * NU + u) * kWave] + digits_to_f32(pv[nb][u]) * (code_scale_inv(u & 3) * kw_inv);
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
     const int h = 4 * nb + grp;
     if (h < G) {
       float* mh = mw + h * (D + 2);
       if (n == 0) {
-        mh[0] = mref[nb];
-        mh[1] = l;
+        mh[0] = kw_inv > 0.0f ? mref[nb] : -INFINITY;   // no page processed: empty partial
+        mh[1] = lz[nb][0];
       }
 #pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        const float part = kw > 0.0f ? digits_to_f32(pv[nb][u]) * (code_scale_inv(u & 3) / kw) : 0.0f;
-        mh[2 + NU * n + u] = facc[nb][u] + part + z;
-      }
+      for (int u = 0; u < NU; ++u) mh[2 + NU * n + u] = acc[nb][u] + lz[nb][1];
     }
   }
 }
@@ -566,24 +716,20 @@ __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) vo
   constexpr int NB = (G + 3) / 4;
   using RG = Ring<D, NB>;
   constexpr int kHistBytes = 4 * RG::kWaveBytes;
-  constexpr int kBf16Bytes = (G * D + 4 * kWave * G) * 4;
+  constexpr int kBf16Bytes = 4 * bf16_lds_bytes<D, G>();
   constexpr int kSmem = kHistBytes > kBf16Bytes ? kHistBytes : kBf16Bytes;
-  static_assert(G * (D + 2) * 4 <= RG::kWaveBytes, "merge slot must fit the wave's ring");
+  static_assert(G * (D + 2) * 4 <= RG::kFaccOff, "merge slot must fit below the wave's accumulators");
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
   __shared__ int flags[4];
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int units = p.B * p.n_kv;
   const int id = blockIdx.x;
   bool poison = false;
 
-  if (id < units * p.bf_blocks) {  // ---- BF16 sink / recent chunks (block-uniform)
-    float* q_s = reinterpret_cast<float*>(smem);
-    float* wbuf = q_s + G * D;
+  if (id < units * p.bf_blocks) {  // ---- BF16 sink / recent chunks (block-uniform): one chunk per wave
     const int unit = id % units, cb = id / units;
     const int b = unit / p.n_kv, g = unit % p.n_kv;
-    const size_t part = (size_t)G * (D + 2);
-    for (int e = tid; e < G * D; e += kBlock) q_s[e] = bf16_to_f32(p.q[((size_t)b * p.Hq + g * G) * D + e]);
-    __syncthreads();
     const int c = cb * (kBlock / kWave) + wave;
     if (c < p.chunks) {
       WaveAcc<D, G> st;
@@ -613,17 +759,15 @@ __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) vo
         kb = p.recent_k + off;
         vb = p.recent_v + off;
       }
-      if (nv > 0) bf16_tile<D, G>(st, q_s, p.sm_log2, kb, vb, nv, wbuf + wave * kWave * G, lane);
-      float* dst = p.bpart + (((size_t)b * p.n_kv + g) * p.chunks + c) * part;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        if (lane == 0) {
-          dst[h * (D + 2)] = st.m[h];
-          dst[h * (D + 2) + 1] = poison ? NAN : st.l[h];
-        }
-#pragma unroll
-        for (int k = 0; k < D / kWave; ++k) dst[h * (D + 2) + 2 + lane + kWave * k] = st.a[h][k];
+      if (nv > 0) {
+        bf16x8 qa[D / 32];
+        bf16_q_operands<D, G>(qa, p.q + ((size_t)b * p.Hq + g * G) * D, lane);
+        Bf16Tile<D> tile;
+        bf16_load<D>(tile, kb, vb, nv, lane);
+        bf16_compute<D, G>(st, tile, qa, p.sm_log2, nv, smem + wave * bf16_lds_bytes<D, G>(), lane);
       }
+      store_wave_state<D, G>(st, p.bpart + (((size_t)b * p.n_kv + g) * p.chunks + c) * (size_t)G * (D + 2), lane,
+                             poison);
     }
     return;
   }
@@ -645,7 +789,7 @@ __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) vo
   const int we = min(wb + per_wave, pe);
   uint8_t* ring = smem + wave * RG::kWaveBytes;
   // the wave's merge slot [G][D+2] = (m, l, acc) overlays its own ring once the scan is done
-  hist_wave<D, NB>(p, b, g, wb, we, hl, ring, reinterpret_cast<float*>(ring), poison, lane);
+  hist_wave<D, G>(p, b, g, wb, we, hl, ring, reinterpret_cast<float*>(ring), poison, lane);
   if (lane == 0) flags[wave] = poison ? 1 : 0;
   __syncthreads();
   combine_block(reinterpret_cast<const float*>(smem), RG::kWaveBytes / 4, flags,
@@ -742,20 +886,19 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(DecodeDev p, int max_part
 
 // ---- BF16 paged comparator ---------------------------------------------
 template <int D, int G>
-__global__ __launch_bounds__(kBlock) void bf16_paged_kernel(Bf16Dev p) {
-  constexpr int kWbuf = 4 * kWave * G;
-  __shared__ float q_s[G * D];
-  __shared__ float mrg[4 * G * (D + 2)];
-  __shared__ float wbuf[kWbuf];
+__global__ __launch_bounds__(kBlock, (G > 8 ? 1 : 2)) void bf16_paged_kernel(Bf16Dev p) {
+  constexpr int kWaveLds = bf16_lds_bytes<D, G>();
+  constexpr int kMrg = 4 * G * (D + 2) * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kWaveLds > kMrg ? 4 * kWaveLds : kMrg];
   __shared__ int flags[4];
   const int b = blockIdx.z, g = blockIdx.y, x = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int h0 = g * G;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   WaveAcc<D, G> st;
   acc_init(st);
   bool poison = false;
-  for (int e = tid; e < G * D; e += kBlock) q_s[e] = bf16_to_f32(p.q[((size_t)b * p.Hq + h0) * D + e]);
-  __syncthreads();
+  bf16x8 qa[D / 32];
+  bf16_q_operands<D, G>(qa, p.q + ((size_t)b * p.Hq + g * G) * D, lane);
   int cl = p.ctx_len[b];
   if (cl < 0 || cl > p.max_ctx_len) {
     poison = true;
@@ -770,10 +913,14 @@ __global__ __launch_bounds__(kBlock) void bf16_paged_kernel(Bf16Dev p) {
       continue;
     }
     const size_t off = ((size_t)pid * p.n_kv + g) * kPage * D;
-    bf16_tile<D, G>(st, q_s, p.sm_log2, p.k_pages + off, p.v_pages + off, min(kPage, cl - pg * kPage),
-                    wbuf + wave * kWave * G, lane);
+    const int nv = min(kPage, cl - pg * kPage);
+    Bf16Tile<D> tile;
+    bf16_load<D>(tile, p.k_pages + off, p.v_pages + off, nv, lane);
+    bf16_compute<D, G>(st, tile, qa, p.sm_log2, nv, smem + wave * kWaveLds, lane);
   }
-  store_wave_state<D, G>(st, mrg + wave * G * (D + 2), lane);
+  __syncthreads();   // the merge area overlays the tiles' LDS
+  float* mrg = reinterpret_cast<float*>(smem);
+  store_wave_state<D, G>(st, mrg + wave * G * (D + 2), lane, false);
   if (lane == 0) flags[wave] = poison ? 1 : 0;
   __syncthreads();
   combine_block(mrg, G * (D + 2), flags, p.part + (((size_t)b * p.n_kv + g) * p.splits + x) * (size_t)G * (D + 2),
