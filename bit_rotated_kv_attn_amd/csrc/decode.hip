@@ -656,40 +656,55 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int b, int g, int 
 // 1. rotate the query: q_rot = q R_K[g]; MFMA digit operands and constants
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(128) void rotate_query_kernel(DecodeDev p) {
+__global__ __launch_bounds__(kBlock) void rotate_query_kernel(DecodeDev p) {
   constexpr int NCH = D / 64, PLANE = D / 16;
+  constexpr int P = kBlock / D, IP = D / P;   // row parts of each dot product; every load in flight at once
   __shared__ float qs[D];
-  __shared__ float red[2][2];
+  __shared__ float part_s[P][D];
+  __shared__ float red[2][kBlock / kWave];
   const int bh = blockIdx.x;
   const int b = bh / p.Hq, h = bh % p.Hq, g = h / p.G, hl = h % p.G;
-  const int j = threadIdx.x;
-  if (j < D) qs[j] = bf16_to_f32(p.q[(size_t)bh * D + j]);
+  const int tid = threadIdx.x, j = tid % D, part = tid / D;
+  const float* R = p.r_k + (size_t)g * D * D + (size_t)part * IP * D + j;
+  float r[IP];
+#pragma unroll
+  for (int k = 0; k < IP; ++k) r[k] = R[(size_t)k * D];
+  if (tid < D) qs[tid] = bf16_to_f32(p.q[(size_t)bh * D + tid]);
   __syncthreads();
   float acc = 0.0f;
-  if (j < D) {
-    const float* R = p.r_k + (size_t)g * D * D;
-    for (int i = 0; i < D; ++i) acc = fmaf(qs[i], R[i * D + j], acc);
+#pragma unroll
+  for (int k = 0; k < IP; ++k) acc = fmaf(qs[part * IP + k], r[k], acc);
+  part_s[part][j] = acc;
+  __syncthreads();
+  acc = 0.0f;
+  if (tid < D) {
+#pragma unroll
+    for (int q = 0; q < P; ++q) acc += part_s[q][tid];
   }
-  const float amax = wave_max(j < D ? fabsf(acc) : 0.0f);
-  const float asum = wave_sum(j < D ? acc : 0.0f);
-  if ((j & (kWave - 1)) == 0) {
-    red[0][j / kWave] = amax;
-    red[1][j / kWave] = asum;
+  const float amax = wave_max(tid < D ? fabsf(acc) : 0.0f);
+  const float asum = wave_sum(tid < D ? acc : 0.0f);
+  if ((tid & (kWave - 1)) == 0) {
+    red[0][tid / kWave] = amax;
+    red[1][tid / kWave] = asum;
   }
   __syncthreads();
-  const float maxabs = fmaxf(red[0][0], red[0][1]);
-  const float qsum = red[1][0] + red[1][1];
+  float maxabs = 0.0f, qsum = 0.0f;
+#pragma unroll
+  for (int w = 0; w < D / kWave; ++w) {
+    maxabs = fmaxf(maxabs, red[0][w]);
+    qsum += red[1][w];
+  }
   // kq: power of two with 16 * maxabs * kq <= 2^30
   float kq = 1.0f;
   if (maxabs > 0.0f) {
     kq = exp2f(floorf(log2f(kFix / (16.0f * maxabs))));
     if (16.0f * maxabs * kq > kFix) kq *= 0.5f;
   }
-  if (j < D) {
-    const int pp = j & 3;                       // mask index of channel j
+  if (tid < D) {
+    const int pp = tid & 3;                     // mask index of channel tid
     const float scale = kq * (pp == 0 ? 16.0f : pp == 1 ? 4.0f : 1.0f);
     const uint32_t U = balanced_digits((uint32_t)(int)rintf(acc * scale));
-    const int ib = j >> 2;                      // code-row byte of channel j
+    const int ib = tid >> 2;                    // code-row byte of channel tid
     const int kb = ib / PLANE, rem = ib % PLANE, c = rem >> 2, bb = rem & 3;
     const int nb = hl >> 2, hr = hl & 3;
     uint8_t* base = p.qdig + ((((size_t)b * p.n_kv + g) * p.NB + nb) * NCH + c) * kWave * 16;
@@ -699,7 +714,7 @@ __global__ __launch_bounds__(128) void rotate_query_kernel(DecodeDev p) {
       base[lane * 16 + 4 * pp + bb] = (uint8_t)(U >> (8 * dj));
     }
   }
-  if (j == 0) {
+  if (tid == 0) {
     p.qa[bh] = p.sm_log2 / (16.0f * kq);
     p.qb[bh] = p.sm_log2 * qsum;
   }
@@ -799,88 +814,96 @@ __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) vo
 // ---------------------------------------------------------------------------
 // 3. merge: LSE over history splits, * R_V^T, LSE with BF16 chunks, normalise
 // ---------------------------------------------------------------------------
-// Block-wide LSE merge of n partials (stride floats apart) into acc[D] (LDS);
-// returns (M, L) with L = sum exp2(m_i - M) l_i.
-template <int D>
-__device__ __forceinline__ float2 lse_merge(const float* __restrict__ parts, int n, size_t stride, float* w_s,
-                                            float* acc_s, float* red, int tid) {
-  constexpr int TPC = kBlock / D;   // threads per channel
-  float m = -INFINITY;
-  for (int s = tid; s < n; s += kBlock) m = fmaxf(m, parts[s * stride]);
-  m = wave_max(m);
-  if ((tid & (kWave - 1)) == 0) red[tid / kWave] = m;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  float l = 0.0f;
-  for (int s = tid; s < n; s += kBlock) {
-    const float f = exp2_or_zero(parts[s * stride], M);
-    w_s[s] = f;
-    l += f * parts[s * stride + 1];
-  }
-  l = wave_sum(l);
-  if ((tid & (kWave - 1)) == 0) red[tid / kWave] = l;
-  __syncthreads();
-  const float L = red[0] + red[1] + red[2] + red[3];
-  const int c = tid % D, part = tid / D;
-  float a = 0.0f;
-  for (int s = part; s < n; s += TPC) a = fmaf(w_s[s], parts[s * stride + 2 + c], a);
-  acc_s[part * D + c] = a;
-  __syncthreads();
-  if (part == 0) {
-#pragma unroll
-    for (int k = 1; k < TPC; ++k) a += acc_s[k * D + c];
-    acc_s[c] = a;
-  }
-  __syncthreads();
-  return make_float2(M, L);
-}
+// One query head per block.  All partials (history splits and BF16 chunks)
+// share one reference maximum M:
+//   out = (sum_hist f_s acc_s R_V^T + sum_bf16 f_s acc_s) / sum_all f_s l_s,
+//   f_s = exp2(m_s - M).
+// Thread (c, part) owns channel c for the partials s = part (mod TPC); the
+// loads of a round of up to kMergeRound partials per thread, and of the
+// thread's slice of R_V, are all issued before any is used.
+constexpr int kMergeRound = 16;
 
 template <int D>
-__global__ __launch_bounds__(kBlock) void merge_kernel(DecodeDev p, int max_parts) {
-  constexpr int TPC = kBlock / D;
-  extern __shared__ float w_s[];   // max_parts weights
-  __shared__ float acc_s[kBlock];
-  __shared__ float arot[D];
-  __shared__ float red[4];
+__global__ __launch_bounds__(kBlock) void merge_kernel(DecodeDev p) {
+  constexpr int TPC = kBlock / D;   // threads per channel
+  constexpr int SEG = D / TPC;      // R_V row segment per thread
+  __shared__ float red[kBlock / kWave];
+  __shared__ float ah_s[TPC][D], ab_s[TPC][D];
+  __shared__ float l_s[TPC];
   const int bh = blockIdx.x;
   const int b = bh / p.Hq, h = bh % p.Hq, g = h / p.G, kh = h % p.G;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, c = tid % D, part = tid / D;
   const size_t stride = (size_t)p.G * (D + 2);
-  float2 mh = make_float2(-INFINITY, 0.0f);
-  float oh = 0.0f;
-  if (p.splits > 0) {
-    const float* hp = p.hpart + ((size_t)b * p.n_kv + g) * p.splits * stride + (size_t)kh * (D + 2);
-    mh = lse_merge<D>(hp, p.splits, stride, w_s, acc_s, red, tid);
-    if (tid < D) arot[tid] = acc_s[tid];
-    __syncthreads();
-    // out_hist[i] = sum_j arot[j] * R_V[g][i][j]: TPC threads per row, contiguous segments
-    const int i = tid / TPC, seg = tid % TPC;
-    const float* Rrow = p.r_v + ((size_t)g * D + i) * D + seg * (D / TPC);
-    float s = 0.0f;
-#pragma unroll 8
-    for (int k = 0; k < D / TPC; ++k) s = fmaf(arot[seg * (D / TPC) + k], Rrow[k], s);
+  const float* hp = p.hpart + ((size_t)b * p.n_kv + g) * p.splits * stride + (size_t)kh * (D + 2);
+  const float* bp = p.bpart + ((size_t)b * p.n_kv + g) * p.chunks * stride + (size_t)kh * (D + 2);
+  const int n = p.splits, nt = p.splits + p.chunks;
+  // output row i = tid / TPC, segment seg = tid % TPC of R_V[g][i][:]
+  const int i = tid / TPC, seg = tid % TPC;
+  float rv[SEG];
+  {
+    const float* Rrow = p.r_v + ((size_t)g * D + i) * D + seg * SEG;
 #pragma unroll
-    for (int o = 1; o < TPC; o <<= 1) s += __shfl_xor(s, o, kWave);
-    oh = s;
-    __syncthreads();
+    for (int k = 0; k < SEG; ++k) rv[k] = Rrow[k];
   }
-  float2 mb = make_float2(-INFINITY, 0.0f);
-  float ob = 0.0f;
-  if (p.chunks > 0) {
-    const float* bp = p.bpart + ((size_t)b * p.n_kv + g) * p.chunks * stride + (size_t)kh * (D + 2);
-    mb = lse_merge<D>(bp, p.chunks, stride, w_s, acc_s, red, tid);
+  auto part_ptr = [&](int s) { return s < n ? hp + (size_t)s * stride : bp + (size_t)(s - n) * stride; };
+
+  // reference maximum over every partial
+  float m_loc = -INFINITY;
+  for (int s = tid; s < nt; s += kBlock) m_loc = fmaxf(m_loc, part_ptr(s)[0]);
+  m_loc = wave_max(m_loc);
+  if ((tid & (kWave - 1)) == 0) red[tid / kWave] = m_loc;
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kBlock / kWave; ++w) M = fmaxf(M, red[w]);
+
+  float ah = 0.0f, ab = 0.0f, l = 0.0f;
+  for (int s0 = part; s0 < nt; s0 += TPC * kMergeRound) {
+    float mv[kMergeRound], lv[kMergeRound], av[kMergeRound];
+#pragma unroll
+    for (int k = 0; k < kMergeRound; ++k) {
+      const int s = s0 + TPC * k;
+      const float* pp = part_ptr(s < nt ? s : 0);
+      mv[k] = s < nt ? pp[0] : -INFINITY;
+      lv[k] = s < nt ? pp[1] : 0.0f;
+      av[k] = pp[2 + c];
+    }
+#pragma unroll
+    for (int k = 0; k < kMergeRound; ++k) {
+      const int s = s0 + TPC * k;
+      const float f = exp2_or_zero(mv[k], M);
+      l += f * lv[k];
+      if (s < n) ah = fmaf(f, av[k], ah);
+      else if (s < nt) ab = fmaf(f, av[k], ab);
+    }
   }
-  const int i = tid / TPC;
-  if (tid % TPC == 0) {
-    if (p.chunks > 0) ob = acc_s[i];
-    const float Mt = fmaxf(mh.x, mb.x);
-    const float fh = exp2_or_zero(mh.x, Mt), fb = exp2_or_zero(mb.x, Mt);
-    const float den = fh * mh.y + fb * mb.y;
-    float o;
-    if (isnan(den)) o = NAN;
-    else o = (den > 0.0f) ? (fh * oh + fb * ob) / den : 0.0f;
-    p.out[(size_t)bh * D + i] = o;
+  ah_s[part][c] = ah;
+  ab_s[part][c] = ab;
+  if (c == 0) l_s[part] = l;   // the same in every channel of a part
+  __syncthreads();
+  float L = 0.0f;
+#pragma unroll
+  for (int q = 0; q < TPC; ++q) L += l_s[q];
+  // out_hist[i] = sum_j A_hist[j] R_V[g][i][j]
+  float o = 0.0f;
+#pragma unroll
+  for (int k = 0; k < SEG; ++k) {
+    const int jj = seg * SEG + k;
+    float a = 0.0f;
+#pragma unroll
+    for (int q = 0; q < TPC; ++q) a += ah_s[q][jj];
+    o = fmaf(a, rv[k], o);
+  }
+#pragma unroll
+  for (int off = 1; off < TPC; off <<= 1) o += __shfl_xor(o, off, kWave);
+  if (seg == 0) {
+    float ob = 0.0f;
+#pragma unroll
+    for (int q = 0; q < TPC; ++q) ob += ab_s[q][i];
+    float out;
+    if (isnan(L)) out = NAN;
+    else out = (L > 0.0f) ? (o + ob) / L : 0.0f;
+    p.out[(size_t)bh * D + i] = out;
   }
 }
 
@@ -1019,17 +1042,15 @@ hipError_t launch_decode_phase(int phase, const oscar_decode_args& a, const Deco
   const bool d128 = a.head_dim == 128;
   if (phase == kPhaseRotate) {
     if (plan.splits > 0) {
-      if (d128) rotate_query_kernel<128><<<nbh, 128, 0, stream>>>(dv);
-      else rotate_query_kernel<64><<<nbh, 128, 0, stream>>>(dv);
+      if (d128) rotate_query_kernel<128><<<nbh, kBlock, 0, stream>>>(dv);
+      else rotate_query_kernel<64><<<nbh, kBlock, 0, stream>>>(dv);
     }
   } else if (phase == kPhaseScan) {
     if (d128) launch_main_g<128>(dv, stream);
     else launch_main_g<64>(dv, stream);
   } else {
-    const int maxp = plan.splits > plan.chunks ? plan.splits : plan.chunks;
-    const size_t lds = (size_t)(maxp > 0 ? maxp : 1) * sizeof(float);
-    if (d128) merge_kernel<128><<<nbh, kBlock, lds, stream>>>(dv, maxp);
-    else merge_kernel<64><<<nbh, kBlock, lds, stream>>>(dv, maxp);
+    if (d128) merge_kernel<128><<<nbh, kBlock, 0, stream>>>(dv);
+    else merge_kernel<64><<<nbh, kBlock, 0, stream>>>(dv);
   }
   return hipGetLastError();
 }

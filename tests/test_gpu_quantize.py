@@ -28,12 +28,13 @@ def _inputs(seed, n_tok, n_kv, d, n_pages):
     return rng, x, slots
 
 
+@pytest.mark.parametrize("n_tok", [7, 300])          # one block per token / 32-token tiles
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("kind", ["k", "v"])
-def test_signed_permutation_bit_exact(d, kind):
+def test_signed_permutation_bit_exact(d, kind, n_tok):
     """R a signed permutation: every rotated value is exact, so codes, scales
     and zeros must match the oracle bit for bit with no exception."""
-    rng, x, slots = _inputs(1, 300, 3, d, 6)
+    rng, x, slots = _inputs(1, n_tok, 3, d, 6)
     rot = np.stack([pins.signed_permutation(d, rng)[0] for _ in range(3)])
     ref = _oracle(kind, x, rot, 9.5, slots, 6)
     got = gpu_quantize(kind, x, rot, 9.5, slots, 6)
@@ -50,21 +51,22 @@ def test_tiny_config_history(kind):
     compare_quant(kind, got[0], got[1], ref[0], ref[1], ref[2], cfg["head_dim"])
 
 
+@pytest.mark.parametrize("n_tok", [41, 101])         # one block per token / 32-token tiles
 @pytest.mark.parametrize("kind", ["k", "v"])
-def test_edge_cases(kind):
+def test_edge_cases(kind, n_tok):
     """Degenerate groups, fully clipped groups, skipped slots and source rows,
     a gather index, and a ragged token count."""
     d, n_kv, n_pages = 128, 2, 3
     rng = np.random.default_rng(5)
     rot = np.stack([pins.random_orthogonal(d, rng) for _ in range(n_kv)])
-    x = synth.f32_to_bf16_bits(rng.standard_normal((41, n_kv, d)).astype(np.float32))
+    x = synth.f32_to_bf16_bits(rng.standard_normal((n_tok, n_kv, d)).astype(np.float32))
     x[3] = 0                                                   # all-zero token: scale 0
     x[4] = synth.f32_to_bf16_bits(np.full((n_kv, d), 1e4, np.float32))   # clipped everywhere
-    slots = rng.permutation(n_pages * PAGE)[:41].astype(np.int32)
+    slots = rng.permutation(n_pages * PAGE)[:n_tok].astype(np.int32)
     slots[7] = -5
     slots[8] = n_pages * PAGE + 3
-    src = rng.permutation(41).astype(np.int32)
-    src[9] = 41
+    src = rng.permutation(n_tok).astype(np.int32)
+    src[9] = n_tok
     src[10] = -1
     ref = _oracle(kind, x, rot, 2.0, slots, n_pages, src_idx=src)
     got = gpu_quantize(kind, x, rot, 2.0, slots, n_pages, src_idx=src)
