@@ -814,22 +814,96 @@ __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) vo
 // ---------------------------------------------------------------------------
 // 3. merge: LSE over history splits, * R_V^T, LSE with BF16 chunks, normalise
 // ---------------------------------------------------------------------------
-// One query head per block.  All partials (history splits and BF16 chunks)
-// share one reference maximum M:
-//   out = (sum_hist f_s acc_s R_V^T + sum_bf16 f_s acc_s) / sum_all f_s l_s,
-//   f_s = exp2(m_s - M).
-// Thread (c, part) owns channel c for the partials s = part (mod TPC); the
-// loads of a round of up to kMergeRound partials per thread, and of the
-// thread's slice of R_V, are all issued before any is used.
-constexpr int kMergeRound = 16;
+// Online LSE merge of partials (m, l, acc[D]) by one 256-thread block.
+// Thread (c, part) owns channel c of the partials s = part (mod TPC): it loads
+// up to kMergeRound of them at once (m, l and its channel), folds them into a
+// running (m, l, acc) and moves to the next round; the TPC parts are then
+// combined through LDS.  acc is split in two sums: partials s < n_rot (history,
+// still rotated) and the rest.
+constexpr int kMergeRound = 40;
 
+struct MergeState {
+  float m, l, a_rot, a_plain;
+};
+
+template <int D, typename PartPtr>
+__device__ __forceinline__ MergeState merge_partials(PartPtr part_ptr, int n_rot, int nt, int c, int part) {
+  constexpr int TPC = kBlock / D;
+  MergeState st{-INFINITY, 0.0f, 0.0f, 0.0f};
+  for (int s0 = part; s0 < nt; s0 += TPC * kMergeRound) {
+    float mv[kMergeRound], lv[kMergeRound], av[kMergeRound];
+#pragma unroll
+    for (int k = 0; k < kMergeRound; ++k) {
+      const int s = s0 + TPC * k;
+      const float* pp = part_ptr(s < nt ? s : s0);
+      mv[k] = s < nt ? pp[0] : -INFINITY;
+      lv[k] = s < nt ? pp[1] : 0.0f;
+      av[k] = s < nt ? pp[2 + c] : 0.0f;
+    }
+    float rm = st.m;
+#pragma unroll
+    for (int k = 0; k < kMergeRound; ++k) rm = fmaxf(rm, mv[k]);
+    const float alpha = exp2_or_zero(st.m, rm);
+    st.l *= alpha;
+    st.a_rot *= alpha;
+    st.a_plain *= alpha;
+#pragma unroll
+    for (int k = 0; k < kMergeRound; ++k) {
+      const int s = s0 + TPC * k;
+      const float f = exp2_or_zero(mv[k], rm);
+      st.l = fmaf(f, lv[k], st.l);
+      if (s < n_rot) st.a_rot = fmaf(f, av[k], st.a_rot);
+      else st.a_plain = fmaf(f, av[k], st.a_plain);
+    }
+    st.m = rm;
+  }
+  return st;
+}
+
+// Combine the TPC parts' states through LDS; returns the block-wide
+// (M, L) and leaves the combined channel sums in a_rot_s[c], a_plain_s[c].
+template <int D>
+__device__ __forceinline__ float2 combine_parts(const MergeState& st, float* m_s, float* l_s, float* a_rot_s,
+                                                float* a_plain_s, int c, int part) {
+  constexpr int TPC = kBlock / D;
+  if (c == 0) {
+    m_s[part] = st.m;
+    l_s[part] = st.l;
+  }
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < TPC; ++q) M = fmaxf(M, m_s[q]);
+  float L = 0.0f;
+#pragma unroll
+  for (int q = 0; q < TPC; ++q) L = fmaf(exp2_or_zero(m_s[q], M), l_s[q], L);
+  const float f = exp2_or_zero(st.m, M);
+  a_rot_s[part * D + c] = f * st.a_rot;
+  a_plain_s[part * D + c] = f * st.a_plain;
+  __syncthreads();
+  if (part == 0) {
+    float ar = 0.0f, ap = 0.0f;
+#pragma unroll
+    for (int q = 0; q < TPC; ++q) {
+      ar += a_rot_s[q * D + c];
+      ap += a_plain_s[q * D + c];
+    }
+    a_rot_s[c] = ar;
+    a_plain_s[c] = ap;
+  }
+  __syncthreads();
+  return make_float2(M, L);
+}
+
+// One query head per block:
+//   out = (sum_hist f_s acc_s R_V^T + sum_bf16 f_s acc_s) / sum_all f_s l_s,
+//   f_s = exp2(m_s - M) with M the maximum over every partial.
 template <int D>
 __global__ __launch_bounds__(kBlock) void merge_kernel(DecodeDev p) {
   constexpr int TPC = kBlock / D;   // threads per channel
   constexpr int SEG = D / TPC;      // R_V row segment per thread
-  __shared__ float red[kBlock / kWave];
-  __shared__ float ah_s[TPC][D], ab_s[TPC][D];
-  __shared__ float l_s[TPC];
+  __shared__ float m_s[TPC], l_s[TPC];
+  __shared__ float a_rot_s[kBlock], a_plain_s[kBlock];
   const int bh = blockIdx.x;
   const int b = bh / p.Hq, h = bh % p.Hq, g = h / p.G, kh = h % p.G;
   const int tid = threadIdx.x, c = tid % D, part = tid / D;
@@ -837,7 +911,7 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(DecodeDev p) {
   const float* hp = p.hpart + ((size_t)b * p.n_kv + g) * p.splits * stride + (size_t)kh * (D + 2);
   const float* bp = p.bpart + ((size_t)b * p.n_kv + g) * p.chunks * stride + (size_t)kh * (D + 2);
   const int n = p.splits, nt = p.splits + p.chunks;
-  // output row i = tid / TPC, segment seg = tid % TPC of R_V[g][i][:]
+  // this thread's segment of output row i = tid / TPC of the R_V product
   const int i = tid / TPC, seg = tid % TPC;
   float rv[SEG];
   {
@@ -845,64 +919,20 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(DecodeDev p) {
 #pragma unroll
     for (int k = 0; k < SEG; ++k) rv[k] = Rrow[k];
   }
-  auto part_ptr = [&](int s) { return s < n ? hp + (size_t)s * stride : bp + (size_t)(s - n) * stride; };
-
-  // reference maximum over every partial
-  float m_loc = -INFINITY;
-  for (int s = tid; s < nt; s += kBlock) m_loc = fmaxf(m_loc, part_ptr(s)[0]);
-  m_loc = wave_max(m_loc);
-  if ((tid & (kWave - 1)) == 0) red[tid / kWave] = m_loc;
-  __syncthreads();
-  float M = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < kBlock / kWave; ++w) M = fmaxf(M, red[w]);
-
-  float ah = 0.0f, ab = 0.0f, l = 0.0f;
-  for (int s0 = part; s0 < nt; s0 += TPC * kMergeRound) {
-    float mv[kMergeRound], lv[kMergeRound], av[kMergeRound];
-#pragma unroll
-    for (int k = 0; k < kMergeRound; ++k) {
-      const int s = s0 + TPC * k;
-      const float* pp = part_ptr(s < nt ? s : 0);
-      mv[k] = s < nt ? pp[0] : -INFINITY;
-      lv[k] = s < nt ? pp[1] : 0.0f;
-      av[k] = pp[2 + c];
-    }
-#pragma unroll
-    for (int k = 0; k < kMergeRound; ++k) {
-      const int s = s0 + TPC * k;
-      const float f = exp2_or_zero(mv[k], M);
-      l += f * lv[k];
-      if (s < n) ah = fmaf(f, av[k], ah);
-      else if (s < nt) ab = fmaf(f, av[k], ab);
-    }
-  }
-  ah_s[part][c] = ah;
-  ab_s[part][c] = ab;
-  if (c == 0) l_s[part] = l;   // the same in every channel of a part
-  __syncthreads();
-  float L = 0.0f;
-#pragma unroll
-  for (int q = 0; q < TPC; ++q) L += l_s[q];
+  const MergeState st = merge_partials<D>(
+      [&](int s) { return s < n ? hp + (size_t)s * stride : bp + (size_t)(s - n) * stride; }, n, nt, c, part);
+  const float2 ML = combine_parts<D>(st, m_s, l_s, a_rot_s, a_plain_s, c, part);
   // out_hist[i] = sum_j A_hist[j] R_V[g][i][j]
   float o = 0.0f;
 #pragma unroll
-  for (int k = 0; k < SEG; ++k) {
-    const int jj = seg * SEG + k;
-    float a = 0.0f;
-#pragma unroll
-    for (int q = 0; q < TPC; ++q) a += ah_s[q][jj];
-    o = fmaf(a, rv[k], o);
-  }
+  for (int k = 0; k < SEG; ++k) o = fmaf(a_rot_s[seg * SEG + k], rv[k], o);
 #pragma unroll
   for (int off = 1; off < TPC; off <<= 1) o += __shfl_xor(o, off, kWave);
   if (seg == 0) {
-    float ob = 0.0f;
-#pragma unroll
-    for (int q = 0; q < TPC; ++q) ob += ab_s[q][i];
+    const float L = ML.y;
     float out;
     if (isnan(L)) out = NAN;
-    else out = (L > 0.0f) ? (o + ob) / L : 0.0f;
+    else out = (L > 0.0f) ? (o + a_plain_s[i]) / L : 0.0f;
     p.out[(size_t)bh * D + i] = out;
   }
 }
@@ -951,24 +981,23 @@ __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : 2)) void bf16_paged_kernel(Bf1
 }
 
 template <int D>
-__global__ __launch_bounds__(128) void merge_plain_kernel(Bf16Dev p) {
+__global__ __launch_bounds__(kBlock) void merge_plain_kernel(Bf16Dev p) {
+  __shared__ float m_s[kBlock / D], l_s[kBlock / D];
+  __shared__ float a_rot_s[kBlock], a_plain_s[kBlock];
   const int bh = blockIdx.x;
   const int b = bh / p.Hq, h = bh % p.Hq, g = h / p.G, kh = h % p.G;
-  const int c = threadIdx.x;
+  const int tid = threadIdx.x, c = tid % D, part = tid / D;
   const size_t stride = (size_t)p.G * (D + 2);
   const float* pp = p.part + ((size_t)b * p.n_kv + g) * p.splits * stride + (size_t)kh * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < p.splits; ++s) M = fmaxf(M, pp[s * stride]);
-  float L = 0.0f, A = 0.0f;
-  for (int s = 0; s < p.splits; ++s) {
-    const float f = exp2_or_zero(pp[s * stride], M);
-    L += f * pp[s * stride + 1];
-    if (c < D) A += f * pp[s * stride + 2 + c];
+  const MergeState st = merge_partials<D>([&](int s) { return pp + (size_t)s * stride; }, 0, p.splits, c, part);
+  const float2 ML = combine_parts<D>(st, m_s, l_s, a_rot_s, a_plain_s, c, part);
+  if (part == 0) {
+    const float L = ML.y;
+    float o;
+    if (isnan(L)) o = NAN;
+    else o = (L > 0.0f) ? a_plain_s[c] / L : 0.0f;
+    p.out[(size_t)bh * D + c] = o;
   }
-  float o;
-  if (isnan(L)) o = NAN;
-  else o = (L > 0.0f) ? A / L : 0.0f;
-  if (c < D) p.out[(size_t)bh * D + c] = o;
 }
 
 template <int D, int G>
@@ -1073,8 +1102,8 @@ hipError_t launch_decode_bf16(const oscar_bf16_decode_args& a, const Bf16Plan& p
     if (a.head_dim == 128) launch_bf16_g<128>(dv, stream);
     else launch_bf16_g<64>(dv, stream);
   }
-  if (a.head_dim == 128) merge_plain_kernel<128><<<nbh, 128, 0, stream>>>(dv);
-  else merge_plain_kernel<64><<<nbh, 128, 0, stream>>>(dv);
+  if (a.head_dim == 128) merge_plain_kernel<128><<<nbh, kBlock, 0, stream>>>(dv);
+  else merge_plain_kernel<64><<<nbh, kBlock, 0, stream>>>(dv);
   return hipGetLastError();
 }
 
