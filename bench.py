@@ -129,23 +129,26 @@ def main():
     log(f"demoted the history into {R} replicas in {time.time() - t0:.1f}s")
     del hist_k, hist_v
     ws_bytes = hip.oscar_decode_workspace_bytes(B, Hq, n_kv, d, hl, cfg["sink_k"].shape[2], cap)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     dargs = [hip.decode_args(q=q, sink_k=rp["sink_k"], sink_v=rp["sink_v"], recent_k=rp["recent_k"],
                              recent_v=rp["recent_v"], sink_len=sink_len, recent_len=recent_len,
                              hist_len=hist_len, max_hist_len=hl, k_codes=rp["k_codes"], v_codes=rp["v_codes"],
                              k_sz=rp["k_sz"], v_sz=rp["v_sz"], block_table=table, r_k=r_k, r_v=r_v,
                              out=rp["out"], workspace=ws, sm_scale=float(cfg["sm_scale"])) for rp in reps]
 
-    def demote(r):
+    # the step demotes ring slot 0 of every request's recent window (K and V) in
+    # the decode's first launch
+    dem = []
+    for r in range(R):
         rp = reps[r]
-        for kind, x, rot, tau, codes, sz in ((hip.KIND_K, rp["recent_k"], r_k, cfg["tau_k"], rp["k_codes"], rp["k_sz"]),
-                                             (hip.KIND_V, rp["recent_v"], r_v, cfg["tau_v"], rp["v_codes"], rp["v_sz"])):
-            hip.oscar_quantize_pack(kind, x, rot, float(tau), step_slot, codes, sz, src_idx=step_src,
-                                    n_src=B * n_kv * cap, x_tok_stride=d, x_head_stride=cap * d)
+        common = dict(src_idx=step_src, n_src=B * n_kv * cap, x_tok_stride=d, x_head_stride=cap * d)
+        dem.append((hip.demote_args(x=rp["recent_k"], rot=r_k, clip=float(cfg["tau_k"]), dst_slot=step_slot,
+                                    codes=rp["k_codes"], scale_zero=rp["k_sz"], **common),
+                    hip.demote_args(x=rp["recent_v"], rot=r_v, clip=float(cfg["tau_v"]), dst_slot=step_slot,
+                                    codes=rp["v_codes"], scale_zero=rp["v_sz"], **common)))
 
     def step(r):
-        demote(r)
-        hip.oscar_decode_attn(args=dargs[r])
+        hip.oscar_decode_step(args=dargs[r], demote_k=dem[r][0], demote_v=dem[r][1])
 
     def capture(fn, idxs):
         g = torch.cuda.CUDAGraph()
@@ -216,7 +219,7 @@ def main():
         "config": {"workload": shape.name, "batch": B, "context": shape.context, "n_q_heads": Hq,
                    "n_kv_heads": n_kv, "head_dim": d, "sink": int(cfg["sink_len"][0]),
                    "history": hl, "recent": int(cfg["recent_len"][0]), "page_tokens": 64,
-                   "cache_replicas": R, "step": "demote K,V of 1 token/request + decode attention"},
+                   "cache_replicas": R, "step": "oscar_decode_step: demote K,V of 1 token/request + decode attention"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload),
                      "kernel": "decode_main_kernel (oscar_decode_scan)", "kernel_us": scan_us,

@@ -35,6 +35,13 @@ class DecodeArgs(ctypes.Structure):
                 ("block_table", _vp), ("max_pages", _i32), ("r_k", _vp), ("r_v", _vp), ("out", _vp)]
 
 
+class DemoteArgs(ctypes.Structure):
+    """Mirror of ``oscar_demote_args``."""
+    _fields_ = [("x", _vp), ("n_src", _i64), ("x_tok_stride", _i64), ("x_head_stride", _i64),
+                ("src_idx", _vp), ("n_tok", _i64), ("rot", _vp), ("clip", _f32), ("dst_slot", _vp),
+                ("codes", _vp), ("scale_zero", _vp), ("n_pages", _i64)]
+
+
 class Bf16DecodeArgs(ctypes.Structure):
     """Mirror of ``oscar_bf16_decode_args``."""
     _fields_ = [("batch", _i32), ("n_q_heads", _i32), ("n_kv_heads", _i32), ("head_dim", _i32),
@@ -66,6 +73,9 @@ def lib() -> ctypes.CDLL:
     for name in ("oscar_decode_attn", "oscar_decode_rotate_query", "oscar_decode_scan", "oscar_decode_merge"):
         getattr(L, name).restype = ctypes.c_int
         getattr(L, name).argtypes = [ctypes.POINTER(DecodeArgs), _vp, _sz, _vp]
+    L.oscar_decode_step.restype = ctypes.c_int
+    L.oscar_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(DemoteArgs),
+                                    ctypes.POINTER(DemoteArgs), _vp, _sz, _vp]
     L.oscar_decode_bf16_workspace_bytes.restype = _sz
     L.oscar_decode_bf16_workspace_bytes.argtypes = [_i32] * 5
     L.oscar_decode_attn_bf16.restype = ctypes.c_int
@@ -199,6 +209,41 @@ def oscar_decode_scan(*, args=None, stream=None, **kw) -> None:
 def oscar_decode_merge(*, args=None, stream=None, **kw) -> None:
     """Phase 3 of oscar_decode_attn: merge partials, apply R_V^T, normalise."""
     _decode("oscar_decode_merge", args, stream, kw)
+
+
+def demote_args(*, x, rot, clip: float, dst_slot, codes, scale_zero, src_idx=None, n_src=None,
+                x_tok_stride=None, x_head_stride=None) -> DemoteArgs:
+    """Marshal one tensor's demotion for :func:`oscar_decode_step` (arguments
+    as for :func:`oscar_quantize_pack`).  The tensors must stay alive while
+    the call (or a captured graph) uses them."""
+    n_kv, d = rot.shape[0], rot.shape[-1]
+    if x_tok_stride is None:
+        if x.dim() != 3 or x.shape[1:] != (n_kv, d):
+            raise ValueError("x must be [n_src][n_kv][d]")
+        n_src, x_tok_stride, x_head_stride = x.shape[0], n_kv * d, d
+    n_tok = dst_slot.numel()
+    if src_idx is not None and src_idx.numel() != n_tok:
+        raise ValueError("src_idx and dst_slot lengths differ")
+    if codes.shape[1:] != (n_kv, PAGE * d // 4) or scale_zero.shape[1:] != (n_kv, PAGE, 2):
+        raise ValueError("pool shapes do not match [n_pages][n_kv][...]")
+    if dst_slot.dtype.itemsize != 4 or (src_idx is not None and src_idx.dtype.itemsize != 4):
+        raise ValueError("dst_slot / src_idx must be int32")
+    return DemoteArgs(x=_ptr(x, 2, "x"), n_src=int(n_src), x_tok_stride=int(x_tok_stride),
+                      x_head_stride=int(x_head_stride), src_idx=_ptr(src_idx, 4, "src_idx"), n_tok=int(n_tok),
+                      rot=_ptr(rot, 4, "rot"), clip=float(clip), dst_slot=_ptr(dst_slot, 4, "dst_slot"),
+                      codes=_ptr(codes, 1, "codes"), scale_zero=_ptr(scale_zero, 2, "scale_zero"),
+                      n_pages=int(codes.shape[0]))
+
+
+def oscar_decode_step(*, args, demote_k=None, demote_v=None, stream=None) -> None:
+    """One decode step (see oscar_decode_step in oscar.h): the demotions
+    (:func:`demote_args` results, or None) run in the decode's first launch.
+    ``args`` is a :func:`decode_args` tuple."""
+    a, ws, nbytes = args
+    st = lib().oscar_decode_step(ctypes.byref(a), ctypes.byref(demote_k) if demote_k is not None else None,
+                                 ctypes.byref(demote_v) if demote_v is not None else None, ws, nbytes,
+                                 _stream(stream))
+    _check(st, "oscar_decode_step")
 
 
 def oscar_decode_bf16_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, max_ctx_len) -> int:

@@ -101,13 +101,28 @@ oscar_status check_decode(const oscar_decode_args* a, void* workspace, size_t wo
   return OSCAR_OK;
 }
 
+oscar_status check_demote(const oscar_demote_args* d, int32_t n_kv) {
+  if (!d || d->n_tok == 0) return OSCAR_OK;
+  if (d->n_tok < 0 || d->n_tok > ((int64_t)1 << 24) / n_kv) return OSCAR_EINVAL;
+  if (d->n_src < 0 || d->x_tok_stride < 0 || d->x_head_stride < 0) return OSCAR_EINVAL;
+  if (d->n_pages < 0 || d->n_pages > ((int64_t)1 << 40)) return OSCAR_EINVAL;
+  if (!std::isfinite(d->clip) || !(d->clip > 0.0f) || d->clip > 65504.0f) return OSCAR_EINVAL;
+  if (!d->x || !d->rot || !d->dst_slot || !d->codes || !d->scale_zero) return OSCAR_EINVAL;
+  return OSCAR_OK;
+}
+
 oscar_status run_phases(const oscar_decode_args* a, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream, int first, int last) {
+                        hipStream_t stream, int first, int last, const oscar_demote_args* dk = nullptr,
+                        const oscar_demote_args* dv = nullptr) {
   DecodePlan plan;
-  const oscar_status st = check_decode(a, workspace, workspace_bytes, &plan);
-  if (st != OSCAR_OK || a->batch == 0) return st;
+  oscar_status st = check_decode(a, workspace, workspace_bytes, &plan);
+  if (st != OSCAR_OK) return st;
+  if ((st = check_demote(dk, a->n_kv_heads)) != OSCAR_OK || (st = check_demote(dv, a->n_kv_heads)) != OSCAR_OK)
+    return st;
+  const bool demote = (dk && dk->n_tok > 0) || (dv && dv->n_tok > 0);
+  if (a->batch == 0 && !demote) return OSCAR_OK;
   for (int ph = first; ph <= last; ++ph) {
-    const hipError_t e = launch_decode_phase(ph, *a, plan, static_cast<char*>(workspace), stream);
+    const hipError_t e = launch_decode_phase(ph, *a, plan, static_cast<char*>(workspace), stream, dk, dv);
     if (e != hipSuccess) return OSCAR_EHIP;
   }
   return OSCAR_OK;
@@ -119,6 +134,12 @@ extern "C" {
 oscar_status oscar_decode_attn(const oscar_decode_args* a, void* workspace, size_t workspace_bytes,
                                hipStream_t stream) {
   return run_phases(a, workspace, workspace_bytes, stream, kPhaseRotate, kPhaseMerge);
+}
+
+oscar_status oscar_decode_step(const oscar_decode_args* a, const oscar_demote_args* demote_k,
+                               const oscar_demote_args* demote_v, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  return run_phases(a, workspace, workspace_bytes, stream, kPhaseRotate, kPhaseMerge, demote_k, demote_v);
 }
 
 oscar_status oscar_decode_rotate_query(const oscar_decode_args* a, void* workspace, size_t workspace_bytes,

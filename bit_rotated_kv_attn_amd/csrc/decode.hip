@@ -31,6 +31,7 @@
 //                           with the BF16 partials, normalise
 // Softmax state uses base-2 exponents (logits pre-scaled by log2 e).
 #include "common.hpp"
+#include "demote.hpp"
 
 namespace oscar {
 namespace {
@@ -59,6 +60,37 @@ struct DecodeDev {
   float *qa, *qb;    // [B][Hq] logit constants: sm_log2/(16 kq), sm_log2*sum(q_rot)
   float *hpart, *bpart;
 };
+
+struct DemoteDev {   // one tensor's demotion inside a decode step (n_tok = 0: none)
+  const uint16_t* x;
+  int64_t n_src, tok_stride, head_stride;
+  const int32_t* src_idx;
+  int64_t n_tok;
+  const float* rot;
+  float clip;
+  const int32_t* dst_slot;
+  uint8_t* codes;
+  uint32_t* sz;
+  int64_t n_pages;
+};
+
+DemoteDev make_demote(const oscar_demote_args* d) {
+  DemoteDev m{};
+  if (!d) return m;
+  m.x = d->x;
+  m.n_src = d->n_src;
+  m.tok_stride = d->x_tok_stride;
+  m.head_stride = d->x_head_stride;
+  m.src_idx = d->src_idx;
+  m.n_tok = d->n_tok;
+  m.rot = d->rot;
+  m.clip = d->clip;
+  m.dst_slot = d->dst_slot;
+  m.codes = d->codes;
+  m.sz = reinterpret_cast<uint32_t*>(d->scale_zero);
+  m.n_pages = d->n_pages;
+  return m;
+}
 
 struct Bf16Dev {
   int B, Hq, n_kv, G, max_pages, max_ctx_len, splits, pps;
@@ -656,13 +688,12 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int b, int g, int 
 // 1. rotate the query: q_rot = q R_K[g]; MFMA digit operands and constants
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kBlock) void rotate_query_kernel(DecodeDev p) {
+__device__ __forceinline__ void rotate_query_block(const DecodeDev& p, int bh) {
   constexpr int NCH = D / 64, PLANE = D / 16;
   constexpr int P = kBlock / D, IP = D / P;   // row parts of each dot product; every load in flight at once
   __shared__ float qs[D];
   __shared__ float part_s[P][D];
   __shared__ float red[2][kBlock / kWave];
-  const int bh = blockIdx.x;
   const int b = bh / p.Hq, h = bh % p.Hq, g = h / p.G, hl = h % p.G;
   const int tid = threadIdx.x, j = tid % D, part = tid / D;
   const float* R = p.r_k + (size_t)g * D * D + (size_t)part * IP * D + j;
@@ -718,6 +749,25 @@ __global__ __launch_bounds__(kBlock) void rotate_query_kernel(DecodeDev p) {
     p.qa[bh] = p.sm_log2 / (16.0f * kq);
     p.qb[bh] = p.sm_log2 * qsum;
   }
+}
+
+// Launch 1 of a decode: one block per query head rotates q; in a decode step
+// the same launch also demotes the step's K and V tokens (one block per
+// token and KV head), which the decode does not read.
+template <int D>
+__global__ __launch_bounds__(kBlock) void prepare_kernel(DecodeDev p, int n_rot, DemoteDev dk, DemoteDev dv) {
+  int id = blockIdx.x;
+  if (id < n_rot) {
+    rotate_query_block<D>(p, id);
+    return;
+  }
+  id -= n_rot;
+  const int64_t nk = dk.n_tok * p.n_kv;
+  const DemoteDev& dm = id < nk ? dk : dv;
+  const int kind = id < nk ? OSCAR_KIND_K : OSCAR_KIND_V;
+  if (id >= nk) id -= (int)nk;
+  demote_token_block<D>(kind, dm.x, dm.n_src, dm.tok_stride, dm.head_stride, dm.src_idx, id / p.n_kv, id % p.n_kv,
+                        p.n_kv, dm.rot, dm.clip, dm.dst_slot, dm.codes, dm.sz, dm.n_pages);
 }
 
 // ---------------------------------------------------------------------------
@@ -1064,16 +1114,21 @@ DecodeDev make_dev(const oscar_decode_args& a, const DecodePlan& plan, char* ws)
 }  // namespace
 
 hipError_t launch_decode_phase(int phase, const oscar_decode_args& a, const DecodePlan& plan, char* ws,
-                               hipStream_t stream) {
-  if (a.batch == 0) return hipSuccess;
+                               hipStream_t stream, const oscar_demote_args* demote_k,
+                               const oscar_demote_args* demote_v) {
   const DecodeDev dv = make_dev(a, plan, ws);
   const unsigned nbh = (unsigned)a.batch * (unsigned)a.n_q_heads;
   const bool d128 = a.head_dim == 128;
   if (phase == kPhaseRotate) {
-    if (plan.splits > 0) {
-      if (d128) rotate_query_kernel<128><<<nbh, kBlock, 0, stream>>>(dv);
-      else rotate_query_kernel<64><<<nbh, kBlock, 0, stream>>>(dv);
+    const int n_rot = plan.splits > 0 ? (int)nbh : 0;
+    const DemoteDev mk = make_demote(demote_k), mv = make_demote(demote_v);
+    const int64_t blocks = n_rot + (mk.n_tok + mv.n_tok) * a.n_kv_heads;
+    if (blocks > 0) {
+      if (d128) prepare_kernel<128><<<(unsigned)blocks, kBlock, 0, stream>>>(dv, n_rot, mk, mv);
+      else prepare_kernel<64><<<(unsigned)blocks, kBlock, 0, stream>>>(dv, n_rot, mk, mv);
     }
+  } else if (a.batch == 0) {
+    return hipSuccess;
   } else if (phase == kPhaseScan) {
     if (d128) launch_main_g<128>(dv, stream);
     else launch_main_g<64>(dv, stream);

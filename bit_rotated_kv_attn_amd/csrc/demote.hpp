@@ -1,0 +1,98 @@
+// One-token INT2 demotion (rotate -> clip -> quantise -> pack) by one
+// 256-thread block, shared by oscar_quantize_pack's few-token path and the
+// fused decode step.  Same arithmetic as the tiled kernel: the rotated value is
+// an fp64 dot product rounded once to fp32; zero = fp16(min), scale =
+// fp16((max - min) / 3); code = rint((y - zero) / scale) clamped to [0, 3].
+// Source: the demotion step of the serving pipeline in the myzaker.com article
+// on OSCAR; R and the clip threshold from the gist.science OSCAR technical
+// summary, section 2.2A.
+#pragma once
+
+#include "common.hpp"
+
+namespace oscar {
+
+// Thread (j, part) loads its D/P entries of column j of R at once, so the
+// block waits for one round of loads, and computes a partial fp64 dot; the P
+// partials are added in fp64 and rounded once to fp32.
+template <int D>
+__device__ __forceinline__ void demote_token_block(int kind, const uint16_t* __restrict__ x, int64_t n_src,
+                                                   int64_t tok_stride, int64_t head_stride,
+                                                   const int32_t* __restrict__ src_idx, int64_t t, int g, int n_kv,
+                                                   const float* __restrict__ rot, float clip,
+                                                   const int32_t* __restrict__ dst_slot, uint8_t* __restrict__ codes,
+                                                   uint32_t* __restrict__ sz, int64_t n_pages) {
+  constexpr int P = kBlock / D;          // row parts of the dot product
+  constexpr int IP = D / P;              // rows per part
+  constexpr int kRowBytes = D / 4;
+  constexpr int kPlane = D / 16;
+  __shared__ float xs[D];
+  __shared__ double parts[P][D];
+  __shared__ float ys[D];
+  __shared__ float red[2][kBlock / kWave];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int64_t src = src_idx ? (int64_t)src_idx[t] : t;
+  const int64_t slot = dst_slot[t];
+  if (src < 0 || src >= n_src || slot < 0 || slot >= n_pages * kPage) return;   // block-uniform
+
+  const int j = tid % D, part = tid / D;
+  const float* R = rot + (size_t)g * D * D + (size_t)part * IP * D + j;
+  float r[IP];
+#pragma unroll
+  for (int k = 0; k < IP; ++k) r[k] = R[(size_t)k * D];
+  if (tid < D) xs[tid] = bf16_to_f32(x[src * tok_stride + (int64_t)g * head_stride + tid]);
+  __syncthreads();
+  double acc = 0.0;
+#pragma unroll
+  for (int k = 0; k < IP; ++k) acc = fma((double)xs[part * IP + k], (double)r[k], acc);
+  parts[part][j] = acc;
+  __syncthreads();
+
+  float mn = INFINITY, mx = -INFINITY;
+  if (tid < D) {
+    double y = parts[0][tid];
+#pragma unroll
+    for (int q = 1; q < P; ++q) y += parts[q][tid];
+    const float yc = fminf(fmaxf((float)y, -clip), clip);
+    ys[tid] = yc;
+    mn = yc;
+    mx = yc;
+  }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  if (lane == 0) {
+    red[0][wave] = mn;
+    red[1][wave] = mx;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kBlock / kWave; ++w) {
+    mn = fminf(mn, red[0][w]);
+    mx = fmaxf(mx, red[1][w]);
+  }
+  const __half zh = __float2half_rn(mn);
+  const __half sh = __float2half_rn(__fdiv_rn(mx - mn, 3.0f));
+  const float z = __half2float(zh), s = __half2float(sh);
+  const int64_t page = slot / kPage;
+  const int o = (int)(slot % kPage);
+  if (tid == 0)
+    sz[(page * n_kv + g) * kPage + o] = (uint32_t)__half_as_ushort(sh) | ((uint32_t)__half_as_ushort(zh) << 16);
+  if (tid < kRowBytes) {
+    const int i = tid;
+    uint32_t byte = 0;
+    if (s != 0.0f) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float v = rintf(__fdiv_rn(ys[4 * i + q] - z, s));
+        v = fminf(fmaxf(v, 0.0f), 3.0f);
+        byte |= (uint32_t)v << (2 * q);
+      }
+    }
+    uint8_t* blk = codes + (page * n_kv + g) * (int64_t)(kPage * kRowBytes);
+    const int pos = (kind == OSCAR_KIND_K) ? (i / kPlane) * (kPage * kPlane) + o * kPlane + (i % kPlane)
+                                           : i * kPage + o;
+    blk[pos] = (uint8_t)byte;
+  }
+}
+
+}  // namespace oscar

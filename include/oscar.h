@@ -185,6 +185,42 @@ OSCAR_API oscar_status oscar_decode_merge(const oscar_decode_args* args, void* w
                                           size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * One tensor's demotion inside a decode step: the arguments of
+ * oscar_quantize_pack except kind, n_kv and head_dim (taken from the step).
+ * n_tok in [0, 2^24 / n_kv]; the other rules are those of oscar_quantize_pack.
+ */
+typedef struct oscar_demote_args {
+  const uint16_t* x;          /* bf16 source: element (s, g, c) at x[s*x_tok_stride + g*x_head_stride + c] */
+  int64_t n_src;
+  int64_t x_tok_stride;
+  int64_t x_head_stride;
+  const int32_t* src_idx;     /* int32 [n_tok] or NULL */
+  int64_t n_tok;
+  const float* rot;           /* fp32 [n_kv][head_dim][head_dim] */
+  float clip;
+  const int32_t* dst_slot;    /* int32 [n_tok] */
+  uint8_t* codes;             /* INT2 code pool */
+  uint16_t* scale_zero;       /* fp16 (scale, zero) pool */
+  int64_t n_pages;
+} oscar_demote_args;
+
+/*
+ * One steady-state decode step (the serving pipeline of the myzaker.com
+ * article on OSCAR): demote the step's K and V tokens into INT2 history and
+ * run decode attention, with the demotions folded into the decode's first
+ * launch (three launches in all instead of five).  demote_k / demote_v may
+ * be NULL.  They may write into the pools this decode reads, but only into
+ * slots the decode does not attend (at or past hist_len of their request): the
+ * step attends the token it demotes in BF16 from the recent window, and the
+ * caller's next step counts it in hist_len.  Otherwise the result is
+ * unspecified.  Same workspace and status rules as oscar_decode_attn; with
+ * batch 0 only the demotions run.
+ */
+OSCAR_API oscar_status oscar_decode_step(const oscar_decode_args* args, const oscar_demote_args* demote_k,
+                                         const oscar_demote_args* demote_v, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream);
+
+/*
  * BF16 comparator: plain decode attention with the whole context held in
  * BF16 pages (no rotation, no quantisation), same GQA mapping and output
  * rules.  Used to measure the INT2 path against a BF16 cache of the same

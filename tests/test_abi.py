@@ -115,3 +115,39 @@ def test_workspace_sizes_are_positive():
     assert hip.oscar_decode_workspace_bytes(1, 64, 8, 128, 99680) > 0
     assert hip.oscar_decode_workspace_bytes(1, 64, 8, 128, 0) > 0
     assert hip.oscar_decode_bf16_workspace_bytes(28, 32, 8, 128, 100000) > 0
+
+
+def _demote(**kw):
+    d = hip.DemoteArgs(x=1, n_src=4, x_tok_stride=256, x_head_stride=128, src_idx=None, n_tok=1, rot=1, clip=3.0,
+                       dst_slot=1, codes=1, scale_zero=1, n_pages=2)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_tok=-1), hip.OSCAR_EINVAL),
+    (dict(n_tok=(1 << 24)), hip.OSCAR_EINVAL),                      # > 2^24 / n_kv
+    (dict(clip=0.0), hip.OSCAR_EINVAL),
+    (dict(clip=float("inf")), hip.OSCAR_EINVAL),
+    (dict(x=None), hip.OSCAR_EINVAL),
+    (dict(rot=None), hip.OSCAR_EINVAL),
+    (dict(codes=None), hip.OSCAR_EINVAL),
+    (dict(n_src=-2), hip.OSCAR_EINVAL),
+    (dict(n_tok=0, x=None, rot=None, codes=None), None),            # nothing to demote: decode checks decide
+])
+def test_decode_step_validation(kw, status):
+    """Step arguments are checked on the host before any HIP call: bad
+    demotion arguments fail even when the decode arguments are valid."""
+    L = hip.lib()
+    a = _decode_args(q=None)                                         # decode itself invalid
+    good = _decode_args()
+    dk = _demote(**kw)
+    if status is None:
+        assert L.oscar_decode_step(ctypes.byref(a), ctypes.byref(dk), None, ctypes.c_void_p(256), 1 << 30,
+                                   None) == hip.OSCAR_EINVAL
+        return
+    assert L.oscar_decode_step(ctypes.byref(good), ctypes.byref(dk), None, ctypes.c_void_p(260), 1 << 30,
+                               None) == hip.OSCAR_EWORKSPACE   # workspace checked first
+    assert L.oscar_decode_step(ctypes.byref(_decode_args(batch=0, q=None, out=None)), None, ctypes.byref(dk),
+                               None, 0, None) == status

@@ -1,0 +1,103 @@
+"""GPU parity of oscar_decode_step: the step's K and V demotions run in the
+decode's first launch.  The decode must equal the oracle decode of the cache
+as given (the demoted slots lie past hist_len), and the demoted slots must
+equal the oracle quantiser's output for the demoted tokens."""
+import numpy as np
+import pytest
+import torch
+
+import bit_rotated_kv_attn_amd as hip
+import oracle
+import synth
+from gpu_util import PAGE, compare_out, compare_quant, dev, host, oracle_pools
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [
+    synth.DecodeShape("step-b1-h4kv2-d64-L1024", 1, 4, 2, 64, 1024),          # history ends on a page boundary
+    synth.DecodeShape("step-b3-h16kv2-d128-L1000", 3, 16, 2, 128, 1000),       # partial last page, 3 requests
+]
+
+
+def _with_free_slots(cfg):
+    """Append one page per request to the pool and the table so that slot
+    hist_len of every request exists; return the widened config and the
+    step's destination slots."""
+    B = cfg["q"].shape[0]
+    table = cfg["block_table"]
+    extra = (cfg["n_pages"] + np.arange(B)).astype(np.int32)[:, None]
+    cfg = dict(cfg, block_table=np.concatenate([table, extra], axis=1), n_pages=cfg["n_pages"] + B)
+    hl = cfg["hist_len"]
+    slot = cfg["block_table"][np.arange(B), hl // PAGE] * PAGE + hl % PAGE
+    return cfg, slot.astype(np.int32)
+
+
+def _pools_with_room(cfg):
+    kc, vc, ks, vs = oracle_pools(cfg)
+    return kc, vc, ks, vs
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[s.name for s in SHAPES])
+def test_decode_step_matches_separate_oracle_steps(shape):
+    cfg, slot = _with_free_slots(synth.make_decode_config(0, shape=shape, seed_index=7))
+    B, Hq, d = cfg["q"].shape
+    n_kv, cap = cfg["n_kv"], cfg["recent_k"].shape[2]
+    kc, vc, ks, vs = _pools_with_room(cfg)
+    ref_out = oracle.decode_attn_ref(cfg, kc, vc, ks, vs)
+    # the step demotes ring slot 3 of every request's recent window
+    ring = 3
+    src = (np.arange(B) * n_kv * cap + ring).astype(np.int32)
+    kc_ref, vc_ref, ks_ref, vs_ref = kc.copy(), vc.copy(), ks.copy(), vs.copy()
+    dk_ref = oracle.quantize_pack_ref("k", cfg["recent_k"][:, :, ring, :], cfg["r_k"], cfg["tau_k"], slot,
+                                      kc_ref, ks_ref)
+    dv_ref = oracle.quantize_pack_ref("v", cfg["recent_v"][:, :, ring, :], cfg["r_v"], cfg["tau_v"], slot,
+                                      vc_ref, vs_ref)
+
+    pools = [dev(p) for p in (kc, vc, ks, vs)]
+    ws = torch.zeros(hip.oscar_decode_workspace_bytes(B, Hq, n_kv, d, int(cfg["hist_len"].max()), 64, cap),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    rk, rv, rec_k, rec_v = dev(cfg["r_k"]), dev(cfg["r_v"]), dev(cfg["recent_k"]), dev(cfg["recent_v"])
+    src_t, slot_t = dev(src), dev(slot)
+    args = hip.decode_args(q=dev(cfg["q"]), sink_k=dev(cfg["sink_k"]), sink_v=dev(cfg["sink_v"]), recent_k=rec_k,
+                           recent_v=rec_v, sink_len=dev(cfg["sink_len"]), recent_len=dev(cfg["recent_len"]),
+                           hist_len=dev(cfg["hist_len"]), max_hist_len=int(cfg["hist_len"].max()),
+                           k_codes=pools[0], v_codes=pools[1], k_sz=pools[2], v_sz=pools[3],
+                           block_table=dev(cfg["block_table"]), r_k=rk, r_v=rv, out=out, workspace=ws,
+                           sm_scale=float(cfg["sm_scale"]))
+    common = dict(src_idx=src_t, n_src=B * n_kv * cap, x_tok_stride=d, x_head_stride=cap * d)
+    dk = hip.demote_args(x=rec_k, rot=rk, clip=float(cfg["tau_k"]), dst_slot=slot_t, codes=pools[0],
+                         scale_zero=pools[2], **common)
+    dv = hip.demote_args(x=rec_v, rot=rv, clip=float(cfg["tau_v"]), dst_slot=slot_t, codes=pools[1],
+                         scale_zero=pools[3], **common)
+    hip.oscar_decode_step(args=args, demote_k=dk, demote_v=dv)
+    torch.cuda.synchronize()
+    compare_out(host(out), ref_out, what=f"step decode {shape.name}")
+    compare_quant("k", host(pools[0]), host(pools[2], np.uint16), kc_ref, ks_ref, dk_ref, d)
+    compare_quant("v", host(pools[1]), host(pools[3], np.uint16), vc_ref, vs_ref, dv_ref, d)
+
+
+def test_decode_step_without_demotion_equals_decode():
+    cfg = synth.make_decode_config(0)
+    B, Hq, d = cfg["q"].shape
+    pools = [dev(p) for p in oracle_pools(cfg)]
+    cap = cfg["recent_k"].shape[2]
+    ws = torch.zeros(hip.oscar_decode_workspace_bytes(B, Hq, cfg["n_kv"], d, int(cfg["hist_len"].max()), 64, cap),
+                     dtype=torch.uint8, device="cuda")
+    outs = []
+    for use_step in (False, True):
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+        args = hip.decode_args(q=dev(cfg["q"]), sink_k=dev(cfg["sink_k"]), sink_v=dev(cfg["sink_v"]),
+                               recent_k=dev(cfg["recent_k"]), recent_v=dev(cfg["recent_v"]),
+                               sink_len=dev(cfg["sink_len"]), recent_len=dev(cfg["recent_len"]),
+                               hist_len=dev(cfg["hist_len"]), max_hist_len=int(cfg["hist_len"].max()),
+                               k_codes=pools[0], v_codes=pools[1], k_sz=pools[2], v_sz=pools[3],
+                               block_table=dev(cfg["block_table"]), r_k=dev(cfg["r_k"]), r_v=dev(cfg["r_v"]),
+                               out=out, workspace=ws, sm_scale=float(cfg["sm_scale"]))
+        if use_step:
+            hip.oscar_decode_step(args=args)
+        else:
+            hip.oscar_decode_attn(args=args)
+        torch.cuda.synchronize()
+        outs.append(host(out))
+    assert np.array_equal(outs[0], outs[1])
