@@ -122,7 +122,9 @@ __device__ __forceinline__ float code_scale_inv(int p) {  // 1 / (x1, x4, x16, x
   return p == 0 ? 1.0f : p == 1 ? 0.25f : 0.0625f;
 }
 
-// fp32 value of a 4-digit (base 256, balanced) integer held in one MFMA result column
+// fp32 value of a 4-digit (base 256, balanced) integer held in one MFMA result
+// column.  A PV digit sum can approach 2^25 over a wave's pages, so the digits
+// are converted one by one (x + 256y could overflow int32).
 __device__ __forceinline__ float digits_to_f32(v4i d) {
   return fmaf((float)d.w, 16777216.0f, fmaf((float)d.z, 65536.0f, fmaf((float)d.y, 256.0f, (float)d.x)));
 }
@@ -136,6 +138,21 @@ __device__ __forceinline__ void clear_in_place(v4i& a) {
     int x = a[k];
     asm volatile("v_mov_b32 %0, 0" : "+v"(x));
     a[k] = x;
+  }
+}
+
+// a value equal in every lane, moved to a scalar register
+__device__ __forceinline__ float wave_uniform(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
+// issue priority of the wave (0 lowest .. 3 highest; the level is wave-uniform)
+__device__ __forceinline__ void set_wave_priority(int level) {
+  switch (level) {
+    case 3: __builtin_amdgcn_s_setprio(3); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    default: __builtin_amdgcn_s_setprio(0); break;
   }
 }
 
@@ -180,7 +197,7 @@ struct Bf16Tile {
 
 // LDS bytes per wave for one BF16 tile: V tile, weights [64][G], reductions
 template <int D, int G>
-constexpr int bf16_lds_bytes() { return 64 * D * 2 + 64 * G * 4 + 3 * 16 * 4; }
+constexpr int bf16_lds_bytes() { return 32 * D * 2 + 64 * G * 4 + 3 * 16 * 4; }   // V staged 32 tokens at a time
 
 // q rows of the G heads as MFMA A operands (rows >= G are zero)
 template <int D, int G>
@@ -219,12 +236,10 @@ template <int D, int G>
 __device__ __forceinline__ void bf16_compute(WaveAcc<D, G>& st, const Bf16Tile<D>& t, const bf16x8* qa,
                                              float sm_log2, int nv, uint8_t* lds, int lane) {
   constexpr int CPL = D / kWave;
-  uint16_t* vt = reinterpret_cast<uint16_t*>(lds);            // [64][D]
-  float* w = reinterpret_cast<float*>(lds + 64 * D * 2);     // [64][G]
+  uint16_t* vt = reinterpret_cast<uint16_t*>(lds);            // [32][D]: one half of the V tile
+  float* w = reinterpret_cast<float*>(lds + 32 * D * 2);     // [64][G]
   float* red = w + 64 * G;                                    // [3][16]
   const int r = lane & 15, kg = lane >> 4;
-#pragma unroll
-  for (int j = 0; j < D / 8; ++j) *reinterpret_cast<uint4*>(vt + 8 * (lane + kWave * j)) = t.v[j];
 
   // QK: lane (r, kg) holds heads 4kg+i of token 16tb + r
   float lg[4][4], mloc[4];
@@ -285,25 +300,36 @@ __device__ __forceinline__ void bf16_compute(WaveAcc<D, G>& st, const Bf16Tile<D
 #pragma unroll
     for (int k = 0; k < CPL; ++k) st.a[h][k] *= alpha[h];
   }
-  // PV: lane holds channels CPL*lane .. CPL*lane + CPL-1
+  // PV: lane holds channels CPL*lane .. CPL*lane + CPL-1; V chunks j < D/16
+  // hold tokens 0..31, the rest tokens 32..63
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if (32 * half >= nv) break;
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j)
+      *reinterpret_cast<uint4*>(vt + 8 * (lane + kWave * j)) = t.v[half * (D / 16) + j];
+    __builtin_amdgcn_wave_barrier();
+    const int tend = min(nv, 32 * half + 32);
 #pragma unroll 4
-  for (int tok = 0; tok < nv; ++tok) {
-    float v[CPL];
-    if constexpr (CPL == 2) {
-      const uint32_t x = *reinterpret_cast<const uint32_t*>(vt + tok * D + 2 * lane);
-      v[0] = bf16_to_f32(x & 0xffffu);
-      v[1] = bf16_to_f32(x >> 16);
-    } else {
-      v[0] = bf16_to_f32(vt[tok * D + lane]);
-    }
+    for (int tok = 32 * half; tok < tend; ++tok) {
+      float v[CPL];
+      const uint16_t* row = vt + (tok - 32 * half) * D;
+      if constexpr (CPL == 2) {
+        const uint32_t x = *reinterpret_cast<const uint32_t*>(row + 2 * lane);
+        v[0] = bf16_to_f32(x & 0xffffu);
+        v[1] = bf16_to_f32(x >> 16);
+      } else {
+        v[0] = bf16_to_f32(row[lane]);
+      }
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float pr = w[tok * G + h];
+      for (int h = 0; h < G; ++h) {
+        const float pr = w[tok * G + h];
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) st.a[h][k] = fmaf(pr, v[k], st.a[h][k]);
+        for (int k = 0; k < CPL; ++k) st.a[h][k] = fmaf(pr, v[k], st.a[h][k]);
+      }
     }
+    __builtin_amdgcn_wave_barrier();
   }
-  __builtin_amdgcn_wave_barrier();
 }
 
 // Wave state -> this wave's slot of the block merge area [G][D+2] = (m, l, acc).
@@ -321,21 +347,38 @@ __device__ __forceinline__ void store_wave_state(const WaveAcc<D, G>& st, float*
 }
 
 // Merge the 4 wave slots of a block (after a barrier; slot v starts at
-// mrg + v*slot floats) into one partial.
-__device__ __forceinline__ void combine_block(const float* mrg, int slot, const int* flags, float* dst, int G,
-                                              int D, int tid) {
+// mrg + v*slot floats) into one partial.  kBlock/G threads serve each head, so
+// a thread computes the four weights of its head once; every LDS read is
+// issued before the first exponential.
+template <int G, int D>
+__device__ __forceinline__ void combine_block(const float* mrg, int slot, const int* flags, float* dst, int tid) {
+  constexpr int R = D + 2, TPH = kBlock / G, IT = (R + TPH - 1) / TPH;
+  const int h = tid / TPH, t = tid - h * TPH;
+  if (h >= G) return;
   const bool bad = flags[0] | flags[1] | flags[2] | flags[3];
-  for (int e = tid; e < G * (D + 2); e += kBlock) {
-    const int h = e / (D + 2), r = e % (D + 2);
-    float M = -INFINITY;
+  const float* src = mrg + h * R;
+  float m[4], x[IT][4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) M = fmaxf(M, mrg[v * slot + h * (D + 2)]);
-    float s = 0.0f;
-    if (r != 0) {
+  for (int v = 0; v < 4; ++v) m[v] = src[v * slot];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) s += exp2_or_zero(mrg[v * slot + h * (D + 2)], M) * mrg[v * slot + e];
+  for (int k = 0; k < IT; ++k) {
+    const int r = min(t + TPH * k, R - 1);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) x[k][v] = src[v * slot + r];
+  }
+  const float M = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
+  float w[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) w[v] = exp2_or_zero(m[v], M);
+#pragma unroll
+  for (int k = 0; k < IT; ++k) {
+    const int r = t + TPH * k;
+    if (r < R) {
+      float s = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) s = fmaf(w[v], x[k][v], s);
+      dst[h * R + r] = (r == 0) ? M : (r == 1 && bad) ? NAN : s;
     }
-    dst[e] = (r == 0) ? M : (r == 1 && bad) ? NAN : s;
   }
 }
 
@@ -350,28 +393,39 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p);
 }
 
-__device__ __forceinline__ void copy16_to_lds(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_base) : "memory");
+// address = scalar base + 32-bit lane offset (the global SADDR form).  No
+// instruction offset: on these copies it also moves the LDS destination.
+__device__ __forceinline__ void copy16_to_lds(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory");
 }
 
-__device__ __forceinline__ void copy4_to_lds(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_base) : "memory");
+__device__ __forceinline__ void copy4_to_lds(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base) : "memory");
 }
 
-// wait until at most n vector-memory operations of this wave are outstanding
-__device__ __forceinline__ void wait_vmem(int n) {
-  switch (n) {
-    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
-    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
-    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
-    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-    case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
-    case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
-    case 18: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+// s_waitcnt immediate for vmcnt(0) with expcnt / lgkmcnt left at their maxima
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// wait for the oldest staged page when `ahead` (wave-uniform, at most A) more
+// pages of K copies each were staged after it
+template <int K, int A>
+__device__ __forceinline__ void wait_page(int ahead) {
+  if constexpr (A == 0) {
+    wait_vmem<0>();
+  } else {
+    if (ahead >= A) {
+      wait_vmem<A * K>();
+    } else {
+      wait_page<K, A - 1>(ahead);
+    }
   }
 }
 
@@ -388,37 +442,51 @@ struct Stage {
   static constexpr int kCopies = 2 * (D / 64) + 2;   // copy instructions per page
 };
 
+// Lane byte offsets of the copies inside a (page, head) block (see Stage).
+struct StageOffsets {
+  uint32_t k, v, sz;
+};
+
 template <int D>
-__device__ __forceinline__ void stage_page(const DecodeDev& p, size_t blk, uint32_t stage_lds, int lane) {
-  using S = Stage<D>;
+__device__ __forceinline__ StageOffsets stage_offsets(int lane) {
   constexpr int NCH = D / 64, PLANE = D / 16;
   const int q = lane >> 4, n = lane & 15;
-  const uint8_t* kblk = p.k_codes + blk * (16 * D) + q * kPage * PLANE + 4 * n * PLANE;
-  const uint8_t* vblk = p.v_codes + blk * (16 * D) + NCH * n * kPage + 16 * q;
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) copy16_to_lds(kblk + 16 * c, stage_lds + S::kK + 1024 * c);
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) copy16_to_lds(vblk + kPage * c, stage_lds + S::kV + 1024 * c);
-  copy4_to_lds(p.k_sz + blk * kPage + lane, stage_lds + S::kKsz);
-  copy4_to_lds(p.v_sz + blk * kPage + lane, stage_lds + S::kVsz);
+  return StageOffsets{(uint32_t)(q * kPage * PLANE + 4 * n * PLANE), (uint32_t)(NCH * n * kPage + 16 * q),
+                      (uint32_t)(4 * lane)};
 }
 
-// Per-wave LDS: a ring of page stages, the weight-digit planes (unless they
-// reuse the consumed K codes) and the fp32 PV accumulators, which are only
-// touched when the softmax reference is raised.  Sized so two blocks of 4
-// waves fit a CU's 160 KB of LDS.
+// blk (the (page, head) block index) is wave-uniform, so the block addresses
+// stay in scalar registers; the second K / V copies of d = 128 differ only in
+// their lane offsets
+template <int D>
+__device__ __forceinline__ void stage_page(const DecodeDev& p, size_t blk, uint32_t stage_lds, StageOffsets o) {
+  using S = Stage<D>;
+  const uint8_t* kb = p.k_codes + blk * (16 * D);
+  const uint8_t* vb = p.v_codes + blk * (16 * D);
+  copy16_to_lds(kb, o.k, stage_lds + S::kK);
+  if constexpr (D == 128) copy16_to_lds(kb, o.k + 16, stage_lds + S::kK + 1024);
+  copy16_to_lds(vb, o.v, stage_lds + S::kV);
+  if constexpr (D == 128) copy16_to_lds(vb, o.v + kPage, stage_lds + S::kV + 1024);
+  copy4_to_lds(p.k_sz + blk * kPage, o.sz, stage_lds + S::kKsz);
+  copy4_to_lds(p.v_sz + blk * kPage, o.sz, stage_lds + S::kVsz);
+}
+
+// Per-wave LDS: a ring of page stages and the weight-digit planes (unless
+// they reuse the consumed K codes).  Two stages: the page being processed and
+// one page in flight.  With every wave of the chip one page ahead, about 9 MB
+// of copies are outstanding, enough to keep HBM busy; deeper rings only
+// lengthen the memory queues, and a wave then stalls issuing its copies
+// instead of computing.
 template <int D, int NB>
 struct Ring {
   static constexpr bool kPlanesInK = NB * 1024 <= 16 * D;   // planes reuse the consumed K codes
 #ifdef OSCAR_SCAN_STAGES
   static constexpr int kStages = OSCAR_SCAN_STAGES;
 #else
-  static constexpr int kStages = D == 128 ? 3 : 4;
+  static constexpr int kStages = 2;
 #endif
   static constexpr int kPlaneBytes = kPlanesInK ? 0 : NB * 1024;
-  static constexpr int kFaccOff = kStages * Stage<D>::kBytes + kPlaneBytes;
-  static constexpr int kFaccBytes = NB * 4 * (D / 64) * kWave * 4;   // [nb][u][lane] fp32
-  static constexpr int kWaveBytes = kFaccOff + kFaccBytes;
+  static constexpr int kWaveBytes = kStages * Stage<D>::kBytes + kPlaneBytes;
 };
 
 // Lane roles (lane = 16*grp + n):
@@ -430,9 +498,42 @@ struct Ring {
 //         A (weight digits) is read back from LDS planes; B lane (n, grp) holds
 //         tokens 16grp..16grp+15 of one channel of V byte column D/64*n + bs.
 //         The result lane holds the 4 digit sums of head (4nb+grp), channel D/16*n + u.
+// QK operands of a history wave: q digit A operands and the logit constants
 template <int D, int G>
-__device__ __forceinline__ void hist_wave(const DecodeDev& p, int b, int g, int pg_begin, int pg_end, int hl,
-                                          uint8_t* ring, float* mw, bool& poison, int lane) {
+struct HistOperands {
+  static constexpr int NB = (G + 3) / 4, NCH = D / 64;
+  v4i qa[NB][NCH];
+  float ca[NB], cb[NB];
+};
+
+template <int D, int G>
+__device__ __forceinline__ void load_hist_operands(const DecodeDev& p, int b, int g, int lane, HistOperands<D, G>& o) {
+  constexpr int NB = HistOperands<D, G>::NB, NCH = HistOperands<D, G>::NCH;
+  const int n = lane & 15, grp = lane >> 4;
+  const int h_base = b * p.Hq + g * G;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int hout = 4 * nb + grp;        // head whose results this lane holds
+    o.ca[nb] = hout < G ? p.qa[h_base + hout] : 0.0f;
+    o.cb[nb] = hout < G ? p.qb[h_base + hout] : 0.0f;
+    const bool row_ok = 4 * nb + (n >> 2) < G;   // head of the A row this lane supplies
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const v4i* src = reinterpret_cast<const v4i*>(p.qdig) +
+                       ((((size_t)b * p.n_kv + g) * NB + nb) * NCH + c) * kWave + lane;
+      o.qa[nb][c] = row_ok ? *src : v4i{0, 0, 0, 0};
+    }
+  }
+}
+
+// One wave's scan of history pages pg_begin .. pg_begin + count - 1.  pid_lane
+// holds the page id of page pg_begin + lane, and qo the QK operands; both were
+// loaded by the caller together with the history length, and this wave's
+// vector loads have completed.
+template <int D, int G>
+__device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begin, int count, int hl, int pid_lane,
+                                          const HistOperands<D, G>& qo, uint8_t* ring, float* mw, bool& poison,
+                                          int lane) {
   constexpr int NB = (G + 3) / 4;
   constexpr int NCH = D / 64;   // code words per token per K plane; V byte columns per lane
   constexpr int NU = 4 * NCH;   // PV result column blocks per head block
@@ -440,37 +541,19 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int b, int g, int 
   using RG = Ring<D, NB>;
   constexpr int NS = RG::kStages;
   const int n = lane & 15, grp = lane >> 4;
-  const int h_base = b * p.Hq + g * G;
-  const int count = pg_end - pg_begin;   // wave-uniform, at most kWave pages
-
-  // the wave's page ids, one per lane, read once: a vector load inside the
-  // page loop would have to wait for every page copy in flight
-  const int pid_lane = lane < count ? p.block_table[(size_t)b * p.max_pages + pg_begin + lane] : -1;
-
-  v4i qa[NB][NCH];
-  float ca[NB], cb[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int hout = 4 * nb + grp;        // head whose results this lane holds
-    ca[nb] = hout < G ? p.qa[h_base + hout] : 0.0f;
-    cb[nb] = hout < G ? p.qb[h_base + hout] : 0.0f;
-    const bool row_ok = 4 * nb + (n >> 2) < G;   // head of the A row this lane supplies
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const v4i* src = reinterpret_cast<const v4i*>(p.qdig) +
-                       ((((size_t)b * p.n_kv + g) * NB + nb) * NCH + c) * kWave + lane;
-      qa[nb][c] = row_ok ? *src : v4i{0, 0, 0, 0};
-    }
-  }
-  wait_vmem(0);   // operands and page ids loaded before the page copies start counting
+  const auto& qa = qo.qa;
+  const auto& ca = qo.ca;
+  const auto& cb = qo.cb;
   const uint64_t page_ok = __ballot(pid_lane >= 0 && (int64_t)pid_lane < p.n_pages);
 
+  // pv: integer digit sums of the PV products since the last rescale; facc:
+  // the fp32 sums folded at each rescale
   v4i pv[NB][NU];
+  float facc[NB][NU];
   // mref: reference maximum (log2 units) of each head block; logits are kept
   // relative to it.  thr: rescale when a relative logit exceeds it (-inf until
   // the first page has set the references).
   float mref[NB], lsum[NB], zsum[NB];
-  float* facc = reinterpret_cast<float*>(ring + RG::kFaccOff) + lane;   // [nb][u], stride kWave
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     mref[nb] = 0.0f;
@@ -479,32 +562,52 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int b, int g, int 
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       pv[nb][u] = v4i{0, 0, 0, 0};
-      facc[(nb * NU + u) * kWave] = 0.0f;
+      facc[nb][u] = 0.0f;
     }
   }
   float thr = -INFINITY, smax = 0.0f, sthr = 0.0f, kw = 0.0f, kw_inv = 0.0f;
 
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_offset(ring));
   uint8_t* planes = RG::kPlanesInK ? nullptr : ring + NS * S::kBytes;
-  // (page, head) block of page i of the range; an invalid page id is staged
-  // from page 0 and skipped
+  // (page, head) block of each of the wave's pages, one per lane; an invalid
+  // page id is staged from page 0 and skipped
+  const size_t blk_lane = ((page_ok >> lane) & 1) ? (size_t)pid_lane * p.n_kv + g : (size_t)g;
   auto page_blk = [&](int i) -> size_t {
-    const int pid = __builtin_amdgcn_readlane(pid_lane, i);
-    return ((page_ok >> i) & 1) ? (size_t)pid * p.n_kv + g : (size_t)g;
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)blk_lane, i);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(blk_lane >> 32), i);
+    return ((size_t)hi << 32) | lo;
   };
+  const StageOffsets soff = stage_offsets<D>(lane);
   const int pre = count < NS - 1 ? count : NS - 1;
-  for (int i = 0; i < pre; ++i) stage_page<D>(p, page_blk(i), ring_lds + i * S::kBytes, lane);
+  for (int i = 0; i < pre; ++i) stage_page<D>(p, page_blk(i), ring_lds + i * S::kBytes, soff);
+  int slot_use = 0, slot_fill = pre;   // ring slots of page i and of page i + NS - 1
+
+  // Issue priority falls with the wave's relative progress through its range
+  // (3 in the first quarter .. 0 in the last).  A SIMD otherwise issues
+  // oldest-first: the older block's waves finish early and the younger ones
+  // are left to run alone, one wave per SIMD, with their page latency
+  // exposed.  This way the waves sharing a SIMD advance and finish together.
+  int prio = 3, prio_next = (count + 3) / 4;   // page index of the next drop
+  set_wave_priority(3);
 
   for (int i = 0; i < count; ++i) {
     const int pg = pg_begin + i;
-    if (i + NS - 1 < count) stage_page<D>(p, page_blk(i + NS - 1), ring_lds + ((i + NS - 1) % NS) * S::kBytes, lane);
-    const int ahead = min(NS - 1, count - 1 - i);
-    wait_vmem(ahead * S::kCopies);
+    if (i == prio_next) {   // three times per wave
+      prio = 3 - (4 * i) / count;
+      set_wave_priority(prio);
+      prio_next = ((4 - prio) * count + 3) / 4;
+    }
+    if (i + NS - 1 < count) {
+      stage_page<D>(p, page_blk(i + NS - 1), ring_lds + slot_fill * S::kBytes, soff);
+      slot_fill = slot_fill == NS - 1 ? 0 : slot_fill + 1;
+    }
+    wait_page<S::kCopies, NS - 1>(count - 1 - i);
+    uint8_t* st = ring + slot_use * S::kBytes;
+    slot_use = slot_use == NS - 1 ? 0 : slot_use + 1;
     if (!((page_ok >> i) & 1)) {
       poison = true;
       continue;
     }
-    uint8_t* st = ring + (i % NS) * S::kBytes;
     const int nv = min(kPage, hl - pg * kPage);
     if (nv < kPage) {
       // slots past the history end hold undefined bytes: give them zero
@@ -522,16 +625,17 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int b, int g, int 
       const uint4 k4 = *reinterpret_cast<const uint4*>(st + S::kK + 1024 * c + 16 * lane);
       kword[4 * c] = k4.x; kword[4 * c + 1] = k4.y; kword[4 * c + 2] = k4.z; kword[4 * c + 3] = k4.w;
     }
+    uint4 vpre[NCH];
+#pragma unroll
+    for (int bs = 0; bs < NCH; ++bs) vpre[bs] = *reinterpret_cast<const uint4*>(st + S::kV + 1024 * bs + 16 * lane);
     const uint4 ksz = *reinterpret_cast<const uint4*>(st + S::kKsz + 16 * n);
     const uint4 vsz = *reinterpret_cast<const uint4*>(st + S::kVsz + 16 * n);
     const uint32_t kw4[4] = {ksz.x, ksz.y, ksz.z, ksz.w};
     const uint32_t vw4[4] = {vsz.x, vsz.y, vsz.z, vsz.w};
     // token 4n+tb
     float sk[4], zk[4], sv[4], zv[4];
-    bool tv[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-      tv[tb] = 4 * n + tb < nv;
       sk[tb] = f16_to_f32(kw4[tb] & 0xffffu);
       zk[tb] = f16_to_f32(kw4[tb] >> 16);
       sv[tb] = f16_to_f32(vw4[tb] & 0xffffu);
@@ -557,13 +661,22 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int b, int g, int 
         // digits: d0 + 2^8 d1 and d2 + 2^8 d3 are exact in int32
         const int lo = dq.x + dq.y * 256, hi = dq.z + dq.w * 256;
         const float dot = fmaf((float)hi, 65536.0f, (float)lo);
-        // an invalid token or head gets fma(0, dot, -inf) = -inf (dot is finite)
-        const float off = (tv[tb] & hok) ? fmaf(zk[tb], cb[nb], -mref[nb]) : -INFINITY;
+        // an invalid head gets fma(0, dot, -inf) = -inf (dot is finite)
+        const float off = hok ? fmaf(zk[tb], cb[nb], -mref[nb]) : -INFINITY;
         lg[nb][tb] = fmaf(sk[tb] * ca[nb], dot, off);
       }
+    }
+    if (nv < kPage) {   // tokens past the history end (the last page only)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+          if (4 * n + tb >= nv) lg[nb][tb] = -INFINITY;
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
       lmax[nb] = fmaxf(fmaxf(lg[nb][0], lg[nb][1]), fmaxf(lg[nb][2], lg[nb][3]));
       need |= lmax[nb] > thr;
-      __builtin_amdgcn_sched_barrier(0);   // bounds the live MFMA operands (register pressure)
     }
     need |= fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])) > sthr;
 
@@ -583,8 +696,7 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int b, int g, int 
           const float alpha = exp2f(-delta);
 #pragma unroll
           for (int u = 0; u < NU; ++u) {
-            float& f = facc[(nb * NU + u) * kWave];
-            f = (f + digits_to_f32(pv[nb][u]) * (code_scale_inv(u & 3) * kw_inv)) * alpha;
+            facc[nb][u] = (facc[nb][u] + digits_to_f32(pv[nb][u]) * (code_scale_inv(u & 3) * kw_inv)) * alpha;
             clear_in_place(pv[nb][u]);
           }
           lsum[nb] *= alpha;
@@ -595,12 +707,14 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int b, int g, int 
         for (int tb = 0; tb < 4; ++tb) lg[nb][tb] -= delta;
       }
       thr = kLazyThr;
-      smax = s_new;
-      sthr = kScaleSlack * smax;
+      // the page maximum of the V scales is the same in every lane: keep the
+      // scale state in scalar registers
+      smax = wave_uniform(s_new);
+      sthr = wave_uniform(kScaleSlack * smax);
       // weights p*scale_V*kw stay below 2^30 * kScaleSlack < 2^31
       const float denom = exp2f(kLazyThr) * (smax > 0.0f ? smax : 1.0f);
-      kw = kFix / denom;
-      kw_inv = denom / kFix;
+      kw = wave_uniform(kFix / denom);
+      kw_inv = wave_uniform(denom / kFix);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -640,7 +754,7 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int b, int g, int 
     // ---- PV
 #pragma unroll
     for (int bs = 0; bs < NCH; ++bs) {
-      const uint4 v4 = *reinterpret_cast<const uint4*>(st + S::kV + 1024 * bs + 16 * lane);
+      const uint4 v4 = vpre[bs];
       const uint32_t r[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
@@ -656,10 +770,11 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int b, int g, int 
     }
     __builtin_amdgcn_wave_barrier();
   }
-  wait_vmem(0);
+  wait_vmem<0>();
+  set_wave_priority(3);   // the block's merge waits for this wave
 
   // ---- fold, reduce over the 16 lanes of each head; each head's (m, l, acc)
-  // slot overlays the start of the ring, below the fp32 accumulators
+  // slot overlays the start of the wave's ring
   float acc[NB][NU], lz[NB][2];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -667,7 +782,7 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int b, int g, int 
     lz[nb][1] = group16_sum(zsum[nb]);
 #pragma unroll
     for (int u = 0; u < NU; ++u)
-      acc[nb][u] = facc[(nb * NU + u) * kWave] + digits_to_f32(pv[nb][u]) * (code_scale_inv(u & 3) * kw_inv);
+      acc[nb][u] = facc[nb][u] + digits_to_f32(pv[nb][u]) * (code_scale_inv(u & 3) * kw_inv);
   }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -783,7 +898,7 @@ __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) vo
   constexpr int kHistBytes = 4 * RG::kWaveBytes;
   constexpr int kBf16Bytes = 4 * bf16_lds_bytes<D, G>();
   constexpr int kSmem = kHistBytes > kBf16Bytes ? kHistBytes : kBf16Bytes;
-  static_assert(G * (D + 2) * 4 <= RG::kFaccOff, "merge slot must fit below the wave's accumulators");
+  static_assert(G * (D + 2) * 4 <= RG::kWaveBytes, "merge slot must fit in the wave's ring");
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
   __shared__ int flags[4];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -793,6 +908,7 @@ __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) vo
   bool poison = false;
 
   if (id < units * p.bf_blocks) {  // ---- BF16 sink / recent chunks (block-uniform): one chunk per wave
+    set_wave_priority(3);   // few waves, each with a whole chunk to do
     const int unit = id % units, cb = id / units;
     const int b = unit / p.n_kv, g = unit % p.n_kv;
     const int c = cb * (kBlock / kWave) + wave;
@@ -841,24 +957,35 @@ __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) vo
   const int hid = id - units * p.bf_blocks;
   const int unit = hid % units, split = hid / units;
   const int b = unit / p.n_kv, g = unit % p.n_kv;
+  const int per_wave = (p.pps + 3) / 4;   // at most 64
+  const int ws0 = split * p.pps + wave * per_wave;   // the wave's first page, before the history length clips it
+  // The page ids of the wave's whole static range, the QK operands and the
+  // history length are requested together: one memory round trip before the
+  // first page copy instead of two.  Table entries past the history end are
+  // loaded (in bounds) but never used.
+  const int pid_lane = (lane < per_wave && ws0 + lane < p.max_pages)
+                           ? p.block_table[(size_t)b * p.max_pages + ws0 + lane] : -1;
+  HistOperands<D, G> qo;
+  load_hist_operands<D, G>(p, b, g, lane, qo);
   int hl = p.hist_len[b];
+  // This wait must be visible to the compiler (builtin, not inline assembly):
+  // otherwise it still counts these loads as pending inside the page loop and
+  // inserts vmcnt waits there that also drain every page copy in flight.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   if (hl < 0 || hl > p.max_hist_len) {
     poison = true;
     hl = 0;
   }
   const int hp = (hl + kPage - 1) / kPage;
-  const int pb = split * p.pps;
-  const int pe = min(pb + p.pps, hp);
-  const int per_wave = (p.pps + 3) / 4;
-  const int wb = min(pb + wave * per_wave, pe);
-  const int we = min(wb + per_wave, pe);
+  const int pe = min(split * p.pps + p.pps, hp);
+  const int count = max(0, min(ws0 + per_wave, pe) - ws0);
   uint8_t* ring = smem + wave * RG::kWaveBytes;
   // the wave's merge slot [G][D+2] = (m, l, acc) overlays its own ring once the scan is done
-  hist_wave<D, G>(p, b, g, wb, we, hl, ring, reinterpret_cast<float*>(ring), poison, lane);
+  hist_wave<D, G>(p, g, ws0, count, hl, pid_lane, qo, ring, reinterpret_cast<float*>(ring), poison, lane);
   if (lane == 0) flags[wave] = poison ? 1 : 0;
   __syncthreads();
-  combine_block(reinterpret_cast<const float*>(smem), RG::kWaveBytes / 4, flags,
-                p.hpart + (((size_t)b * p.n_kv + g) * p.splits + split) * (size_t)G * (D + 2), G, D, tid);
+  combine_block<G, D>(reinterpret_cast<const float*>(smem), RG::kWaveBytes / 4, flags,
+                      p.hpart + (((size_t)b * p.n_kv + g) * p.splits + split) * (size_t)G * (D + 2), tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -1026,8 +1153,8 @@ __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : 2)) void bf16_paged_kernel(Bf1
   store_wave_state<D, G>(st, mrg + wave * G * (D + 2), lane, false);
   if (lane == 0) flags[wave] = poison ? 1 : 0;
   __syncthreads();
-  combine_block(mrg, G * (D + 2), flags, p.part + (((size_t)b * p.n_kv + g) * p.splits + x) * (size_t)G * (D + 2),
-                G, D, tid);
+  combine_block<G, D>(mrg, G * (D + 2), flags, p.part + (((size_t)b * p.n_kv + g) * p.splits + x) * (size_t)G * (D + 2),
+                      tid);
 }
 
 template <int D>
