@@ -73,6 +73,11 @@ constexpr int kMaxPagesPerSplit = 4 * 64;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// One head's partial softmax state in the workspace: (m, l, two pad floats,
+// acc[d]).  The pad puts acc on a 16-byte boundary for vector loads.
+constexpr int kPartAcc = 4;
+__host__ __device__ constexpr int part_row(int d) { return d + kPartAcc; }
+
 inline DecodePlan make_decode_plan(int B, int Hq, int n_kv, int d, int max_hist_len, int sink_cap,
                                    int recent_cap) {
   DecodePlan p{};
@@ -92,7 +97,7 @@ inline DecodePlan make_decode_plan(int B, int Hq, int n_kv, int d, int max_hist_
     p.pages_per_split = (int)((p.hist_pages + s0 - 1) / s0);
     p.splits = (p.hist_pages + p.pages_per_split - 1) / p.pages_per_split;
   }
-  const size_t part = (size_t)G * (d + 2) * sizeof(float);
+  const size_t part = (size_t)G * part_row(d) * sizeof(float);
   size_t off = 0;
   p.off_qdig = off;  off = align256(off + (size_t)B * n_kv * NB * (d / 64) * 64 * 16);
   p.off_qa = off;    off = align256(off + (size_t)B * Hq * sizeof(float));
@@ -121,7 +126,7 @@ inline Bf16Plan make_bf16_plan(int B, int Hq, int n_kv, int d, int max_ctx_len) 
     p.splits = (p.ctx_pages + p.pages_per_split - 1) / p.pages_per_split;
   }
   p.off_part = 0;
-  p.total = align256((size_t)B * n_kv * p.splits * G * (d + 2) * sizeof(float));
+  p.total = align256((size_t)B * n_kv * p.splits * G * part_row(d) * sizeof(float));
   return p;
 }
 

@@ -141,6 +141,13 @@ __device__ __forceinline__ void clear_in_place(v4i& a) {
   }
 }
 
+// c + f * a and f * a, per component
+__device__ __forceinline__ float4 f4_fma(float f, float4 a, float4 c) {
+  return make_float4(fmaf(f, a.x, c.x), fmaf(f, a.y, c.y), fmaf(f, a.z, c.z), fmaf(f, a.w, c.w));
+}
+
+__device__ __forceinline__ float4 f4_scale(float f, float4 a) { return make_float4(f * a.x, f * a.y, f * a.z, f * a.w); }
+
 // a value equal in every lane, moved to a scalar register
 __device__ __forceinline__ float wave_uniform(float x) {
   return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
@@ -338,11 +345,11 @@ __device__ __forceinline__ void store_wave_state(const WaveAcc<D, G>& st, float*
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     if (lane == 0) {
-      mw[h * (D + 2)] = st.m[h];
-      mw[h * (D + 2) + 1] = poison ? NAN : st.l[h];
+      mw[h * part_row(D)] = st.m[h];
+      mw[h * part_row(D) + 1] = poison ? NAN : st.l[h];
     }
 #pragma unroll
-    for (int k = 0; k < D / kWave; ++k) mw[h * (D + 2) + 2 + (D / kWave) * lane + k] = st.a[h][k];
+    for (int k = 0; k < D / kWave; ++k) mw[h * part_row(D) + kPartAcc + (D / kWave) * lane + k] = st.a[h][k];
   }
 }
 
@@ -352,7 +359,7 @@ __device__ __forceinline__ void store_wave_state(const WaveAcc<D, G>& st, float*
 // issued before the first exponential.
 template <int G, int D>
 __device__ __forceinline__ void combine_block(const float* mrg, int slot, const int* flags, float* dst, int tid) {
-  constexpr int R = D + 2, TPH = kBlock / G, IT = (R + TPH - 1) / TPH;
+  constexpr int R = part_row(D), TPH = kBlock / G, IT = (R + TPH - 1) / TPH;
   const int h = tid / TPH, t = tid - h * TPH;
   if (h >= G) return;
   const bool bad = flags[0] | flags[1] | flags[2] | flags[3];
@@ -377,7 +384,7 @@ __device__ __forceinline__ void combine_block(const float* mrg, int slot, const 
       float s = 0.0f;
 #pragma unroll
       for (int v = 0; v < 4; ++v) s = fmaf(w[v], x[k][v], s);
-      dst[h * R + r] = (r == 0) ? M : (r == 1 && bad) ? NAN : s;
+      dst[h * R + r] = (r == 0) ? M : (r == 1) ? (bad ? NAN : s) : (r < kPartAcc) ? 0.0f : s;
     }
   }
 }
@@ -788,13 +795,13 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
   for (int nb = 0; nb < NB; ++nb) {
     const int h = 4 * nb + grp;
     if (h < G) {
-      float* mh = mw + h * (D + 2);
+      float* mh = mw + h * part_row(D);
       if (n == 0) {
         mh[0] = kw_inv > 0.0f ? mref[nb] : -INFINITY;   // no page processed: empty partial
         mh[1] = lz[nb][0];
       }
 #pragma unroll
-      for (int u = 0; u < NU; ++u) mh[2 + NU * n + u] = acc[nb][u] + lz[nb][1];
+      for (int u = 0; u < NU; ++u) mh[kPartAcc + NU * n + u] = acc[nb][u] + lz[nb][1];
     }
   }
 }
@@ -805,24 +812,26 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
 template <int D>
 __device__ __forceinline__ void rotate_query_block(const DecodeDev& p, int bh) {
   constexpr int NCH = D / 64, PLANE = D / 16;
-  constexpr int P = kBlock / D, IP = D / P;   // row parts of each dot product; every load in flight at once
+  // thread (jq, part): columns 4jq..4jq+3 of rows part*IP .. part*IP+IP-1,
+  // loaded as IP 16-byte vectors all in flight at once
+  constexpr int QPR = D / 4, P = kBlock / QPR, IP = D / P;
   __shared__ float qs[D];
-  __shared__ float part_s[P][D];
+  __shared__ __attribute__((aligned(16))) float part_s[P][D];
   __shared__ float red[2][kBlock / kWave];
   const int b = bh / p.Hq, h = bh % p.Hq, g = h / p.G, hl = h % p.G;
-  const int tid = threadIdx.x, j = tid % D, part = tid / D;
-  const float* R = p.r_k + (size_t)g * D * D + (size_t)part * IP * D + j;
-  float r[IP];
+  const int tid = threadIdx.x, jq = tid % QPR, part = tid / QPR;
+  const float4* R = reinterpret_cast<const float4*>(p.r_k + (size_t)g * D * D + (size_t)part * IP * D) + jq;
+  float4 r[IP];
 #pragma unroll
-  for (int k = 0; k < IP; ++k) r[k] = R[(size_t)k * D];
+  for (int k = 0; k < IP; ++k) r[k] = R[(size_t)k * QPR];
   if (tid < D) qs[tid] = bf16_to_f32(p.q[(size_t)bh * D + tid]);
   __syncthreads();
-  float acc = 0.0f;
+  float4 a4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
-  for (int k = 0; k < IP; ++k) acc = fmaf(qs[part * IP + k], r[k], acc);
-  part_s[part][j] = acc;
+  for (int k = 0; k < IP; ++k) a4 = f4_fma(qs[part * IP + k], r[k], a4);
+  reinterpret_cast<float4*>(part_s[part])[jq] = a4;
   __syncthreads();
-  acc = 0.0f;
+  float acc = 0.0f;
   if (tid < D) {
 #pragma unroll
     for (int q = 0; q < P; ++q) acc += part_s[q][tid];
@@ -898,7 +907,7 @@ __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) vo
   constexpr int kHistBytes = 4 * RG::kWaveBytes;
   constexpr int kBf16Bytes = 4 * bf16_lds_bytes<D, G>();
   constexpr int kSmem = kHistBytes > kBf16Bytes ? kHistBytes : kBf16Bytes;
-  static_assert(G * (D + 2) * 4 <= RG::kWaveBytes, "merge slot must fit in the wave's ring");
+  static_assert(G * part_row(D) * 4 <= RG::kWaveBytes, "merge slot must fit in the wave's ring");
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
   __shared__ int flags[4];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -947,7 +956,7 @@ __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) vo
         bf16_load<D>(tile, kb, vb, nv, lane);
         bf16_compute<D, G>(st, tile, qa, p.sm_log2, nv, smem + wave * bf16_lds_bytes<D, G>(), lane);
       }
-      store_wave_state<D, G>(st, p.bpart + (((size_t)b * p.n_kv + g) * p.chunks + c) * (size_t)G * (D + 2), lane,
+      store_wave_state<D, G>(st, p.bpart + (((size_t)b * p.n_kv + g) * p.chunks + c) * (size_t)G * part_row(D), lane,
                              poison);
     }
     return;
@@ -985,88 +994,95 @@ __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) vo
   if (lane == 0) flags[wave] = poison ? 1 : 0;
   __syncthreads();
   combine_block<G, D>(reinterpret_cast<const float*>(smem), RG::kWaveBytes / 4, flags,
-                      p.hpart + (((size_t)b * p.n_kv + g) * p.splits + split) * (size_t)G * (D + 2), tid);
+                      p.hpart + (((size_t)b * p.n_kv + g) * p.splits + split) * (size_t)G * part_row(D), tid);
 }
 
 // ---------------------------------------------------------------------------
 // 3. merge: LSE over history splits, * R_V^T, LSE with BF16 chunks, normalise
 // ---------------------------------------------------------------------------
-// Online LSE merge of partials (m, l, acc[D]) by one 256-thread block.
-// Thread (c, part) owns channel c of the partials s = part (mod TPC): it loads
-// up to kMergeRound of them at once (m, l and its channel), folds them into a
-// running (m, l, acc) and moves to the next round; the TPC parts are then
-// combined through LDS.  acc is split in two sums: partials s < n_rot (history,
-// still rotated) and the rest.
-constexpr int kMergeRound = 40;
+// Online LSE merge of one head's partials (m, l, acc[D]) by a 256-thread
+// block.  Thread (q, grp) owns channels 4q..4q+3 of the partials s = grp,
+// grp + NG, ... (NG = kBlock / (D/4) groups): it issues the loads of up to
+// kMergeRound of them (a float2 (m, l) and a float4 of acc each) before the
+// first use, folds them into a running (m, l, acc) and moves to the next round;
+// the NG group states are then combined through LDS.  acc is split in two
+// sums: partials s < n_rot (history, still rotated) and the rest.
+constexpr int kMergeRound = 12;
 
-struct MergeState {
-  float m, l, a_rot, a_plain;
+template <int D>
+struct MergeShared {
+  static constexpr int NQ = D / 4, NG = kBlock / NQ;
+  float m[NG], l[NG];
+  float4 a_rot[NG][NQ], a_plain[NG][NQ];
+  float rot[D], plain[D];   // combined channel sums
 };
 
+// part_ptr(s): the head's row of partial s (16-byte aligned).  Returns the
+// block-wide (M, L) and leaves the channel sums in sh.rot / sh.plain.
 template <int D, typename PartPtr>
-__device__ __forceinline__ MergeState merge_partials(PartPtr part_ptr, int n_rot, int nt, int c, int part) {
-  constexpr int TPC = kBlock / D;
-  MergeState st{-INFINITY, 0.0f, 0.0f, 0.0f};
-  for (int s0 = part; s0 < nt; s0 += TPC * kMergeRound) {
-    float mv[kMergeRound], lv[kMergeRound], av[kMergeRound];
+__device__ __forceinline__ float2 merge_head(PartPtr part_ptr, int n_rot, int nt, MergeShared<D>& sh, int tid) {
+  constexpr int NQ = MergeShared<D>::NQ, NG = MergeShared<D>::NG;
+  const int q = tid % NQ, grp = tid / NQ;
+  float m = -INFINITY, l = 0.0f;
+  float4 ar = make_float4(0.0f, 0.0f, 0.0f, 0.0f), ap = ar;
+  for (int s0 = grp; s0 < nt; s0 += NG * kMergeRound) {
+    float2 ml[kMergeRound];
+    float4 av[kMergeRound];
 #pragma unroll
     for (int k = 0; k < kMergeRound; ++k) {
-      const int s = s0 + TPC * k;
-      const float* pp = part_ptr(s < nt ? s : s0);
-      mv[k] = s < nt ? pp[0] : -INFINITY;
-      lv[k] = s < nt ? pp[1] : 0.0f;
-      av[k] = s < nt ? pp[2 + c] : 0.0f;
+      const int s = s0 + NG * k;
+      if (s < nt) {
+        const float* pp = part_ptr(s);
+        ml[k] = *reinterpret_cast<const float2*>(pp);
+        av[k] = *reinterpret_cast<const float4*>(pp + kPartAcc + 4 * q);
+      } else {
+        ml[k] = make_float2(-INFINITY, 0.0f);
+        av[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      }
     }
-    float rm = st.m;
+    float rm = m;
 #pragma unroll
-    for (int k = 0; k < kMergeRound; ++k) rm = fmaxf(rm, mv[k]);
-    const float alpha = exp2_or_zero(st.m, rm);
-    st.l *= alpha;
-    st.a_rot *= alpha;
-    st.a_plain *= alpha;
+    for (int k = 0; k < kMergeRound; ++k) rm = fmaxf(rm, ml[k].x);
+    const float alpha = exp2_or_zero(m, rm);
+    l *= alpha;
+    ar = f4_scale(alpha, ar);
+    ap = f4_scale(alpha, ap);
 #pragma unroll
     for (int k = 0; k < kMergeRound; ++k) {
-      const int s = s0 + TPC * k;
-      const float f = exp2_or_zero(mv[k], rm);
-      st.l = fmaf(f, lv[k], st.l);
-      if (s < n_rot) st.a_rot = fmaf(f, av[k], st.a_rot);
-      else st.a_plain = fmaf(f, av[k], st.a_plain);
+      const float f = exp2_or_zero(ml[k].x, rm);
+      const float fr = s0 + NG * k < n_rot ? f : 0.0f;
+      l = fmaf(f, ml[k].y, l);
+      ar = f4_fma(fr, av[k], ar);
+      ap = f4_fma(f - fr, av[k], ap);
     }
-    st.m = rm;
+    m = rm;
   }
-  return st;
-}
-
-// Combine the TPC parts' states through LDS; returns the block-wide
-// (M, L) and leaves the combined channel sums in a_rot_s[c], a_plain_s[c].
-template <int D>
-__device__ __forceinline__ float2 combine_parts(const MergeState& st, float* m_s, float* l_s, float* a_rot_s,
-                                                float* a_plain_s, int c, int part) {
-  constexpr int TPC = kBlock / D;
-  if (c == 0) {
-    m_s[part] = st.m;
-    l_s[part] = st.l;
+  if (q == 0) {
+    sh.m[grp] = m;
+    sh.l[grp] = l;
   }
   __syncthreads();
   float M = -INFINITY;
 #pragma unroll
-  for (int q = 0; q < TPC; ++q) M = fmaxf(M, m_s[q]);
+  for (int k = 0; k < NG; ++k) M = fmaxf(M, sh.m[k]);
   float L = 0.0f;
 #pragma unroll
-  for (int q = 0; q < TPC; ++q) L = fmaf(exp2_or_zero(m_s[q], M), l_s[q], L);
-  const float f = exp2_or_zero(st.m, M);
-  a_rot_s[part * D + c] = f * st.a_rot;
-  a_plain_s[part * D + c] = f * st.a_plain;
+  for (int k = 0; k < NG; ++k) L = fmaf(exp2_or_zero(sh.m[k], M), sh.l[k], L);
+  const float f = exp2_or_zero(m, M);
+  sh.a_rot[grp][q] = f4_scale(f, ar);
+  sh.a_plain[grp][q] = f4_scale(f, ap);
   __syncthreads();
-  if (part == 0) {
-    float ar = 0.0f, ap = 0.0f;
+  if (tid < D) {
+    const float* r0 = reinterpret_cast<const float*>(&sh.a_rot[0][0]);
+    const float* p0 = reinterpret_cast<const float*>(&sh.a_plain[0][0]);
+    float sr = 0.0f, sp = 0.0f;
 #pragma unroll
-    for (int q = 0; q < TPC; ++q) {
-      ar += a_rot_s[q * D + c];
-      ap += a_plain_s[q * D + c];
+    for (int k = 0; k < NG; ++k) {
+      sr += r0[k * D + tid];
+      sp += p0[k * D + tid];
     }
-    a_rot_s[c] = ar;
-    a_plain_s[c] = ap;
+    sh.rot[tid] = sr;
+    sh.plain[tid] = sp;
   }
   __syncthreads();
   return make_float2(M, L);
@@ -1075,41 +1091,45 @@ __device__ __forceinline__ float2 combine_parts(const MergeState& st, float* m_s
 // One query head per block:
 //   out = (sum_hist f_s acc_s R_V^T + sum_bf16 f_s acc_s) / sum_all f_s l_s,
 //   f_s = exp2(m_s - M) with M the maximum over every partial.
+// The R_V row segments are requested first, so their loads overlap the
+// partials'.
 template <int D>
 __global__ __launch_bounds__(kBlock) void merge_kernel(DecodeDev p) {
-  constexpr int TPC = kBlock / D;   // threads per channel
-  constexpr int SEG = D / TPC;      // R_V row segment per thread
-  __shared__ float m_s[TPC], l_s[TPC];
-  __shared__ float a_rot_s[kBlock], a_plain_s[kBlock];
+  constexpr int TPO = kBlock / D;   // threads per output channel
+  constexpr int SEG = D / TPO;      // R_V row segment per thread
+  __shared__ MergeShared<D> sh;
   const int bh = blockIdx.x;
   const int b = bh / p.Hq, h = bh % p.Hq, g = h / p.G, kh = h % p.G;
-  const int tid = threadIdx.x, c = tid % D, part = tid / D;
-  const size_t stride = (size_t)p.G * (D + 2);
-  const float* hp = p.hpart + ((size_t)b * p.n_kv + g) * p.splits * stride + (size_t)kh * (D + 2);
-  const float* bp = p.bpart + ((size_t)b * p.n_kv + g) * p.chunks * stride + (size_t)kh * (D + 2);
+  const int tid = threadIdx.x;
+  const size_t stride = (size_t)p.G * part_row(D);
+  const float* hp = p.hpart + ((size_t)b * p.n_kv + g) * p.splits * stride + (size_t)kh * part_row(D);
+  const float* bp = p.bpart + ((size_t)b * p.n_kv + g) * p.chunks * stride + (size_t)kh * part_row(D);
   const int n = p.splits, nt = p.splits + p.chunks;
-  // this thread's segment of output row i = tid / TPC of the R_V product
-  const int i = tid / TPC, seg = tid % TPC;
-  float rv[SEG];
+  // this thread's segment of output row i of the R_V product
+  const int i = tid / TPO, seg = tid % TPO;
+  float4 rv[SEG / 4];
   {
-    const float* Rrow = p.r_v + ((size_t)g * D + i) * D + seg * SEG;
+    const float4* Rrow = reinterpret_cast<const float4*>(p.r_v + ((size_t)g * D + i) * D + seg * SEG);
 #pragma unroll
-    for (int k = 0; k < SEG; ++k) rv[k] = Rrow[k];
+    for (int k = 0; k < SEG / 4; ++k) rv[k] = Rrow[k];
   }
-  const MergeState st = merge_partials<D>(
-      [&](int s) { return s < n ? hp + (size_t)s * stride : bp + (size_t)(s - n) * stride; }, n, nt, c, part);
-  const float2 ML = combine_parts<D>(st, m_s, l_s, a_rot_s, a_plain_s, c, part);
+  const float2 ML = merge_head<D>(
+      [&](int s) { return s < n ? hp + (size_t)s * stride : bp + (size_t)(s - n) * stride; }, n, nt, sh, tid);
   // out_hist[i] = sum_j A_hist[j] R_V[g][i][j]
   float o = 0.0f;
+  const float4* a4 = reinterpret_cast<const float4*>(sh.rot + seg * SEG);
 #pragma unroll
-  for (int k = 0; k < SEG; ++k) o = fmaf(a_rot_s[seg * SEG + k], rv[k], o);
+  for (int k = 0; k < SEG / 4; ++k) {
+    const float4 a = a4[k];
+    o = fmaf(a.x, rv[k].x, fmaf(a.y, rv[k].y, fmaf(a.z, rv[k].z, fmaf(a.w, rv[k].w, o))));
+  }
 #pragma unroll
-  for (int off = 1; off < TPC; off <<= 1) o += __shfl_xor(o, off, kWave);
+  for (int off = 1; off < TPO; off <<= 1) o += __shfl_xor(o, off, kWave);
   if (seg == 0) {
     const float L = ML.y;
     float out;
     if (isnan(L)) out = NAN;
-    else out = (L > 0.0f) ? (o + a_plain_s[i]) / L : 0.0f;
+    else out = (L > 0.0f) ? (o + sh.plain[i]) / L : 0.0f;
     p.out[(size_t)bh * D + i] = out;
   }
 }
@@ -1118,7 +1138,7 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(DecodeDev p) {
 template <int D, int G>
 __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : 2)) void bf16_paged_kernel(Bf16Dev p) {
   constexpr int kWaveLds = bf16_lds_bytes<D, G>();
-  constexpr int kMrg = 4 * G * (D + 2) * 4;
+  constexpr int kMrg = 4 * G * part_row(D) * 4;
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kWaveLds > kMrg ? 4 * kWaveLds : kMrg];
   __shared__ int flags[4];
   const int b = blockIdx.z, g = blockIdx.y, x = blockIdx.x;
@@ -1150,30 +1170,28 @@ __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : 2)) void bf16_paged_kernel(Bf1
   }
   __syncthreads();   // the merge area overlays the tiles' LDS
   float* mrg = reinterpret_cast<float*>(smem);
-  store_wave_state<D, G>(st, mrg + wave * G * (D + 2), lane, false);
+  store_wave_state<D, G>(st, mrg + wave * G * part_row(D), lane, false);
   if (lane == 0) flags[wave] = poison ? 1 : 0;
   __syncthreads();
-  combine_block<G, D>(mrg, G * (D + 2), flags, p.part + (((size_t)b * p.n_kv + g) * p.splits + x) * (size_t)G * (D + 2),
+  combine_block<G, D>(mrg, G * part_row(D), flags, p.part + (((size_t)b * p.n_kv + g) * p.splits + x) * (size_t)G * part_row(D),
                       tid);
 }
 
 template <int D>
 __global__ __launch_bounds__(kBlock) void merge_plain_kernel(Bf16Dev p) {
-  __shared__ float m_s[kBlock / D], l_s[kBlock / D];
-  __shared__ float a_rot_s[kBlock], a_plain_s[kBlock];
+  __shared__ MergeShared<D> sh;
   const int bh = blockIdx.x;
   const int b = bh / p.Hq, h = bh % p.Hq, g = h / p.G, kh = h % p.G;
-  const int tid = threadIdx.x, c = tid % D, part = tid / D;
-  const size_t stride = (size_t)p.G * (D + 2);
-  const float* pp = p.part + ((size_t)b * p.n_kv + g) * p.splits * stride + (size_t)kh * (D + 2);
-  const MergeState st = merge_partials<D>([&](int s) { return pp + (size_t)s * stride; }, 0, p.splits, c, part);
-  const float2 ML = combine_parts<D>(st, m_s, l_s, a_rot_s, a_plain_s, c, part);
-  if (part == 0) {
+  const int tid = threadIdx.x;
+  const size_t stride = (size_t)p.G * part_row(D);
+  const float* pp = p.part + ((size_t)b * p.n_kv + g) * p.splits * stride + (size_t)kh * part_row(D);
+  const float2 ML = merge_head<D>([&](int s) { return pp + (size_t)s * stride; }, 0, p.splits, sh, tid);
+  if (tid < D) {
     const float L = ML.y;
     float o;
     if (isnan(L)) o = NAN;
-    else o = (L > 0.0f) ? a_plain_s[c] / L : 0.0f;
-    p.out[(size_t)bh * D + c] = o;
+    else o = (L > 0.0f) ? sh.plain[tid] / L : 0.0f;
+    p.out[(size_t)bh * D + tid] = o;
   }
 }
 

@@ -12,9 +12,9 @@
 
 namespace oscar {
 
-// Thread (j, part) loads its D/P entries of column j of R at once, so the
-// block waits for one round of loads, and computes a partial fp64 dot; the P
-// partials are added in fp64 and rounded once to fp32.
+// Thread (jq, part) loads its IP rows of columns 4jq..4jq+3 of R as 16-byte
+// vectors, all in flight at once, and computes four partial fp64 dots; the P
+// partials of a column are added in fp64 and rounded once to fp32.
 template <int D>
 __device__ __forceinline__ void demote_token_block(int kind, const uint16_t* __restrict__ x, int64_t n_src,
                                                    int64_t tok_stride, int64_t head_stride,
@@ -22,7 +22,8 @@ __device__ __forceinline__ void demote_token_block(int kind, const uint16_t* __r
                                                    const float* __restrict__ rot, float clip,
                                                    const int32_t* __restrict__ dst_slot, uint8_t* __restrict__ codes,
                                                    uint32_t* __restrict__ sz, int64_t n_pages) {
-  constexpr int P = kBlock / D;          // row parts of the dot product
+  constexpr int QPR = D / 4;             // column quads per row
+  constexpr int P = kBlock / QPR;        // row parts of the dot product
   constexpr int IP = D / P;              // rows per part
   constexpr int kRowBytes = D / 4;
   constexpr int kPlane = D / 16;
@@ -35,17 +36,26 @@ __device__ __forceinline__ void demote_token_block(int kind, const uint16_t* __r
   const int64_t slot = dst_slot[t];
   if (src < 0 || src >= n_src || slot < 0 || slot >= n_pages * kPage) return;   // block-uniform
 
-  const int j = tid % D, part = tid / D;
-  const float* R = rot + (size_t)g * D * D + (size_t)part * IP * D + j;
-  float r[IP];
+  const int jq = tid % QPR, part = tid / QPR;
+  const float4* R = reinterpret_cast<const float4*>(rot + (size_t)g * D * D + (size_t)part * IP * D) + jq;
+  float4 r[IP];
 #pragma unroll
-  for (int k = 0; k < IP; ++k) r[k] = R[(size_t)k * D];
+  for (int k = 0; k < IP; ++k) r[k] = R[(size_t)k * QPR];
   if (tid < D) xs[tid] = bf16_to_f32(x[src * tok_stride + (int64_t)g * head_stride + tid]);
   __syncthreads();
-  double acc = 0.0;
+  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
 #pragma unroll
-  for (int k = 0; k < IP; ++k) acc = fma((double)xs[part * IP + k], (double)r[k], acc);
-  parts[part][j] = acc;
+  for (int k = 0; k < IP; ++k) {
+    const double xv = (double)xs[part * IP + k];
+    a0 = fma(xv, (double)r[k].x, a0);
+    a1 = fma(xv, (double)r[k].y, a1);
+    a2 = fma(xv, (double)r[k].z, a2);
+    a3 = fma(xv, (double)r[k].w, a3);
+  }
+  parts[part][4 * jq] = a0;
+  parts[part][4 * jq + 1] = a1;
+  parts[part][4 * jq + 2] = a2;
+  parts[part][4 * jq + 3] = a3;
   __syncthreads();
 
   float mn = INFINITY, mx = -INFINITY;
