@@ -88,7 +88,7 @@ inline DecodePlan make_decode_plan(int B, int Hq, int n_kv, int d, int max_hist_
   p.chunks = p.sink_chunks + (recent_cap + kPage - 1) / kPage;
   if (p.hist_pages > 0) {
     const long units = (long)(B > 0 ? B : 1) * n_kv;
-    long target = kResidentBlocks - units * ((p.chunks + 3) / 4);   // blocks left for history
+    long target = kResidentBlocks - units * p.chunks;   // blocks left for history (one BF16 block per chunk)
     if (target < units) target = units;
     long s0 = (target + units - 1) / units;
     const long s_min = (p.hist_pages + kMaxPagesPerSplit - 1) / kMaxPagesPerSplit;

@@ -18,15 +18,19 @@
 // (no conversion), the rotated query and the softmax weights become 30-bit
 // fixed-point integers split into four balanced 8-bit digits, one MFMA row per
 // (head, digit), so 4 heads fill the 16 rows.  Products and sums are exact;
-// the only roundings are the fixed-point conversions (relative 2^-24) and the
+// the only roundings are the fixed-point conversions (a query element to
+// 2^-26 of the largest, a weight to 2^-18 of the reference weight) and the
 // fp32 combination of the digit results.  PV accumulates in int32 across a
-// split's pages; the softmax reference maximum is only raised when a logit
-// exceeds it by 2^8 (then the integer accumulator is folded into fp32).
+// wave's pages; the softmax reference maximum is only raised when a logit
+// exceeds it by 2^12 (then the integer accumulator is folded into fp32).
 //
 // Launches (all on the caller's stream):
-//   1. rotate_query_kernel  q_rot = q R_K[g] per query head -> MFMA digit operands
-//   2. decode_main_kernel   one grid: BF16 sink/recent chunks (first) and INT2
-//                           history splits; each writes an (m, l, acc) partial
+//   1. prepare_kernel       q_rot = q R_K[g] per query head -> MFMA digit
+//                           operands; in a decode step also the step's K / V
+//                           demotions
+//   2. decode_main_kernel   one grid: INT2 history splits, then the BF16
+//                           sink / recent chunks; each block writes an
+//                           (m, l, acc) partial per head
 //   3. merge_kernel         LSE merge of the history partials, * R_V^T, LSE merge
 //                           with the BF16 partials, normalise
 // Softmax state uses base-2 exponents (logits pre-scaled by log2 e).
@@ -41,13 +45,18 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 constexpr uint32_t kMask0 = 0x03030303u;  // code field 0 of each byte (x1)
 constexpr uint32_t kMask1 = 0x0C0C0C0Cu;  // field 1 (x4)
 constexpr uint32_t kMask2 = 0x30303030u;  // field 2 (x16); field 3 is shifted into it
-constexpr float kLazyThr = 8.0f;          // raise the reference max only past +2^8
+// Raise the reference maximum only when a logit passes it by 2^kLazyThr.
+// Weights stay below 1.75 * 2^30 for any threshold (kw scales with it); 12
+// keeps a reference weight at 2^18 fixed-point units and leaves about one
+// page in forty to the fold path on the long-context workloads.
+constexpr float kLazyThr = 12.0f;
 constexpr float kScaleSlack = 1.75f;      // refold when a V scale exceeds 1.75x the running max
 constexpr float kFix = 1073741824.0f;     // 2^30: fixed-point range of digits
+constexpr int kBf16WaveTokens = 16;       // tokens of a BF16 chunk per wave (4 waves per chunk)
 
 struct DecodeDev {
   int B, Hq, n_kv, G, NB, sink_cap, recent_cap, max_hist_len, max_pages;
-  int splits, pps, chunks, sink_chunks, bf_blocks;
+  int splits, pps, chunks, sink_chunks, bf_blocks;   // bf_blocks: BF16 blocks per unit (one per chunk)
   float sm_log2;
   int64_t n_pages;
   const uint16_t *q, *sink_k, *sink_v, *recent_k, *recent_v;
@@ -907,6 +916,7 @@ __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) vo
   constexpr int kHistBytes = 4 * RG::kWaveBytes;
   constexpr int kBf16Bytes = 4 * bf16_lds_bytes<D, G>();
   constexpr int kSmem = kHistBytes > kBf16Bytes ? kHistBytes : kBf16Bytes;
+  static_assert(4 * G * part_row(D) * 4 <= kSmem, "BF16 merge slots must fit");
   static_assert(G * part_row(D) * 4 <= RG::kWaveBytes, "merge slot must fit in the wave's ring");
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
   __shared__ int flags[4];
@@ -916,54 +926,59 @@ __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) vo
   const int id = blockIdx.x;
   bool poison = false;
 
-  if (id < units * p.bf_blocks) {  // ---- BF16 sink / recent chunks (block-uniform): one chunk per wave
-    set_wave_priority(3);   // few waves, each with a whole chunk to do
-    const int unit = id % units, cb = id / units;
+  if (id >= units * p.splits) {
+    // ---- BF16 sink / recent chunk (block-uniform), after every history block:
+    // one chunk per block, 16 tokens per wave.  Spread this thin, a block's
+    // loads stay small next to the history block that shares its CU.
+    const int cid = id - units * p.splits;
+    const int unit = cid % units, c = cid / units;
     const int b = unit / p.n_kv, g = unit % p.n_kv;
-    const int c = cb * (kBlock / kWave) + wave;
-    if (c < p.chunks) {
-      WaveAcc<D, G> st;
-      acc_init(st);
-      const uint16_t *kb, *vb;
-      int nv;
-      if (c < p.sink_chunks) {
-        int sl = p.sink_len[b];
-        if (sl < 0 || sl > p.sink_cap) {
-          poison = true;
-          sl = 0;
-        }
-        const int t0 = c * kPage;
-        nv = min(kPage, sl - t0);
-        const size_t off = (((size_t)b * p.n_kv + g) * p.sink_cap + t0) * D;
-        kb = p.sink_k + off;
-        vb = p.sink_v + off;
-      } else {
-        int rl = p.recent_len[b];
-        if (rl < 0 || rl > p.recent_cap) {
-          poison = true;
-          rl = 0;
-        }
-        const int t0 = (c - p.sink_chunks) * kPage;
-        nv = min(kPage, rl - t0);
-        const size_t off = (((size_t)b * p.n_kv + g) * p.recent_cap + t0) * D;
-        kb = p.recent_k + off;
-        vb = p.recent_v + off;
+    WaveAcc<D, G> st;
+    acc_init(st);
+    const uint16_t *kb, *vb;
+    int nv;
+    if (c < p.sink_chunks) {
+      int sl = p.sink_len[b];
+      if (sl < 0 || sl > p.sink_cap) {
+        poison = true;
+        sl = 0;
       }
-      if (nv > 0) {
-        bf16x8 qa[D / 32];
-        bf16_q_operands<D, G>(qa, p.q + ((size_t)b * p.Hq + g * G) * D, lane);
-        Bf16Tile<D> tile;
-        bf16_load<D>(tile, kb, vb, nv, lane);
-        bf16_compute<D, G>(st, tile, qa, p.sm_log2, nv, smem + wave * bf16_lds_bytes<D, G>(), lane);
+      const int t0 = c * kPage + kBf16WaveTokens * wave;
+      nv = min(kBf16WaveTokens, sl - t0);
+      const size_t off = (((size_t)b * p.n_kv + g) * p.sink_cap + t0) * D;
+      kb = p.sink_k + off;
+      vb = p.sink_v + off;
+    } else {
+      int rl = p.recent_len[b];
+      if (rl < 0 || rl > p.recent_cap) {
+        poison = true;
+        rl = 0;
       }
-      store_wave_state<D, G>(st, p.bpart + (((size_t)b * p.n_kv + g) * p.chunks + c) * (size_t)G * part_row(D), lane,
-                             poison);
+      const int t0 = (c - p.sink_chunks) * kPage + kBf16WaveTokens * wave;
+      nv = min(kBf16WaveTokens, rl - t0);
+      const size_t off = (((size_t)b * p.n_kv + g) * p.recent_cap + t0) * D;
+      kb = p.recent_k + off;
+      vb = p.recent_v + off;
     }
+    if (nv > 0) {
+      bf16x8 qa[D / 32];
+      bf16_q_operands<D, G>(qa, p.q + ((size_t)b * p.Hq + g * G) * D, lane);
+      Bf16Tile<D> tile;
+      bf16_load<D>(tile, kb, vb, nv, lane);
+      bf16_compute<D, G>(st, tile, qa, p.sm_log2, nv, smem + wave * bf16_lds_bytes<D, G>(), lane);
+    }
+    __syncthreads();   // the merge slots overlay the tiles' LDS
+    float* mrg = reinterpret_cast<float*>(smem);
+    store_wave_state<D, G>(st, mrg + wave * G * part_row(D), lane, false);
+    if (lane == 0) flags[wave] = poison ? 1 : 0;
+    __syncthreads();
+    combine_block<G, D>(mrg, G * part_row(D), flags,
+                        p.bpart + (((size_t)b * p.n_kv + g) * p.chunks + c) * (size_t)G * part_row(D), tid);
     return;
   }
 
   // ---- INT2 history split: waves take contiguous page ranges
-  const int hid = id - units * p.bf_blocks;
+  const int hid = id;
   const int unit = hid % units, split = hid / units;
   const int b = unit / p.n_kv, g = unit % p.n_kv;
   const int per_wave = (p.pps + 3) / 4;   // at most 64
@@ -1238,7 +1253,7 @@ DecodeDev make_dev(const oscar_decode_args& a, const DecodePlan& plan, char* ws)
   dv.max_hist_len = a.max_hist_len; dv.max_pages = a.max_pages;
   dv.splits = plan.splits; dv.pps = plan.pages_per_split;
   dv.chunks = plan.chunks; dv.sink_chunks = plan.sink_chunks;
-  dv.bf_blocks = (plan.chunks + 3) / 4;
+  dv.bf_blocks = plan.chunks;
   dv.sm_log2 = a.sm_scale * kLog2e;
   dv.n_pages = a.n_pages;
   dv.q = a.q; dv.sink_k = a.sink_k; dv.sink_v = a.sink_v; dv.recent_k = a.recent_k; dv.recent_v = a.recent_v;
