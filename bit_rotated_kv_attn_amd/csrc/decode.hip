@@ -110,16 +110,27 @@ struct Bf16Dev {
   float *out, *part;
 };
 
+// Reductions over the 16 lanes of a DPP row (lanes 16k..16k+15), every lane
+// receiving the result: quad permutes (lane ^ 1, lane ^ 2), then the half-row
+// and row mirrors.  VALU data movement, no LDS round trips.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
 __device__ __forceinline__ float group16_max(float v) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = fmaxf(v, dpp_f32<kDppXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  return fmaxf(v, dpp_f32<kDppMirror>(v));
 }
 
 __device__ __forceinline__ float group16_sum(float v) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_f32<kDppXor1>(v);
+  v += dpp_f32<kDppXor2>(v);
+  v += dpp_f32<kDppHalfMirror>(v);
+  return v + dpp_f32<kDppMirror>(v);
 }
 
 // operand mask p of a raw code word: bytes hold field p of each byte (x1, x4, x16, x16)
