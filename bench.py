@@ -104,7 +104,10 @@ def main():
     cap = cfg["recent_k"].shape[2]
     step_src = t((np.arange(B) * n_kv * cap).astype(np.int32))
 
-    hist_bytes = int(cfg["hist_len"].sum()) * n_kv * (2 * d // 4 + 2 * 4)
+    # algorithmic bytes: every history token of a physical page once (a page
+    # shared by several requests' tables needs reading only once), the BF16
+    # windows and the block-table entries
+    hist_bytes = unique_tokens(cfg["block_table"], cfg["hist_len"]) * n_kv * (2 * d // 4 + 2 * 4)
     win_bytes = int((cfg["sink_len"] + cfg["recent_len"]).sum()) * n_kv * 4 * d
     table_bytes = int(sum(-(-int(h) // 64) for h in cfg["hist_len"])) * 4
     scan_bytes = hist_bytes + win_bytes + table_bytes
@@ -258,7 +261,7 @@ def main():
         nb = max(1, K // Rb)
         bf_sec, _ = timed(g_bf, None, nb)
         bf_us = bf_sec * 1e6 / (nb * Rb)
-        bf_need = int(bf["ctx_len"].sum()) * n_kv * 4 * d
+        bf_need = unique_tokens(bf["block_table"], bf["ctx_len"]) * n_kv * 4 * d
         result["bf16_comparator"] = {"decode_us": bf_us, "tokens_per_s": B / (bf_us * 1e-6),
                                      "algorithmic_GBps": bf_need / (bf_us * 1e-6) / 1e9, "replicas": Rb,
                                      "kernel": "oscar_decode_attn_bf16"}
@@ -304,6 +307,18 @@ def measured_traffic(workload: str):
         return float(fields["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def unique_tokens(table, lens) -> int:
+    """Tokens per KV head counted once per physical page slot: the valid
+    tokens of each page are the most that any request holding it uses."""
+    used = {}
+    for b, h in enumerate(lens):
+        h = int(h)
+        for i in range(-(-h // 64)):
+            pid = int(table[b, i])
+            used[pid] = max(used.get(pid, 0), min(64, h - 64 * i))
+    return sum(used.values())
 
 
 def ensure_free_slot(cfg):
