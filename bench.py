@@ -133,13 +133,16 @@ def main():
     torch.cuda.synchronize()
     log(f"demoted the history into {R} replicas in {time.time() - t0:.1f}s")
     del hist_k, hist_v
+    # a prefix-cache hit: the leading history pages every request holds at the same ids
+    shared = min(shape.shared_hist_pages, shape.hist_pages)
     ws_bytes = hip.oscar_decode_workspace_bytes(B, Hq, n_kv, d, hl, cfg["sink_k"].shape[2], cap)
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     dargs = [hip.decode_args(q=q, sink_k=rp["sink_k"], sink_v=rp["sink_v"], recent_k=rp["recent_k"],
                              recent_v=rp["recent_v"], sink_len=sink_len, recent_len=recent_len,
                              hist_len=hist_len, max_hist_len=hl, k_codes=rp["k_codes"], v_codes=rp["v_codes"],
                              k_sz=rp["k_sz"], v_sz=rp["v_sz"], block_table=table, r_k=r_k, r_v=r_v,
-                             out=rp["out"], workspace=ws, sm_scale=float(cfg["sm_scale"])) for rp in reps]
+                             out=rp["out"], workspace=ws, sm_scale=float(cfg["sm_scale"]),
+                             shared_pages=shared) for rp in reps]
 
     # the step demotes ring slot 0 of every request's recent window (K and V) in
     # the decode's first launch
@@ -228,7 +231,8 @@ def main():
         "config": {"workload": shape.name, "batch": B, "context": shape.context, "n_q_heads": Hq,
                    "n_kv_heads": n_kv, "head_dim": d, "sink": int(cfg["sink_len"][0]),
                    "history": hl, "recent": int(cfg["recent_len"][0]), "page_tokens": 64,
-                   "cache_replicas": R, "step": "oscar_decode_step: demote K,V of 1 token/request + decode attention"},
+                   "cache_replicas": R, "shared_prefix_pages": shared,
+                   "step": "oscar_decode_step: demote K,V of 1 token/request + decode attention"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload),
                      "kernel": "decode_main_kernel (oscar_decode_scan)", "kernel_us": scan_us,

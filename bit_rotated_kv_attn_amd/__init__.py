@@ -21,6 +21,7 @@ KIND_K, KIND_V = 0, 1
 COMPUTE_DTYPE = "i8 MFMA (exact integer digits) + f32 softmax; f64 rotation in demotion"
 OSCAR_OK, OSCAR_EINVAL, OSCAR_EUNSUPPORTED, OSCAR_EWORKSPACE, OSCAR_EHIP = range(5)
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liboscar.so")
+ABI_VERSION = 2   # OSCAR_ABI_VERSION of the oscar.h these mirrors follow
 
 _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 
@@ -32,7 +33,8 @@ class DecodeArgs(ctypes.Structure):
                 ("recent_v", _vp), ("sink_cap", _i32), ("recent_cap", _i32), ("sink_len", _vp),
                 ("recent_len", _vp), ("hist_len", _vp), ("max_hist_len", _i32), ("k_codes", _vp),
                 ("v_codes", _vp), ("k_sz", _vp), ("v_sz", _vp), ("n_pages", _i64),
-                ("block_table", _vp), ("max_pages", _i32), ("r_k", _vp), ("r_v", _vp), ("out", _vp)]
+                ("block_table", _vp), ("max_pages", _i32), ("r_k", _vp), ("r_v", _vp), ("out", _vp),
+                ("shared_pages", _i32)]
 
 
 class DemoteArgs(ctypes.Structure):
@@ -80,7 +82,7 @@ def lib() -> ctypes.CDLL:
     L.oscar_decode_bf16_workspace_bytes.argtypes = [_i32] * 5
     L.oscar_decode_attn_bf16.restype = ctypes.c_int
     L.oscar_decode_attn_bf16.argtypes = [ctypes.POINTER(Bf16DecodeArgs), _vp, _sz, _vp]
-    if L.oscar_abi_version() != 1:
+    if L.oscar_abi_version() != ABI_VERSION:
         raise RuntimeError("liboscar ABI version mismatch")
     _lib = L
     return L
@@ -157,13 +159,14 @@ def oscar_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, max_his
 
 def decode_args(*, q, sink_k, sink_v, recent_k, recent_v, sink_len, recent_len, hist_len, max_hist_len: int,
                 k_codes, v_codes, k_sz, v_sz, block_table, r_k, r_v, out, workspace,
-                sm_scale: float | None = None):
+                sm_scale: float | None = None, shared_pages: int = 0):
     """Marshal tensors into (DecodeArgs, workspace pointer, workspace bytes).
 
     q bf16 [B][Hq][d]; sink_k/v bf16 [B][n_kv][sink_cap][d]; recent_k/v bf16
     [B][n_kv][recent_cap][d]; *_len int32 [B]; pools as for oscar_quantize_pack;
     block_table int32 [B][max_pages]; r_k/r_v fp32 [n_kv][d][d]; out fp32
-    [B][Hq][d]; workspace uint8 device tensor (size from oscar_decode_workspace_bytes).
+    [B][Hq][d]; workspace uint8 device tensor (size from oscar_decode_workspace_bytes);
+    shared_pages: leading history pages every request holds at the same ids (0: none).
     The tensors must stay alive while the call (or a captured graph) uses them."""
     B, Hq, d = q.shape
     n_kv = sink_k.shape[1]
@@ -179,7 +182,8 @@ def decode_args(*, q, sink_k, sink_v, recent_k, recent_v, sink_len, recent_len, 
                    k_codes=_ptr(k_codes, 1, "k_codes"), v_codes=_ptr(v_codes, 1, "v_codes"),
                    k_sz=_ptr(k_sz, 2, "k_sz"), v_sz=_ptr(v_sz, 2, "v_sz"), n_pages=k_codes.shape[0],
                    block_table=_ptr(block_table, 4, "block_table"), max_pages=block_table.shape[1],
-                   r_k=_ptr(r_k, 4, "r_k"), r_v=_ptr(r_v, 4, "r_v"), out=_ptr(out, 4, "out"))
+                   r_k=_ptr(r_k, 4, "r_k"), r_v=_ptr(r_v, 4, "r_v"), out=_ptr(out, 4, "out"),
+                   shared_pages=int(shared_pages))
     return a, _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size()
 
 

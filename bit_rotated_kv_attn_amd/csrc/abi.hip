@@ -83,6 +83,8 @@ oscar_status check_decode(const oscar_decode_args* a, void* workspace, size_t wo
                                        a->max_hist_len, a->sink_cap, a->recent_cap);
   if (st != OSCAR_OK) return st;
   if (!std::isfinite(a->sm_scale) || !(a->sm_scale > 0.0f)) return OSCAR_EINVAL;
+  if (a->shared_pages < 0 || (int64_t)a->shared_pages * OSCAR_PAGE_TOKENS > a->max_hist_len)
+    return OSCAR_EINVAL;
   *plan = make_decode_plan(a->batch, a->n_q_heads, a->n_kv_heads, a->head_dim, a->max_hist_len,
                            a->sink_cap, a->recent_cap);
   if (a->batch == 0) return OSCAR_OK;

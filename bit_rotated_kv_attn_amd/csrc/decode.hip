@@ -57,6 +57,9 @@ constexpr int kBf16WaveTokens = 16;       // tokens of a BF16 chunk per wave (4 
 struct DecodeDev {
   int B, Hq, n_kv, G, NB, sink_cap, recent_cap, max_hist_len, max_pages;
   int splits, pps, chunks, sink_chunks, bf_blocks;   // bf_blocks: BF16 blocks per unit (one per chunk)
+  // shared-prefix packing (G = 4 only): the first n_pref splits lie inside the
+  // prefix and are read once for each of the `pairs` request pairs (2i, 2i+1)
+  int n_pref, pairs;
   float sm_log2;
   int64_t n_pages;
   const uint16_t *q, *sink_k, *sink_v, *recent_k, *recent_v;
@@ -377,8 +380,11 @@ __device__ __forceinline__ void store_wave_state(const WaveAcc<D, G>& st, float*
 // mrg + v*slot floats) into one partial.  kBlock/G threads serve each head, so
 // a thread computes the four weights of its head once; every LDS read is
 // issued before the first exponential.
-template <int G, int D>
-__device__ __forceinline__ void combine_block(const float* mrg, int slot, const int* flags, float* dst, int tid) {
+// Heads h >= GH (a block that serves two requests) write to the next
+// request's rows, ustride floats further on.
+template <int G, int D, int GH = G>
+__device__ __forceinline__ void combine_block(const float* mrg, int slot, const int* flags, float* dst, int tid,
+                                              size_t ustride = 0) {
   constexpr int R = part_row(D), TPH = kBlock / G, IT = (R + TPH - 1) / TPH;
   const int h = tid / TPH, t = tid - h * TPH;
   if (h >= G) return;
@@ -404,7 +410,7 @@ __device__ __forceinline__ void combine_block(const float* mrg, int slot, const 
       float s = 0.0f;
 #pragma unroll
       for (int v = 0; v < 4; ++v) s = fmaf(w[v], x[k][v], s);
-      dst[h * R + r] = (r == 0) ? M : (r == 1) ? (bad ? NAN : s) : (r < kPartAcc) ? 0.0f : s;
+      dst[(h / GH) * ustride + (h % GH) * R + r] = (r == 0) ? M : (r == 1) ? (bad ? NAN : s) : (r < kPartAcc) ? 0.0f : s;
     }
   }
 }
@@ -550,6 +556,23 @@ __device__ __forceinline__ void load_hist_operands(const DecodeDev& p, int b, in
                        ((((size_t)b * p.n_kv + g) * NB + nb) * NCH + c) * kWave + lane;
       o.qa[nb][c] = row_ok ? *src : v4i{0, 0, 0, 0};
     }
+  }
+}
+
+// The QK operands of a request pair (b, b+1) at group size 4: head block nb
+// of the 8-head wave is request b+nb's only head block.
+template <int D>
+__device__ __forceinline__ void load_pair_operands(const DecodeDev& p, int b, int g, int lane, HistOperands<D, 8>& o) {
+  constexpr int NCH = D / 64;
+  const int grp = lane >> 4;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int unit = (b + nb) * p.n_kv + g;
+    o.ca[nb] = p.qa[(size_t)(b + nb) * p.Hq + g * 4 + grp];
+    o.cb[nb] = p.qb[(size_t)(b + nb) * p.Hq + g * 4 + grp];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      o.qa[nb][c] = reinterpret_cast<const v4i*>(p.qdig)[((size_t)unit * NCH + c) * kWave + lane];
   }
 }
 
@@ -924,7 +947,10 @@ template <int D, int G>
 __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) void decode_main_kernel(DecodeDev p) {
   constexpr int NB = (G + 3) / 4;
   using RG = Ring<D, NB>;
-  constexpr int kHistBytes = 4 * RG::kWaveBytes;
+  // a group-4 kernel also runs 8-head waves (two requests) on shared-prefix splits
+  constexpr int kHistOwn = 4 * RG::kWaveBytes;
+  constexpr int kHistPair = G == 4 ? 4 * Ring<D, 2>::kWaveBytes : 0;
+  constexpr int kHistBytes = kHistOwn > kHistPair ? kHistOwn : kHistPair;
   constexpr int kBf16Bytes = 4 * bf16_lds_bytes<D, G>();
   constexpr int kSmem = kHistBytes > kBf16Bytes ? kHistBytes : kBf16Bytes;
   static_assert(4 * G * part_row(D) * 4 <= kSmem, "BF16 merge slots must fit");
@@ -935,13 +961,19 @@ __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) vo
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int units = p.B * p.n_kv;
   const int id = blockIdx.x;
+  // block ids: the shared-prefix splits read for request pairs (split, pair,
+  // KV head), the other history splits (split, request, KV head), an odd last
+  // request's prefix splits (split, KV head), then the BF16 chunks
+  const int n_packed = p.n_pref * p.pairs * p.n_kv;
+  const int n_rest = (p.splits - p.n_pref) * units;
+  const int n_hist = n_packed + n_rest + p.n_pref * (p.B & 1) * p.n_kv;
   bool poison = false;
 
-  if (id >= units * p.splits) {
+  if (id >= n_hist) {
     // ---- BF16 sink / recent chunk (block-uniform), after every history block:
     // one chunk per block, 16 tokens per wave.  Spread this thin, a block's
     // loads stay small next to the history block that shares its CU.
-    const int cid = id - units * p.splits;
+    const int cid = id - n_hist;
     const int unit = cid % units, c = cid / units;
     const int b = unit / p.n_kv, g = unit % p.n_kv;
     WaveAcc<D, G> st;
@@ -988,10 +1020,56 @@ __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) vo
     return;
   }
 
-  // ---- INT2 history split: waves take contiguous page ranges
-  const int hid = id;
-  const int unit = hid % units, split = hid / units;
-  const int b = unit / p.n_kv, g = unit % p.n_kv;
+  if constexpr (G == 4) {
+    if (id < n_packed) {
+      // ---- a split inside the shared prefix for requests b and b+1: one
+      // 8-head wave reads each page once for both
+      using RP = Ring<D, 2>;
+      static_assert(8 * part_row(D) * 4 <= RP::kWaveBytes, "merge slot must fit in the wave's ring");
+      const int per_split = p.pairs * p.n_kv;
+      const int split = id / per_split, pair = (id % per_split) / p.n_kv, g = id % p.n_kv;
+      const int b = 2 * pair;
+      const int per_wave = (p.pps + 3) / 4;
+      const int ws0 = split * p.pps + wave * per_wave;
+      const int pe = split * p.pps + p.pps;   // split end; the prefix holds it whole
+      const bool mine = lane < per_wave && ws0 + lane < pe;
+      const int32_t* row = p.block_table + (size_t)b * p.max_pages;
+      const int pid_lane = mine ? row[ws0 + lane] : -1;
+      const int pid_other = mine ? row[p.max_pages + ws0 + lane] : -1;
+      HistOperands<D, 8> qo;
+      load_pair_operands<D>(p, b, g, lane, qo);
+      const int hl0 = p.hist_len[b], hl1 = p.hist_len[b + 1];
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      const int full = pe * kPage;   // both histories must cover the split
+      if (hl0 < full || hl1 < full || hl0 > p.max_hist_len || hl1 > p.max_hist_len || __any(pid_lane != pid_other))
+        poison = true;
+      const int count =
+          __builtin_amdgcn_readfirstlane(poison ? 0 : max(0, min(ws0 + per_wave, pe) - ws0));
+      uint8_t* ring = smem + wave * RP::kWaveBytes;
+      hist_wave<D, 8>(p, g, ws0, count, full, pid_lane, qo, ring, reinterpret_cast<float*>(ring), poison, lane);
+      if (lane == 0) flags[wave] = poison ? 1 : 0;
+      __syncthreads();
+      const size_t rows = (size_t)4 * part_row(D);
+      combine_block<8, D, 4>(reinterpret_cast<const float*>(smem), RP::kWaveBytes / 4, flags,
+                             p.hpart + (((size_t)b * p.n_kv + g) * p.splits + split) * rows, tid,
+                             (size_t)p.n_kv * p.splits * rows);
+      return;
+    }
+  }
+
+  // ---- INT2 history split of one request: waves take contiguous page ranges
+  int b, g, split;
+  if (id < n_packed + n_rest) {
+    const int j = id - n_packed, unit = j % units;
+    split = p.n_pref + j / units;
+    b = unit / p.n_kv;
+    g = unit % p.n_kv;
+  } else {   // the odd last request's prefix splits
+    const int j = id - n_packed - n_rest;
+    split = j / p.n_kv;
+    g = j % p.n_kv;
+    b = p.B - 1;
+  }
   const int per_wave = (p.pps + 3) / 4;   // at most 64
   const int ws0 = split * p.pps + wave * per_wave;   // the wave's first page, before the history length clips it
   // The page ids of the wave's whole static range, the QK operands and the
@@ -1223,7 +1301,9 @@ __global__ __launch_bounds__(kBlock) void merge_plain_kernel(Bf16Dev p) {
 
 template <int D, int G>
 void launch_main(const DecodeDev& dv, hipStream_t stream) {
-  const long blocks = (long)dv.B * dv.n_kv * (dv.bf_blocks + dv.splits);
+  const long units = (long)dv.B * dv.n_kv;
+  const long blocks = (long)dv.n_pref * dv.pairs * dv.n_kv + (long)(dv.splits - dv.n_pref) * units +
+                      (long)dv.n_pref * (dv.B & 1) * dv.n_kv + units * dv.bf_blocks;
   if (blocks == 0) return;
   decode_main_kernel<D, G><<<dim3((unsigned)blocks), kBlock, 0, stream>>>(dv);
 }
@@ -1265,6 +1345,10 @@ DecodeDev make_dev(const oscar_decode_args& a, const DecodePlan& plan, char* ws)
   dv.splits = plan.splits; dv.pps = plan.pages_per_split;
   dv.chunks = plan.chunks; dv.sink_chunks = plan.sink_chunks;
   dv.bf_blocks = plan.chunks;
+  // pack the splits that lie wholly inside a shared prefix (group size 4, two or more requests)
+  dv.pairs = a.batch / 2;
+  dv.n_pref = (dv.G == 4 && dv.pairs > 0 && plan.splits > 0) ? std::min(plan.splits, a.shared_pages / plan.pages_per_split)
+                                                            : 0;
   dv.sm_log2 = a.sm_scale * kLog2e;
   dv.n_pages = a.n_pages;
   dv.q = a.q; dv.sink_k = a.sink_k; dv.sink_v = a.sink_v; dv.recent_k = a.recent_k; dv.recent_v = a.recent_v;

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define OSCAR_ABI_VERSION 1
+#define OSCAR_ABI_VERSION 2
 #define OSCAR_PAGE_TOKENS 64
 
 #ifndef OSCAR_API
@@ -151,6 +151,18 @@ typedef struct oscar_decode_args {
   const float* r_k;         /* fp32 [n_kv][d][d], the R used to quantise K         */
   const float* r_v;         /* fp32 [n_kv][d][d], the R used to quantise V         */
   float* out;               /* fp32 [B][n_q_heads][head_dim]                       */
+  int32_t shared_pages;     /* 0, or the length in pages of a history prefix that every
+                               request holds at the same physical pages: block_table[b][i]
+                               is one id for all b when i < shared_pages, and every
+                               hist_len[b] >= 64*shared_pages (0 <= shared_pages and
+                               64*shared_pages <= max_hist_len).  A prefix cache makes such
+                               tables.  With n_q_heads/n_kv_heads = 4 the scan then reads
+                               the history splits that lie inside the prefix once for each
+                               pair of requests (0,1), (2,3), ... (8 query heads per KV
+                               head and page instead of 4); other group sizes ignore it.
+                               For each pair the scan checks the pages it reads for both:
+                               if the two rows' ids differ there, or either history ends
+                               before them, both requests' output rows are NaN.        */
 } oscar_decode_args;
 
 /* Workspace bytes oscar_decode_attn needs for these sizes (0 on invalid sizes).

@@ -51,7 +51,7 @@ def oracle_pools(cfg: dict):
 
 
 def gpu_decode(cfg: dict, pools, *, block_table=None, hist_len=None, sink_len=None, recent_len=None,
-               max_hist_len=None, reps: int = 1) -> np.ndarray:
+               max_hist_len=None, reps: int = 1, shared_pages: int = 0) -> np.ndarray:
     kc, vc, ks, vs = (p if isinstance(p, torch.Tensor) else dev(p) for p in pools)
     q = dev(cfg["q"])
     B, Hq, d = cfg["q"].shape
@@ -68,7 +68,7 @@ def gpu_decode(cfg: dict, pools, *, block_table=None, hist_len=None, sink_len=No
                 recent_len=dev(cfg["recent_len"] if recent_len is None else recent_len),
                 hist_len=dev(hl), max_hist_len=mh, k_codes=kc, v_codes=vc, k_sz=ks, v_sz=vs,
                 block_table=dev(table), r_k=dev(cfg["r_k"]), r_v=dev(cfg["r_v"]), out=out, workspace=ws,
-                sm_scale=float(cfg["sm_scale"]))
+                sm_scale=float(cfg["sm_scale"]), shared_pages=shared_pages)
     for _ in range(reps):
         hip.oscar_decode_attn(**args)
     torch.cuda.synchronize()

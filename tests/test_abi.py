@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
     L = hip.lib()
     for n in declared_functions():
         assert hasattr(L, n), n
-    assert hip.oscar_abi_version() == 1
+    assert hip.oscar_abi_version() == hip.ABI_VERSION == 2
     # the binding offers a function of the same name for each entry point
     for n in declared_functions():
         assert callable(getattr(hip, n)), n
@@ -92,6 +92,8 @@ def _decode_args(**kw):
     (dict(n_pages=0), hip.OSCAR_EINVAL),
     (dict(sink_cap=5000), hip.OSCAR_EINVAL),
     (dict(max_hist_len=-1), hip.OSCAR_EINVAL),
+    (dict(shared_pages=-1), hip.OSCAR_EINVAL),
+    (dict(shared_pages=2), hip.OSCAR_EINVAL),                        # 2 pages > max_hist_len 100
     (dict(batch=0, q=None, out=None), hip.OSCAR_OK),
 ])
 def test_decode_validation(kw, status):

@@ -115,8 +115,9 @@ def test_qwen3_32b_layer_100k():
 
 
 def test_batch28_shared_prefix_100k_sampled():
-    """28 requests x 100k context, 1406 shared history pages; pages are drawn
-    directly (uniform codes, realistic fp16 scale/zero).  The oracle computes a
+    """28 requests x 100k context, 1406 shared history pages, declared to the
+    scan (read once per request pair); pages are drawn directly (uniform codes,
+    realistic fp16 scale/zero).  The oracle computes a
     seeded sample of (request, head) rows; the rest are checked finite."""
     cfg = synth.make_decode_config(4, materialize_history=False)
     rng = np.random.default_rng(2024)
@@ -124,7 +125,7 @@ def test_batch28_shared_prefix_100k_sampled():
     kc, ks = synth.random_pages(rng, cfg["n_pages"], cfg["n_kv"], cfg["head_dim"], sigma)
     vc, vs = synth.random_pages(rng, cfg["n_pages"], cfg["n_kv"], cfg["head_dim"], sigma)
     pools = (kc, vc, ks, vs)
-    got = gpu_decode(cfg, pools)
+    got = gpu_decode(cfg, pools, shared_pages=cfg["shape"].shared_hist_pages)
     heads = [(0, 0), (5, 13), (27, 31), (14, 8), (27, 2)]
     ref = oracle.decode_attn_ref(cfg, *pools, heads=heads)
     idx = tuple(np.array(heads).T)
