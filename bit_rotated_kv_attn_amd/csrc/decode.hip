@@ -1239,6 +1239,107 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(DecodeDev p) {
 }
 
 // ---- BF16 paged comparator ---------------------------------------------
+// One (request, KV head) per block, for launches whose heads have at most
+// kUnitRound partials each (large batches, few splits): the R_V rows are
+// loaded once for the unit's G heads rather than once per head, and every
+// partial of every head is requested in one round.  Thread (h, q) owns
+// channels 4q..4q+3 of head h.
+constexpr int kUnitRound = 16;
+
+template <int D, int G>
+__global__ __launch_bounds__(kBlock) void merge_unit_kernel(DecodeDev p) {
+  constexpr int QPR = D / 4, R = part_row(D), TPO = kBlock / D, SEG = D / TPO;
+  static_assert(G * QPR <= kBlock, "one (head, channel quad) per thread");
+  __shared__ __attribute__((aligned(16))) float arot[G][D];
+  __shared__ __attribute__((aligned(16))) float aplain[G][D];
+  __shared__ float Ls[G];
+  const int unit = blockIdx.x, b = unit / p.n_kv, g = unit % p.n_kv;
+  const int tid = threadIdx.x;
+  const int i = tid / TPO, seg = tid % TPO;   // output channel and R_V row segment of this thread
+  float4 rv[SEG / 4];
+  {
+    const float4* Rrow = reinterpret_cast<const float4*>(p.r_v + ((size_t)g * D + i) * D + seg * SEG);
+#pragma unroll
+    for (int k = 0; k < SEG / 4; ++k) rv[k] = Rrow[k];
+  }
+  const size_t stride = (size_t)G * R;
+  const int n = p.splits, nt = p.splits + p.chunks;
+  const float* hb = p.hpart + (size_t)unit * n * stride;
+  const float* bb = p.bpart + (size_t)unit * p.chunks * stride;
+  if (tid < G * QPR) {
+    const int h = tid / QPR, q = tid % QPR;
+    float2 ml[kUnitRound];
+    float4 av[kUnitRound];
+#pragma unroll
+    for (int s = 0; s < kUnitRound; ++s) {
+      if (s < nt) {
+        const float* pp = (s < n ? hb + (size_t)s * stride : bb + (size_t)(s - n) * stride) + h * R;
+        ml[s] = *reinterpret_cast<const float2*>(pp);
+        av[s] = *reinterpret_cast<const float4*>(pp + kPartAcc + 4 * q);
+      } else {
+        ml[s] = make_float2(-INFINITY, 0.0f);
+        av[s] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      }
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kUnitRound; ++s) M = fmaxf(M, ml[s].x);
+    float L = 0.0f;
+    float4 ar = make_float4(0.0f, 0.0f, 0.0f, 0.0f), ap = ar;
+#pragma unroll
+    for (int s = 0; s < kUnitRound; ++s) {
+      const float f = exp2_or_zero(ml[s].x, M);
+      const float fr = s < n ? f : 0.0f;   // history partials are still rotated
+      L = fmaf(f, ml[s].y, L);
+      ar = f4_fma(fr, av[s], ar);
+      ap = f4_fma(f - fr, av[s], ap);
+    }
+    *reinterpret_cast<float4*>(&arot[h][4 * q]) = ar;
+    *reinterpret_cast<float4*>(&aplain[h][4 * q]) = ap;
+    if (q == 0) Ls[h] = L;
+  }
+  __syncthreads();
+  // out[h][i] = (sum_j A_hist[h][j] R_V[g][i][j] + A_bf16[h][i]) / L[h]
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float4* a4 = reinterpret_cast<const float4*>(&arot[h][seg * SEG]);
+    float o = 0.0f;
+#pragma unroll
+    for (int k = 0; k < SEG / 4; ++k) {
+      const float4 a = a4[k];
+      o = fmaf(a.x, rv[k].x, fmaf(a.y, rv[k].y, fmaf(a.z, rv[k].z, fmaf(a.w, rv[k].w, o))));
+    }
+#pragma unroll
+    for (int off = 1; off < TPO; off <<= 1) o += __shfl_xor(o, off, kWave);
+    if (seg == 0) {
+      const float L = Ls[h];
+      float out;
+      if (isnan(L)) out = NAN;
+      else out = (L > 0.0f) ? (o + aplain[h][i]) / L : 0.0f;
+      p.out[((size_t)b * p.Hq + (size_t)g * G + h) * D + i] = out;
+    }
+  }
+}
+
+// The per-unit merge when each head's partials fit in one round and the G
+// heads' channel quads fit in one block.
+template <int D>
+bool launch_merge_unit(const DecodeDev& dv, hipStream_t stream) {
+  if (dv.splits + dv.chunks > kUnitRound || dv.G * (D / 4) > kBlock) return false;
+  const unsigned units = (unsigned)dv.B * (unsigned)dv.n_kv;
+  switch (dv.G) {
+    case 1: merge_unit_kernel<D, 1><<<units, kBlock, 0, stream>>>(dv); break;
+    case 2: merge_unit_kernel<D, 2><<<units, kBlock, 0, stream>>>(dv); break;
+    case 4: merge_unit_kernel<D, 4><<<units, kBlock, 0, stream>>>(dv); break;
+    case 8: merge_unit_kernel<D, 8><<<units, kBlock, 0, stream>>>(dv); break;
+    default:
+      if constexpr (16 * (D / 4) <= kBlock) merge_unit_kernel<D, 16><<<units, kBlock, 0, stream>>>(dv);
+      else return false;
+      break;
+  }
+  return true;
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : 2)) void bf16_paged_kernel(Bf16Dev p) {
   constexpr int kWaveLds = bf16_lds_bytes<D, G>();
@@ -1387,9 +1488,10 @@ hipError_t launch_decode_phase(int phase, const oscar_decode_args& a, const Deco
   } else if (phase == kPhaseScan) {
     if (d128) launch_main_g<128>(dv, stream);
     else launch_main_g<64>(dv, stream);
+  } else if (d128) {
+    if (!launch_merge_unit<128>(dv, stream)) merge_kernel<128><<<nbh, kBlock, 0, stream>>>(dv);
   } else {
-    if (d128) merge_kernel<128><<<nbh, kBlock, 0, stream>>>(dv);
-    else merge_kernel<64><<<nbh, kBlock, 0, stream>>>(dv);
+    if (!launch_merge_unit<64>(dv, stream)) merge_kernel<64><<<nbh, kBlock, 0, stream>>>(dv);
   }
   return hipGetLastError();
 }

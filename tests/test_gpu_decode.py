@@ -44,6 +44,28 @@ def test_ragged_segments(G, d):
     compare_out(got, ref, what=f"ragged G={G} d={d}")
 
 
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("d", [64, 128])
+def test_large_batch_merge(G, d):
+    """16 requests x 2 KV heads: at most 11 history splits per head, so every
+    head's partials fit one round and the merge runs one block per (request,
+    KV head) (per head when G*d/4 exceeds a block).  Ragged segments, an empty
+    history and an empty context among them."""
+    rng = np.random.default_rng(70 + G + d)
+    B = 16
+    hist = [int(x) for x in rng.integers(1, 700, size=B)]
+    sink = [int(x) for x in rng.integers(0, 65, size=B)]
+    recent = [int(x) for x in rng.integers(0, 257, size=B)]
+    hist[3] = 0
+    sink[5], hist[5], recent[5] = 0, 0, 0
+    cfg, pools = ragged_cache(80 + G + d, B=B, n_kv=2, G=G, d=d, sink=tuple(sink), hist=tuple(hist),
+                              recent=tuple(recent))
+    ref = oracle.decode_attn_ref(cfg, *pools)
+    got = gpu_decode(cfg, pools)
+    assert not got[5].any()
+    compare_out(got, ref, what=f"large batch G={G} d={d}")
+
+
 def test_empty_context_rows_are_zero():
     cfg, pools = ragged_cache(3, B=2, n_kv=1, G=4, d=64, sink=(0, 3), hist=(0, 70), recent=(0, 2))
     got = gpu_decode(cfg, pools)
