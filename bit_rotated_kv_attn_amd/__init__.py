@@ -8,6 +8,10 @@ kernels of liboscar.so.  There is no fallback: if the library is not built,
 every call raises.  Build it with ``python -m bit_rotated_kv_attn_amd.build``.
 
 PyTorch is used for device memory and streams only.
+
+The offline calibration that produces the rotations and clip thresholds these
+calls take (``bit_rotated_kv_attn_amd.calibrate``) is a separate host-side
+step, run once per model before any decode; it is not part of the decode path.
 """
 from __future__ import annotations
 
