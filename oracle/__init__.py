@@ -36,14 +36,16 @@ Page sources, cited by title and section:
 Parity status of each function is given in its docstring.  Every public
 function is pinned by ``tests/test_oracle_*.py``.
 """
-from .quant import (PAGE, bf16_to_f64, f16_bits_to_f64, rotate_round_f32, quantize_group,
+from .quant import (PAGE, UNIFORM, LLOYD_MAX, LM_LEVELS, LM_THRESHOLDS, LM_UNIT, code_levels, bf16_to_f64,
+                    f16_bits_to_f64, rotate_round_f32, quantize_group, quantize_group_lloyd_max,
                     pack_codes_row, unpack_codes_row, k_byte_offsets, v_byte_offsets,
                     quantize_pack_ref, read_history_codes, page_block_bytes)
 from .attention import (attn_plain, attn_partial, merge_partials, dequant_history,
                         decode_attn_ref, bf16_paged_attn_ref)
 
 __all__ = [
-    "PAGE", "bf16_to_f64", "f16_bits_to_f64", "rotate_round_f32", "quantize_group",
+    "PAGE", "UNIFORM", "LLOYD_MAX", "LM_LEVELS", "LM_THRESHOLDS", "LM_UNIT", "code_levels",
+    "bf16_to_f64", "f16_bits_to_f64", "rotate_round_f32", "quantize_group", "quantize_group_lloyd_max",
     "pack_codes_row", "unpack_codes_row", "k_byte_offsets", "v_byte_offsets",
     "quantize_pack_ref", "read_history_codes", "page_block_bytes",
     "attn_plain", "attn_partial", "merge_partials", "dequant_history", "decode_attn_ref",

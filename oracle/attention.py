@@ -24,7 +24,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .quant import PAGE, bf16_to_f64, f16_bits_to_f64, read_history_codes
+from .quant import PAGE, UNIFORM, bf16_to_f64, code_levels, f16_bits_to_f64, read_history_codes
 
 
 def attn_plain(q: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float) -> np.ndarray:
@@ -67,17 +67,18 @@ def merge_partials(parts) -> np.ndarray:
 
 
 def dequant_history(kind: str, codes_pool, sz_pool, table_row, hist_len: int, g: int, d: int,
-                    n_pages: int | None = None) -> np.ndarray:
-    """Dequantised, still-rotated history vectors x_hat = zero + code * scale
-    (float64 [hist_len, d]) of KV head g, in history order.  History token t
-    is in page table_row[t // 64] at offset t % 64."""
+                    n_pages: int | None = None, codebook: str = UNIFORM) -> np.ndarray:
+    """Dequantised, still-rotated history vectors x_hat = zero + level(code) *
+    scale (float64 [hist_len, d]) of KV head g, in history order; level(c) = c
+    for the uniform codebook, LM_LEVELS[c] for the Lloyd-Max one.  History
+    token t is in page table_row[t // 64] at offset t % 64."""
     t = np.arange(hist_len)
     pages = np.asarray(table_row, dtype=np.int64)[t // PAGE]
     n_pages = codes_pool.shape[0] if n_pages is None else n_pages
     if hist_len and (pages.min() < 0 or pages.max() >= n_pages):
         raise ValueError("block table entry outside the page pool")
     codes, s16, z16 = read_history_codes(kind, codes_pool, sz_pool, pages, t % PAGE, g, d)
-    return f16_bits_to_f64(z16)[:, None] + codes.astype(np.float64) * f16_bits_to_f64(s16)[:, None]
+    return f16_bits_to_f64(z16)[:, None] + code_levels(codebook)[codes] * f16_bits_to_f64(s16)[:, None]
 
 
 def decode_attn_ref(cfg: dict, k_codes, v_codes, k_sz, v_sz, block_table=None, hist_len=None,
@@ -87,7 +88,8 @@ def decode_attn_ref(cfg: dict, k_codes, v_codes, k_sz, v_sz, block_table=None, h
     cfg holds: q bf16 [B][Hq][d]; sink_k/sink_v bf16 [B][n_kv][sink_cap][d];
     recent_k/recent_v bf16 [B][n_kv][recent_cap][d]; sink_len, recent_len,
     hist_len int32 [B]; block_table int32 [B][max_pages]; r_k, r_v fp32
-    [n_kv][d][d]; sm_scale.  Optional overrides replace the cfg entries.
+    [n_kv][d][d]; sm_scale; optionally codebook ("uniform" by default or
+    "lloyd_max").  Optional overrides replace the cfg entries.
     ``heads`` restricts the work to a list of (b, h) pairs (others are NaN).
 
     Returns float32 [B][Hq][d]."""
@@ -114,8 +116,9 @@ def decode_attn_ref(cfg: dict, k_codes, v_codes, k_sz, v_sz, block_table=None, h
                 continue
             Rk = np.asarray(cfg["r_k"][g], dtype=np.float32).astype(np.float64)
             Rv = np.asarray(cfg["r_v"][g], dtype=np.float32).astype(np.float64)
-            xk = dequant_history("k", k_codes, k_sz, table[b], int(hl[b]), g, d)
-            xv = dequant_history("v", v_codes, v_sz, table[b], int(hl[b]), g, d)
+            cb = cfg.get("codebook", UNIFORM)
+            xk = dequant_history("k", k_codes, k_sz, table[b], int(hl[b]), g, d, codebook=cb)
+            xv = dequant_history("v", v_codes, v_sz, table[b], int(hl[b]), g, d, codebook=cb)
             K = np.concatenate([bf16_to_f64(cfg["sink_k"][b, g, : sl[b]]), xk @ Rk.T,
                                 bf16_to_f64(cfg["recent_k"][b, g, : rl[b]])])
             V = np.concatenate([bf16_to_f64(cfg["sink_v"][b, g, : sl[b]]), xv @ Rv.T,

@@ -16,6 +16,17 @@ Readings where the pages leave the step open:
   scale = fp16((max - min) / 3), code = clamp(rint((y - zero) / scale), 0, 3),
   round half to even, dequantised as zero + code * scale;
 * degenerate group (scale rounds to 0): all codes 0;
+* Lloyd-Max variant (the authors' repository combines the rotation with a
+  Lloyd-Max codebook, [GIST] section on code availability; the pages give no
+  levels): the 4-level mean-squared-error optimal quantiser of a Gaussian,
+  levels +-0.4528 and +-1.5104 standard deviations, taken here in the integer
+  ratio 3 : 10, LM_LEVELS = (-10, -3, 3, 10) units.  Per group: mean m and
+  population standard deviation s of the clipped values in float64 (two
+  passes), zero = fp16(fp32(m)), scale = fp16(fp32(LM_UNIT * s)) with
+  LM_UNIT = 0.15104 (so 10 units = 1.5104 s).  With z, u the fp16 values
+  widened, the decision thresholds are the midpoints t = fp32(z + u * th),
+  th = (-6.5, 0, 6.5), and the code is the number of thresholds the clipped
+  value reaches (y >= t).  Dequantised as zero + LM_LEVELS[code] * scale;
 * pack order: byte i of a token's row holds channels 4i..4i+3, with channel
   4i+j in bits 2j..2j+1;
 * in-page layout (64-token pages, one block per (page, KV head)):
@@ -28,6 +39,19 @@ from __future__ import annotations
 import numpy as np
 
 PAGE = 64
+UNIFORM, LLOYD_MAX = "uniform", "lloyd_max"
+LM_LEVELS = np.array([-10.0, -3.0, 3.0, 10.0])
+LM_THRESHOLDS = np.array([-6.5, 0.0, 6.5])
+LM_UNIT = 0.15104
+
+
+def code_levels(codebook: str) -> np.ndarray:
+    """Dequantised level of each code in units of the group scale."""
+    if codebook == UNIFORM:
+        return np.array([0.0, 1.0, 2.0, 3.0])
+    if codebook == LLOYD_MAX:
+        return LM_LEVELS.copy()
+    raise ValueError("codebook must be 'uniform' or 'lloyd_max'")
 
 
 def bf16_to_f64(bits) -> np.ndarray:
@@ -45,6 +69,28 @@ def rotate_round_f32(x_bits: np.ndarray, rot: np.ndarray) -> np.ndarray:
     """y = x R for row vectors, accumulated in float64 and rounded once to
     float32.  x_bits: bf16 [..., d]; rot: fp32 [d, d]."""
     return (bf16_to_f64(x_bits) @ np.asarray(rot, dtype=np.float32).astype(np.float64)).astype(np.float32)
+
+
+def quantize_group_lloyd_max(y: np.ndarray, clip):
+    """Clip and quantise the rows of y (float32 [n, d]) to the Lloyd-Max codes
+    (one group per row).  Returns the same tuple as :func:`quantize_group`;
+    info holds the float32 clipped values and the float64 mean and deviation."""
+    y = np.asarray(y, dtype=np.float32)
+    tau = np.float32(clip)
+    yc = np.minimum(np.maximum(y, -tau), tau)
+    y64 = yc.astype(np.float64)
+    mean = y64.sum(axis=1) / y64.shape[1]
+    dev = np.sqrt(((y64 - mean[:, None]) ** 2).sum(axis=1) / y64.shape[1])
+    zero16 = mean.astype(np.float32).astype(np.float16)
+    scale16 = (LM_UNIT * dev).astype(np.float32).astype(np.float16)
+    z = zero16.astype(np.float64)[:, None]
+    u = scale16.astype(np.float64)[:, None]
+    codes = np.zeros(yc.shape, np.uint8)
+    for th in LM_THRESHOLDS:
+        t = (z + u * th).astype(np.float32)       # exact in float64, one rounding to float32
+        codes += (yc >= t).astype(np.uint8)
+    info = dict(yc=yc, mn=mean, mx=dev, range3=(LM_UNIT * dev).astype(np.float32))
+    return codes, scale16.view(np.uint16), zero16.view(np.uint16), info
 
 
 def quantize_group(y: np.ndarray, clip):
@@ -116,7 +162,7 @@ def _offsets(kind: str, offset, d: int):
 
 def quantize_pack_ref(kind: str, x_bits: np.ndarray, rot: np.ndarray, clip, dst_slot: np.ndarray,
                       codes_pool: np.ndarray, sz_pool: np.ndarray, src_idx: np.ndarray | None = None,
-                      chunk: int = 16384):
+                      chunk: int = 16384, codebook: str = UNIFORM):
     """Demote tokens of one tensor (K or V) of one layer into INT2 pages, in place.
 
     x_bits   bf16 [n_src][n_kv][d]
@@ -127,6 +173,7 @@ def quantize_pack_ref(kind: str, x_bits: np.ndarray, rot: np.ndarray, clip, dst_
     src_idx  int32 [n_tok] rows of x, or None for rows 0..n_tok-1; rows
              outside [0, n_src) are skipped
     codes_pool uint8 [n_pages][n_kv][64*d/4]; sz_pool uint16 [n_pages][n_kv][64][2]
+    codebook "uniform" (min-max) or "lloyd_max"
 
     Returns a dict of per-(token, head) diagnostics for the written tokens
     (arrays [n_written][n_kv]...) used by the parity checker."""
@@ -137,6 +184,7 @@ def quantize_pack_ref(kind: str, x_bits: np.ndarray, rot: np.ndarray, clip, dst_
         raise ValueError("clip must be finite, > 0 and <= 65504")
     if d % 16:
         raise ValueError("head_dim must be a multiple of 16")
+    quantize = {UNIFORM: quantize_group, LLOYD_MAX: quantize_group_lloyd_max}[codebook]
     n_pages = codes_pool.shape[0]
     dst = np.asarray(dst_slot, dtype=np.int64).ravel()
     src = np.arange(dst.size) if src_idx is None else np.asarray(src_idx, dtype=np.int64).ravel()
@@ -152,7 +200,7 @@ def quantize_pack_ref(kind: str, x_bits: np.ndarray, rot: np.ndarray, clip, dst_
         yc_h, mn_h, mx_h, r3_h, cd_h, sc_h, zr_h = ([] for _ in range(7))
         for g in range(n_kv):
             y = rotate_round_f32(x_bits[ss, g, :], rot[g])
-            codes, s16, z16, info = quantize_group(y, tau)
+            codes, s16, z16, info = quantize(y, tau)
             codes_pool[page[:, None], g, pos] = pack_codes_row(codes)
             sz_pool[page, g, off, 0] = s16
             sz_pool[page, g, off, 1] = z16

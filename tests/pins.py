@@ -228,8 +228,13 @@ def _write_pages_bruteforce(codes, scale, zero, slots, n_pages, d, nkv):
     return kc, vc, ks, vs
 
 
+# Dequantised level of each 2-bit code, per codebook (the Lloyd-Max levels are
+# +-0.4528 and +-1.5104 deviations of a Gaussian in the ratio 3 : 10)
+CODE_LEVELS = {"uniform": (0.0, 1.0, 2.0, 3.0), "lloyd_max": (-10.0, -3.0, 3.0, 10.0)}
+
+
 def make_small_cache(seed=7, B=2, Hq=6, nkv=3, d=32, sink=(5, 0), hist=(70, 9), recent=(3, 11),
-                     sink_cap=6, recent_cap=12, rot="orth"):
+                     sink_cap=6, recent_cap=12, rot="orth", codebook="uniform"):
     """A small three-segment cache with directly drawn codes and fp16
     scale/zero (no quantisation step).  Returns (cfg, pools, truth) where truth
     holds the materialised float64 K/V of every (b, g) in context order."""
@@ -271,6 +276,9 @@ def make_small_cache(seed=7, B=2, Hq=6, nkv=3, d=32, sink=(5, 0), hist=(70, 9), 
                sink_len=np.array(sink, np.int32), recent_len=np.array(recent, np.int32),
                hist_len=np.array(hist, np.int32), block_table=table, r_k=rk, r_v=rv,
                sm_scale=np.float32(1 / np.sqrt(d)))
+    if codebook != "uniform":
+        cfg["codebook"] = codebook
+    lv = np.array(CODE_LEVELS[codebook])
     # truth: dequantised rotated history, inverse-rotated with R^T (row vectors)
     truth = {}
     off = 0
@@ -278,8 +286,8 @@ def make_small_cache(seed=7, B=2, Hq=6, nkv=3, d=32, sink=(5, 0), hist=(70, 9), 
         sl = slice(off, off + hist[b])
         off += hist[b]
         for g in range(nkv):
-            xk = zk[sl, g].astype(np.float64)[:, None] + ck[sl, g].astype(np.float64) * sk[sl, g].astype(np.float64)[:, None]
-            xv = zv[sl, g].astype(np.float64)[:, None] + cv[sl, g].astype(np.float64) * sv[sl, g].astype(np.float64)[:, None]
+            xk = zk[sl, g].astype(np.float64)[:, None] + lv[ck[sl, g]] * sk[sl, g].astype(np.float64)[:, None]
+            xv = zv[sl, g].astype(np.float64)[:, None] + lv[cv[sl, g]] * sv[sl, g].astype(np.float64)[:, None]
             K = np.concatenate([synth.bf16_bits_to_f32(cfg["sink_k"][b, g, :sink[b]]).astype(np.float64),
                                 xk @ rk[g].astype(np.float64).T,
                                 synth.bf16_bits_to_f32(cfg["recent_k"][b, g, :recent[b]]).astype(np.float64)])
