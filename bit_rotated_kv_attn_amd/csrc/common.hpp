@@ -41,6 +41,30 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Lloyd-Max codebook (oscar.h): levels (-10, -3, 3, 10) in scale units, the
+// scale per unit of deviation and the decision thresholds between the levels
+constexpr double kLmUnit = 0.15104;
+constexpr float kLmThreshold = 6.5f;
+
+// fp16 (scale, zero) of a Lloyd-Max group from its fp64 sum and sum of
+// squared deviations over n values: zero = fp16(fp32(mean)), scale =
+// fp16(fp32(kLmUnit * deviation))
+__device__ __forceinline__ void lm_scale_zero(double mean, double sq, int n, __half& sh, __half& zh) {
+  zh = __float2half_rn((float)mean);
+  sh = __float2half_rn((float)(kLmUnit * sqrt(sq / n)));
+}
+
+// Lloyd-Max code: the number of thresholds fp32(z + s*t), t in (-6.5, 0, 6.5), that y reaches
+__device__ __forceinline__ uint32_t lm_code(float y, float z, float s) {
+  return (uint32_t)(y >= fmaf(s, -kLmThreshold, z)) + (uint32_t)(y >= z) + (uint32_t)(y >= fmaf(s, kLmThreshold, z));
+}
+
 // exp2 that maps a -inf difference to 0 (empty partials carry m = -inf)
 __device__ __forceinline__ float exp2_or_zero(float m, float ref) {
   return (m == -INFINITY) ? 0.0f : exp2f(m - ref);

@@ -60,6 +60,7 @@ struct DecodeDev {
   // shared-prefix packing (G = 4 only): the first n_pref splits lie inside the
   // prefix and are read once for each of the `pairs` request pairs (2i, 2i+1)
   int n_pref, pairs;
+  int lm;   // the pools hold Lloyd-Max codes (oscar.h OSCAR_CODEBOOK_LLOYD_MAX)
   float sm_log2;
   int64_t n_pages;
   const uint16_t *q, *sink_k, *sink_v, *recent_k, *recent_v;
@@ -143,6 +144,25 @@ __device__ __forceinline__ int code_mask(uint32_t w, int p) {
 
 __device__ __forceinline__ float code_scale_inv(int p) {  // 1 / (x1, x4, x16, x16)
   return p == 0 ? 1.0f : p == 1 ? 0.25f : 0.0625f;
+}
+
+// Lloyd-Max levels (-10, -3, 3, 10) as the int8 bytes of one word, indexed by the code
+constexpr uint32_t kLmLevels = 0x0A03FDF6u;
+
+// MFMA operand p of a raw code word: the uniform codebook masks field p in
+// place (x1, x4, x16, x16); the Lloyd-Max one moves field p to the low bits of
+// each byte and replaces the code by its level with a byte permute
+template <bool LM>
+__device__ __forceinline__ int code_operand(uint32_t w, int p) {
+  if constexpr (LM) return (int)__builtin_amdgcn_perm(kLmLevels, kLmLevels, (w >> (2 * p)) & kMask0);
+  else return code_mask(w, p);
+}
+
+// factor that undoes operand p's in-place weight
+template <bool LM>
+__device__ __forceinline__ float code_scale(int p) {
+  if constexpr (LM) return 1.0f;
+  else return code_scale_inv(p);
 }
 
 // fp32 value of a 4-digit (base 256, balanced) integer held in one MFMA result
@@ -580,7 +600,7 @@ __device__ __forceinline__ void load_pair_operands(const DecodeDev& p, int b, in
 // holds the page id of page pg_begin + lane, and qo the QK operands; both were
 // loaded by the caller together with the history length, and this wave's
 // vector loads have completed.
-template <int D, int G>
+template <int D, int G, bool LM>
 __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begin, int count, int hl, int pid_lane,
                                           const HistOperands<D, G>& qo, uint8_t* ring, float* mw, bool& poison,
                                           int lane) {
@@ -705,7 +725,8 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
           const uint32_t w = kword[tb * NCH + c];
-          const v4i bop = v4i{code_mask(w, 0), code_mask(w, 1), code_mask(w, 2), code_mask(w, 3)};
+          const v4i bop = v4i{code_operand<LM>(w, 0), code_operand<LM>(w, 1), code_operand<LM>(w, 2),
+                              code_operand<LM>(w, 3)};
           dq = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[nb][c], bop, c == 0 ? v4i{0, 0, 0, 0} : dq, 0, 0, 0);
         }
         // digits: d0 + 2^8 d1 and d2 + 2^8 d3 are exact in int32
@@ -746,7 +767,7 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
           const float alpha = exp2f(-delta);
 #pragma unroll
           for (int u = 0; u < NU; ++u) {
-            facc[nb][u] = (facc[nb][u] + digits_to_f32(pv[nb][u]) * (code_scale_inv(u & 3) * kw_inv)) * alpha;
+            facc[nb][u] = (facc[nb][u] + digits_to_f32(pv[nb][u]) * (code_scale<LM>(u & 3) * kw_inv)) * alpha;
             clear_in_place(pv[nb][u]);
           }
           lsum[nb] *= alpha;
@@ -813,7 +834,8 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
         const v4i wa = *reinterpret_cast<const v4i*>(pl + nb * 1024 + 256 * grp + 16 * (n ^ (4 * grp)));
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) {
-          const v4i bop = v4i{code_mask(r[0], pp), code_mask(r[1], pp), code_mask(r[2], pp), code_mask(r[3], pp)};
+          const v4i bop = v4i{code_operand<LM>(r[0], pp), code_operand<LM>(r[1], pp), code_operand<LM>(r[2], pp),
+                              code_operand<LM>(r[3], pp)};
           pv[nb][4 * bs + pp] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa, bop, pv[nb][4 * bs + pp], 0, 0, 0);
         }
       }
@@ -832,7 +854,7 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
     lz[nb][1] = group16_sum(zsum[nb]);
 #pragma unroll
     for (int u = 0; u < NU; ++u)
-      acc[nb][u] = facc[nb][u] + digits_to_f32(pv[nb][u]) * (code_scale_inv(u & 3) * kw_inv);
+      acc[nb][u] = facc[nb][u] + digits_to_f32(pv[nb][u]) * (code_scale<LM>(u & 3) * kw_inv);
   }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -900,7 +922,8 @@ __device__ __forceinline__ void rotate_query_block(const DecodeDev& p, int bh) {
   }
   if (tid < D) {
     const int pp = tid & 3;                     // mask index of channel tid
-    const float scale = kq * (pp == 0 ? 16.0f : pp == 1 ? 4.0f : 1.0f);
+    // the plane factor cancels the operand's in-place weight (Lloyd-Max operands carry none)
+    const float scale = kq * ((pp == 0 || p.lm) ? 16.0f : pp == 1 ? 4.0f : 1.0f);
     const uint32_t U = balanced_digits((uint32_t)(int)rintf(acc * scale));
     const int ib = tid >> 2;                    // code-row byte of channel tid
     const int kb = ib / PLANE, rem = ib % PLANE, c = rem >> 2, bb = rem & 3;
@@ -931,7 +954,7 @@ __global__ __launch_bounds__(kBlock) void prepare_kernel(DecodeDev p, int n_rot,
   id -= n_rot;
   const int64_t nk = dk.n_tok * p.n_kv;
   const DemoteDev& dm = id < nk ? dk : dv;
-  const int kind = id < nk ? OSCAR_KIND_K : OSCAR_KIND_V;
+  const int kind = (id < nk ? OSCAR_KIND_K : OSCAR_KIND_V) | (p.lm ? OSCAR_CODEBOOK_LLOYD_MAX : 0);
   if (id >= nk) id -= (int)nk;
   demote_token_block<D>(kind, dm.x, dm.n_src, dm.tok_stride, dm.head_stride, dm.src_idx, id / p.n_kv, id % p.n_kv,
                         p.n_kv, dm.rot, dm.clip, dm.dst_slot, dm.codes, dm.sz, dm.n_pages);
@@ -943,7 +966,7 @@ __global__ __launch_bounds__(kBlock) void prepare_kernel(DecodeDev p, int n_rot,
 #ifndef OSCAR_SCAN_WAVES_PER_SIMD
 #define OSCAR_SCAN_WAVES_PER_SIMD 2
 #endif
-template <int D, int G>
+template <int D, int G, bool LM>
 __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) void decode_main_kernel(DecodeDev p) {
   constexpr int NB = (G + 3) / 4;
   using RG = Ring<D, NB>;
@@ -1046,7 +1069,7 @@ __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) vo
       const int count =
           __builtin_amdgcn_readfirstlane(poison ? 0 : max(0, min(ws0 + per_wave, pe) - ws0));
       uint8_t* ring = smem + wave * RP::kWaveBytes;
-      hist_wave<D, 8>(p, g, ws0, count, full, pid_lane, qo, ring, reinterpret_cast<float*>(ring), poison, lane);
+      hist_wave<D, 8, LM>(p, g, ws0, count, full, pid_lane, qo, ring, reinterpret_cast<float*>(ring), poison, lane);
       if (lane == 0) flags[wave] = poison ? 1 : 0;
       __syncthreads();
       const size_t rows = (size_t)4 * part_row(D);
@@ -1094,7 +1117,7 @@ __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) vo
   const int count = max(0, min(ws0 + per_wave, pe) - ws0);
   uint8_t* ring = smem + wave * RG::kWaveBytes;
   // the wave's merge slot [G][D+2] = (m, l, acc) overlays its own ring once the scan is done
-  hist_wave<D, G>(p, g, ws0, count, hl, pid_lane, qo, ring, reinterpret_cast<float*>(ring), poison, lane);
+  hist_wave<D, G, LM>(p, g, ws0, count, hl, pid_lane, qo, ring, reinterpret_cast<float*>(ring), poison, lane);
   if (lane == 0) flags[wave] = poison ? 1 : 0;
   __syncthreads();
   combine_block<G, D>(reinterpret_cast<const float*>(smem), RG::kWaveBytes / 4, flags,
@@ -1406,7 +1429,8 @@ void launch_main(const DecodeDev& dv, hipStream_t stream) {
   const long blocks = (long)dv.n_pref * dv.pairs * dv.n_kv + (long)(dv.splits - dv.n_pref) * units +
                       (long)dv.n_pref * (dv.B & 1) * dv.n_kv + units * dv.bf_blocks;
   if (blocks == 0) return;
-  decode_main_kernel<D, G><<<dim3((unsigned)blocks), kBlock, 0, stream>>>(dv);
+  if (dv.lm) decode_main_kernel<D, G, true><<<dim3((unsigned)blocks), kBlock, 0, stream>>>(dv);
+  else decode_main_kernel<D, G, false><<<dim3((unsigned)blocks), kBlock, 0, stream>>>(dv);
 }
 
 template <int D>
@@ -1446,6 +1470,7 @@ DecodeDev make_dev(const oscar_decode_args& a, const DecodePlan& plan, char* ws)
   dv.splits = plan.splits; dv.pps = plan.pages_per_split;
   dv.chunks = plan.chunks; dv.sink_chunks = plan.sink_chunks;
   dv.bf_blocks = plan.chunks;
+  dv.lm = a.codebook == OSCAR_CODEBOOK_LLOYD_MAX ? 1 : 0;
   // pack the splits that lie wholly inside a shared prefix (group size 4, two or more requests)
   dv.pairs = a.batch / 2;
   dv.n_pref = (dv.G == 4 && dv.pairs > 0 && plan.splits > 0) ? std::min(plan.splits, a.shared_pages / plan.pages_per_split)

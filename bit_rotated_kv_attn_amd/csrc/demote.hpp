@@ -2,7 +2,9 @@
 // 256-thread block, shared by oscar_quantize_pack's few-token path and the
 // fused decode step.  Same arithmetic as the tiled kernel: the rotated value is
 // an fp64 dot product rounded once to fp32; zero = fp16(min), scale =
-// fp16((max - min) / 3); code = rint((y - zero) / scale) clamped to [0, 3].
+// fp16((max - min) / 3); code = rint((y - zero) / scale) clamped to [0, 3]
+// (or the Lloyd-Max statistics and thresholds of oscar.h when kind carries
+// OSCAR_CODEBOOK_LLOYD_MAX).
 // Source: the demotion step of the serving pipeline in the myzaker.com article
 // on OSCAR; R and the clip threshold from the gist.science OSCAR technical
 // summary, section 2.2A.
@@ -31,7 +33,10 @@ __device__ __forceinline__ void demote_token_block(int kind, const uint16_t* __r
   __shared__ double parts[P][D];
   __shared__ float ys[D];
   __shared__ float red[2][kBlock / kWave];
+  __shared__ double dred[kBlock / kWave];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const bool lm = (kind & OSCAR_CODEBOOK_LLOYD_MAX) != 0;
+  const bool k_layout = (kind & ~OSCAR_CODEBOOK_LLOYD_MAX) == OSCAR_KIND_K;
   const int64_t src = src_idx ? (int64_t)src_idx[t] : t;
   const int64_t slot = dst_slot[t];
   if (src < 0 || src >= n_src || slot < 0 || slot >= n_pages * kPage) return;   // block-uniform
@@ -80,8 +85,26 @@ __device__ __forceinline__ void demote_token_block(int kind, const uint16_t* __r
     mn = fminf(mn, red[0][w]);
     mx = fmaxf(mx, red[1][w]);
   }
-  const __half zh = __float2half_rn(mn);
-  const __half sh = __float2half_rn(__fdiv_rn(mx - mn, 3.0f));
+  __half zh = __float2half_rn(mn);
+  __half sh = __float2half_rn(__fdiv_rn(mx - mn, 3.0f));
+  if (lm) {   // block-uniform: mean, then the sum of squared deviations, in fp64
+    double v = wave_sum_f64(tid < D ? (double)ys[tid] : 0.0);
+    if (lane == 0) dred[wave] = v;
+    __syncthreads();
+    double tot = 0.0;
+#pragma unroll
+    for (int w = 0; w < kBlock / kWave; ++w) tot += dred[w];
+    const double mean = tot / D;
+    __syncthreads();
+    const double dv = tid < D ? (double)ys[tid] - mean : 0.0;
+    v = wave_sum_f64(__dmul_rn(dv, dv));
+    if (lane == 0) dred[wave] = v;
+    __syncthreads();
+    double sq = 0.0;
+#pragma unroll
+    for (int w = 0; w < kBlock / kWave; ++w) sq += dred[w];
+    lm_scale_zero(mean, sq, D, sh, zh);
+  }
   const float z = __half2float(zh), s = __half2float(sh);
   const int64_t page = slot / kPage;
   const int o = (int)(slot % kPage);
@@ -90,7 +113,10 @@ __device__ __forceinline__ void demote_token_block(int kind, const uint16_t* __r
   if (tid < kRowBytes) {
     const int i = tid;
     uint32_t byte = 0;
-    if (s != 0.0f) {
+    if (lm) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) byte |= lm_code(ys[4 * i + q], z, s) << (2 * q);
+    } else if (s != 0.0f) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float v = rintf(__fdiv_rn(ys[4 * i + q] - z, s));
@@ -99,8 +125,7 @@ __device__ __forceinline__ void demote_token_block(int kind, const uint16_t* __r
       }
     }
     uint8_t* blk = codes + (page * n_kv + g) * (int64_t)(kPage * kRowBytes);
-    const int pos = (kind == OSCAR_KIND_K) ? (i / kPlane) * (kPage * kPlane) + o * kPlane + (i % kPlane)
-                                           : i * kPage + o;
+    const int pos = k_layout ? (i / kPlane) * (kPage * kPlane) + o * kPlane + (i % kPlane) : i * kPage + o;
     blk[pos] = (uint8_t)byte;
   }
 }

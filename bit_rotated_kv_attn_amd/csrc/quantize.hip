@@ -39,6 +39,8 @@ __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(
   const int g = blockIdx.y;
   const int64_t t0 = (int64_t)blockIdx.x * kQTok;
   const int tid = threadIdx.x;
+  const bool lm = (kind & OSCAR_CODEBOOK_LLOYD_MAX) != 0;
+  const bool k_layout = (kind & ~OSCAR_CODEBOOK_LLOYD_MAX) == OSCAR_KIND_K;
 
   if (tid < kQTok) {
     const int64_t t = t0 + tid;
@@ -81,7 +83,8 @@ __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(
   }
   __syncthreads();
 
-  // per-token group statistics: zero = fp16(min), scale = fp16((max - min) / 3)
+  // per-token group statistics: zero = fp16(min), scale = fp16((max - min) / 3),
+  // or the Lloyd-Max mean and deviation (fp64)
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   for (int t = wave; t < kQTok; t += kBlock / kWave) {
     float mn = INFINITY, mx = -INFINITY;
@@ -91,9 +94,20 @@ __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(
     }
     mn = wave_min(mn);
     mx = wave_max(mx);
+    __half z = __float2half_rn(mn);
+    __half s = __float2half_rn(__fdiv_rn(mx - mn, 3.0f));
+    if (lm) {
+      double s1 = 0.0;
+      for (int c = lane; c < D; c += kWave) s1 += (double)ys[t][c];
+      const double mean = wave_sum_f64(s1) / D;
+      double s2 = 0.0;
+      for (int c = lane; c < D; c += kWave) {
+        const double dv = (double)ys[t][c] - mean;
+        s2 = __dadd_rn(s2, __dmul_rn(dv, dv));
+      }
+      lm_scale_zero(mean, wave_sum_f64(s2), D, s, z);
+    }
     if (lane == 0) {
-      const __half z = __float2half_rn(mn);
-      const __half s = __float2half_rn(__fdiv_rn(mx - mn, 3.0f));
       zf[t] = __half2float(z);
       sf[t] = __half2float(s);
       const int64_t slot = dst_s[t];
@@ -114,7 +128,10 @@ __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(
     if (slot < 0) continue;
     const float z = zf[t], s = sf[t];
     uint32_t byte = 0;
-    if (s != 0.0f) {
+    if (lm) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) byte |= lm_code(ys[t][4 * i + q], z, s) << (2 * q);
+    } else if (s != 0.0f) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float v = rintf(__fdiv_rn(ys[t][4 * i + q] - z, s));
@@ -125,8 +142,7 @@ __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(
     const int64_t page = slot / kPage;
     const int o = (int)(slot % kPage);
     uint8_t* blk = codes + (page * n_kv + g) * (int64_t)(kPage * kRowBytes);
-    const int pos = (kind == OSCAR_KIND_K) ? (i / kPlane) * (kPage * kPlane) + o * kPlane + (i % kPlane)
-                                           : i * kPage + o;
+    const int pos = k_layout ? (i / kPlane) * (kPage * kPlane) + o * kPlane + (i % kPlane) : i * kPage + o;
     blk[pos] = (uint8_t)byte;
   }
 }

@@ -68,6 +68,22 @@ typedef enum oscar_status {
 
 typedef enum oscar_kind { OSCAR_KIND_K = 0, OSCAR_KIND_V = 1 } oscar_kind;
 
+/* INT2 codebooks: how a 2-bit code c of a (token, head) group dequantises with
+ * the group's fp16 (scale, zero), and how the demotion chooses them.
+ *  UNIFORM    zero + c*scale; zero = fp16(min), scale = fp16((max - min)/3),
+ *             c = rint((y - zero)/scale) clamped to [0, 3] (the pages' scale /
+ *             zero-point quantiser).
+ *  LLOYD_MAX  zero + L[c]*scale, L = (-10, -3, 3, 10): the 4-level quantiser
+ *             with the least mean squared error for a Gaussian (levels at
+ *             +-0.4528 and +-1.5104 deviations, here in the ratio 3:10), which
+ *             the OSCAR authors pair with the rotation.  zero = fp16(fp32(mean)),
+ *             scale = fp16(fp32(0.15104 * deviation)), mean and population
+ *             deviation of the clipped group in fp64; c = the number of
+ *             thresholds fp32(zero + scale*t), t in (-6.5, 0, 6.5), that y reaches.
+ * The pools of a layer hold one codebook; demotion and decode must agree. */
+#define OSCAR_CODEBOOK_UNIFORM 0
+#define OSCAR_CODEBOOK_LLOYD_MAX 0x100
+
 /* ABI version of the loaded library (OSCAR_ABI_VERSION). */
 OSCAR_API int oscar_abi_version(void);
 
@@ -86,7 +102,8 @@ OSCAR_API const char* oscar_status_str(int status);
  *   even, all codes 0 when scale is 0; pack 4 codes per byte; write the code
  *   row and (scale, zero) into slot dst_slot = page*64 + offset.
  *
- *  kind          OSCAR_KIND_K or OSCAR_KIND_V (selects the in-page layout)
+ *  kind          OSCAR_KIND_K or OSCAR_KIND_V (selects the in-page layout),
+ *                optionally OR'ed with OSCAR_CODEBOOK_LLOYD_MAX
  *  x             bf16; element (token s, head g, channel c) is at
  *                x[s*x_tok_stride + g*x_head_stride + c]; the caller
  *                guarantees that address is valid for every s in [0, n_src)
@@ -163,6 +180,9 @@ typedef struct oscar_decode_args {
                                For each pair the scan checks the pages it reads for both:
                                if the two rows' ids differ there, or either history ends
                                before them, both requests' output rows are NaN.        */
+  int32_t codebook;         /* OSCAR_CODEBOOK_UNIFORM or OSCAR_CODEBOOK_LLOYD_MAX: the
+                               codebook the pools were demoted with (a decode step also
+                               demotes with it)                                        */
 } oscar_decode_args;
 
 /* Workspace bytes oscar_decode_attn needs for these sizes (0 on invalid sizes).

@@ -38,15 +38,21 @@ def empty_pools(n_pages: int, n_kv: int, d: int, device="cuda"):
     return codes, sz
 
 
+# codebook name (oracle, cfg["codebook"]) -> the C ABI flag
+CODEBOOK_FLAG = {"uniform": hip.CODEBOOK_UNIFORM, "lloyd_max": hip.CODEBOOK_LLOYD_MAX}
+
+
 def oracle_pools(cfg: dict):
-    """K/V pools of a decode config filled by the oracle quantiser."""
+    """K/V pools of a decode config filled by the oracle quantiser (with the
+    config's codebook, uniform by default)."""
+    cb = cfg.get("codebook", "uniform")
     d, nkv, P = cfg["head_dim"], cfg["n_kv"], cfg["n_pages"]
     kc = np.zeros((P, nkv, PAGE * d // 4), np.uint8)
     vc = np.zeros_like(kc)
     ks = np.zeros((P, nkv, PAGE, 2), np.uint16)
     vs = np.zeros_like(ks)
-    oracle.quantize_pack_ref("k", cfg["hist_k"], cfg["r_k"], cfg["tau_k"], cfg["hist_slot"], kc, ks)
-    oracle.quantize_pack_ref("v", cfg["hist_v"], cfg["r_v"], cfg["tau_v"], cfg["hist_slot"], vc, vs)
+    oracle.quantize_pack_ref("k", cfg["hist_k"], cfg["r_k"], cfg["tau_k"], cfg["hist_slot"], kc, ks, codebook=cb)
+    oracle.quantize_pack_ref("v", cfg["hist_v"], cfg["r_v"], cfg["tau_v"], cfg["hist_slot"], vc, vs, codebook=cb)
     return kc, vc, ks, vs
 
 
@@ -68,7 +74,8 @@ def gpu_decode(cfg: dict, pools, *, block_table=None, hist_len=None, sink_len=No
                 recent_len=dev(cfg["recent_len"] if recent_len is None else recent_len),
                 hist_len=dev(hl), max_hist_len=mh, k_codes=kc, v_codes=vc, k_sz=ks, v_sz=vs,
                 block_table=dev(table), r_k=dev(cfg["r_k"]), r_v=dev(cfg["r_v"]), out=out, workspace=ws,
-                sm_scale=float(cfg["sm_scale"]), shared_pages=shared_pages)
+                sm_scale=float(cfg["sm_scale"]), shared_pages=shared_pages,
+                codebook=CODEBOOK_FLAG[cfg.get("codebook", "uniform")])
     for _ in range(reps):
         hip.oscar_decode_attn(**args)
     torch.cuda.synchronize()
@@ -76,10 +83,11 @@ def gpu_decode(cfg: dict, pools, *, block_table=None, hist_len=None, sink_len=No
 
 
 def gpu_quantize(kind: str, x: np.ndarray, rot: np.ndarray, clip, dst_slot: np.ndarray, n_pages: int,
-                 src_idx=None, pools=None):
+                 src_idx=None, pools=None, codebook: str = "uniform"):
     n_kv, d = rot.shape[0], rot.shape[-1]
     codes, sz = pools if pools is not None else empty_pools(n_pages, n_kv, d)
-    hip.oscar_quantize_pack(hip.KIND_K if kind == "k" else hip.KIND_V, dev(x), dev(rot), float(clip),
+    hip.oscar_quantize_pack((hip.KIND_K if kind == "k" else hip.KIND_V) | CODEBOOK_FLAG[codebook], dev(x), dev(rot),
+                            float(clip),
                             dev(dst_slot.astype(np.int32)), codes, sz,
                             src_idx=None if src_idx is None else dev(src_idx.astype(np.int32)))
     torch.cuda.synchronize()
@@ -96,7 +104,8 @@ def compare_out(got: np.ndarray, ref: np.ndarray, max_abs=MAX_ABS, rel_l2=REL_L2
     return ma, rl
 
 
-def compare_quant(kind: str, gpu_codes, gpu_sz, ref_codes, ref_sz, diag, d: int, exact: bool = False):
+def compare_quant(kind: str, gpu_codes, gpu_sz, ref_codes, ref_sz, diag, d: int, exact: bool = False,
+                  codebook: str = "uniform"):
     """Quantiser parity: scale/zero bit-exact; code bytes bit-exact except
     codes that differ by one level where the oracle's rotated value lies
     within BIN_EDGE_REL (relative) of the bin edge between them.  Bytes and
@@ -123,7 +132,10 @@ def compare_quant(kind: str, gpu_codes, gpu_sz, ref_codes, ref_sz, diag, d: int,
             assert abs(a - b) == 1, f"code differs by more than one level (token {t}, head {g}, ch {c})"
             z = float(np.array(diag["zero16"][t, g]).view(np.float16))
             s = float(np.array(diag["scale16"][t, g]).view(np.float16))
-            e = z + (min(a, b) + 0.5) * s
+            if codebook == "uniform":
+                e = z + (min(a, b) + 0.5) * s
+            else:   # the threshold between Lloyd-Max codes a and b
+                e = float(np.float32(z + s * oracle.LM_THRESHOLDS[min(a, b)]))
             y = float(diag["yc"][t, g, c])
             assert abs(y - e) <= BIN_EDGE_REL * max(abs(e), s), f"code mismatch away from a bin edge ({y} vs {e})"
             n_bad += 1
