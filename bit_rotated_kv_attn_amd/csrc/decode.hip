@@ -15,7 +15,8 @@
 //
 // History scan on the matrix cores, in exact integer arithmetic
 // (v_mfma_i32_16x16x64_i8): the 2-bit codes become int8 operands by masking
-// (no conversion), the rotated query and the softmax weights become 30-bit
+// (no conversion; with the Lloyd-Max codebook a byte permute maps each code to
+// its int8 level, and c reads L[c] above), the rotated query and the softmax weights become 30-bit
 // fixed-point integers split into four balanced 8-bit digits, one MFMA row per
 // (head, digit), so 4 heads fill the 16 rows.  Products and sums are exact;
 // the only roundings are the fixed-point conversions (a query element to
@@ -28,11 +29,13 @@
 //   1. prepare_kernel       q_rot = q R_K[g] per query head -> MFMA digit
 //                           operands; in a decode step also the step's K / V
 //                           demotions
-//   2. decode_main_kernel   one grid: INT2 history splits, then the BF16
-//                           sink / recent chunks; each block writes an
-//                           (m, l, acc) partial per head
+//   2. decode_main_kernel   one grid: INT2 history splits (those inside a
+//                           declared shared prefix read once per request
+//                           pair), then the BF16 sink / recent chunks; each
+//                           block writes an (m, l, acc) partial per head
 //   3. merge_kernel         LSE merge of the history partials, * R_V^T, LSE merge
-//                           with the BF16 partials, normalise
+//      (merge_unit_kernel)  with the BF16 partials, normalise (one block per
+//                           head, or per (request, KV head) in large batches)
 // Softmax state uses base-2 exponents (logits pre-scaled by log2 e).
 #include "common.hpp"
 #include "demote.hpp"
@@ -961,7 +964,7 @@ __global__ __launch_bounds__(kBlock) void prepare_kernel(DecodeDev p, int n_rot,
 }
 
 // ---------------------------------------------------------------------------
-// 2. scan: BF16 chunk blocks first (4 chunks per block), then history splits
+// 2. scan: history splits, then one BF16 block per 64-token sink / recent chunk
 // ---------------------------------------------------------------------------
 #ifndef OSCAR_SCAN_WAVES_PER_SIMD
 #define OSCAR_SCAN_WAVES_PER_SIMD 2
