@@ -38,7 +38,8 @@
  *      scale/zero: fp16 pairs (scale, zero) per token: [64][2].
  *    Pools: codes uint8 [n_pages][n_kv][64*d/4]; scale_zero uint16
  *    [n_pages][n_kv][64][2].  A K pool and a V pool are separate buffers.
- *  - Dequantisation of a code c is zero + c*scale (rotated space).
+ *  - Dequantisation of a code c is zero + c*scale (rotated space) with the
+ *    default codebook, zero + L[c]*scale with the Lloyd-Max one (below).
  */
 #ifndef OSCAR_H
 #define OSCAR_H
@@ -75,8 +76,9 @@ typedef enum oscar_kind { OSCAR_KIND_K = 0, OSCAR_KIND_V = 1 } oscar_kind;
  *             zero-point quantiser).
  *  LLOYD_MAX  zero + L[c]*scale, L = (-10, -3, 3, 10): the 4-level quantiser
  *             with the least mean squared error for a Gaussian (levels at
- *             +-0.4528 and +-1.5104 deviations, here in the ratio 3:10), which
- *             the OSCAR authors pair with the rotation.  zero = fp16(fp32(mean)),
+ *             +-0.4528 and +-1.5104 deviations, here in the ratio 3:10).  The
+ *             gist.science summary says the authors' code pairs a Lloyd-Max
+ *             codebook with the rotation and gives no levels.  zero = fp16(fp32(mean)),
  *             scale = fp16(fp32(0.15104 * deviation)), mean and population
  *             deviation of the clipped group in fp64; c = the number of
  *             thresholds fp32(zero + scale*t), t in (-6.5, 0, 6.5), that y reaches.
@@ -99,7 +101,8 @@ OSCAR_API const char* oscar_status_str(int status);
  *   over the d channels of each (token, head): zero = fp16(min y_c),
  *   scale = fp16((max y_c - min y_c) / 3) (fp32 subtract and divide);
  *   code = clamp(rint((y_c - zero) / scale), 0, 3) in fp32, round half to
- *   even, all codes 0 when scale is 0; pack 4 codes per byte; write the code
+ *   even, all codes 0 when scale is 0 (the Lloyd-Max codebook replaces these
+ *   three steps with its own, above); pack 4 codes per byte; write the code
  *   row and (scale, zero) into slot dst_slot = page*64 + offset.
  *
  *  kind          OSCAR_KIND_K or OSCAR_KIND_V (selects the in-page layout),
@@ -207,6 +210,8 @@ OSCAR_API oscar_status oscar_decode_attn(const oscar_decode_args* args, void* wo
  *                              tiles; one online-softmax partial per split/tile
  *   oscar_decode_merge         log-sum-exp merge of the history partials, times
  *                              R_V^T, merge with the BF16 partials, normalise
+ *                              (one block per query head, or per (request, KV
+ *                              head) when each head has at most 16 partials)
  * Same validation and status codes as oscar_decode_attn.
  */
 OSCAR_API oscar_status oscar_decode_rotate_query(const oscar_decode_args* args, void* workspace,
@@ -218,7 +223,8 @@ OSCAR_API oscar_status oscar_decode_merge(const oscar_decode_args* args, void* w
 
 /*
  * One tensor's demotion inside a decode step: the arguments of
- * oscar_quantize_pack except kind, n_kv and head_dim (taken from the step).
+ * oscar_quantize_pack except kind, n_kv and head_dim (taken from the step:
+ * demote_k is K and demote_v is V, both with the step's args->codebook).
  * n_tok in [0, 2^24 / n_kv]; the other rules are those of oscar_quantize_pack.
  */
 typedef struct oscar_demote_args {
