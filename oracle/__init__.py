@@ -36,7 +36,7 @@ Page sources, cited by title and section:
 Parity status of each function is given in its docstring.  Every public
 function is pinned by ``tests/test_oracle_*.py``.
 """
-from .quant import (PAGE, UNIFORM, LLOYD_MAX, LM_LEVELS, LM_THRESHOLDS, LM_UNIT, code_levels, bf16_to_f64,
+from .quant import (PAGE, quantize_rows_grouped, UNIFORM, LLOYD_MAX, LM_LEVELS, LM_THRESHOLDS, LM_UNIT, code_levels, bf16_to_f64,
                     f16_bits_to_f64, rotate_round_f32, quantize_group, quantize_group_lloyd_max,
                     pack_codes_row, unpack_codes_row, k_byte_offsets, v_byte_offsets,
                     quantize_pack_ref, read_history_codes, page_block_bytes)
@@ -44,7 +44,7 @@ from .attention import (attn_plain, attn_partial, merge_partials, dequant_histor
                         decode_attn_ref, bf16_paged_attn_ref)
 
 __all__ = [
-    "PAGE", "UNIFORM", "LLOYD_MAX", "LM_LEVELS", "LM_THRESHOLDS", "LM_UNIT", "code_levels",
+    "PAGE", "quantize_rows_grouped", "UNIFORM", "LLOYD_MAX", "LM_LEVELS", "LM_THRESHOLDS", "LM_UNIT", "code_levels",
     "bf16_to_f64", "f16_bits_to_f64", "rotate_round_f32", "quantize_group", "quantize_group_lloyd_max",
     "pack_codes_row", "unpack_codes_row", "k_byte_offsets", "v_byte_offsets",
     "quantize_pack_ref", "read_history_codes", "page_block_bytes",

@@ -70,7 +70,9 @@ def dequant_history(kind: str, codes_pool, sz_pool, table_row, hist_len: int, g:
                     n_pages: int | None = None, codebook: str = UNIFORM) -> np.ndarray:
     """Dequantised, still-rotated history vectors x_hat = zero + level(code) *
     scale (float64 [hist_len, d]) of KV head g, in history order; level(c) = c
-    for the uniform codebook, LM_LEVELS[c] for the Lloyd-Max one.  History
+    for the uniform codebook, LM_LEVELS[c] for the Lloyd-Max one; scale and
+    zero are those of the channel's group (one group per head unless the
+    scale/zero pool holds more).  History
     token t is in page table_row[t // 64] at offset t % 64."""
     t = np.arange(hist_len)
     pages = np.asarray(table_row, dtype=np.int64)[t // PAGE]
@@ -78,7 +80,11 @@ def dequant_history(kind: str, codes_pool, sz_pool, table_row, hist_len: int, g:
     if hist_len and (pages.min() < 0 or pages.max() >= n_pages):
         raise ValueError("block table entry outside the page pool")
     codes, s16, z16 = read_history_codes(kind, codes_pool, sz_pool, pages, t % PAGE, g, d)
-    return f16_bits_to_f64(z16)[:, None] + code_levels(codebook)[codes] * f16_bits_to_f64(s16)[:, None]
+    ng = sz_pool.shape[2] // PAGE
+    z, s = f16_bits_to_f64(z16).reshape(hist_len, ng), f16_bits_to_f64(s16).reshape(hist_len, ng)
+    # channel c belongs to group c // (d / ng)
+    z, s = np.repeat(z, d // ng, axis=1), np.repeat(s, d // ng, axis=1)
+    return z + code_levels(codebook)[codes] * s
 
 
 def decode_attn_ref(cfg: dict, k_codes, v_codes, k_sz, v_sz, block_table=None, hist_len=None,

@@ -10,7 +10,10 @@ one [ZAKER] names for dequantisation.
 Readings where the pages leave the step open:
 
 * rotation convention: row vectors, y = x R;
-* quantisation group: the d channels of one (token, KV head);
+* quantisation group: the d channels of one (token, KV head); the sub-head
+  variant splits them into consecutive groups of g channels (g = 64 at
+  d = 128), each with its own (scale, zero), which is where the bit-reversal
+  permutation of [GIST] 2.2A balances the groups;
 * clipping: symmetric clamp to [-tau, tau] before the group min/max;
 * quantiser: asymmetric min-max with zero = fp16(min) and
   scale = fp16((max - min) / 3), code = clamp(rint((y - zero) / scale), 0, 3),
@@ -32,7 +35,8 @@ Readings where the pages leave the step open:
 * in-page layout (64-token pages, one block per (page, KV head)):
   K codes are 4 planes; plane p holds bytes [p*d/16, (p+1)*d/16) of every
   token's row, token-major.  V codes are byte-column-major: byte i of token o
-  sits at i*64 + o.  scale/zero are fp16 pairs (scale, zero) per token.
+  sits at i*64 + o.  scale/zero are fp16 pairs (scale, zero) per token; with
+  n groups per head they are group-planar: group j of token o at j*64 + o.
 """
 from __future__ import annotations
 
@@ -160,9 +164,21 @@ def _offsets(kind: str, offset, d: int):
     raise ValueError("kind must be 'k' or 'v'")
 
 
+def quantize_rows_grouped(quantize, y: np.ndarray, clip, group: int):
+    """Quantise each consecutive block of ``group`` channels of every row of y
+    [n, d] as its own group.  Returns codes [n, d] and fp16 bits [n, d/group]
+    of scale and zero, and info with the per-group fields reshaped to [n, ng]
+    (yc stays [n, d])."""
+    n, d = y.shape
+    ng = d // group
+    codes, s16, z16, info = quantize(np.ascontiguousarray(y).reshape(n * ng, group), clip)
+    info = {k: (v.reshape(n, d) if k == "yc" else v.reshape(n, ng)) for k, v in info.items()}
+    return codes.reshape(n, d), s16.reshape(n, ng), z16.reshape(n, ng), info
+
+
 def quantize_pack_ref(kind: str, x_bits: np.ndarray, rot: np.ndarray, clip, dst_slot: np.ndarray,
                       codes_pool: np.ndarray, sz_pool: np.ndarray, src_idx: np.ndarray | None = None,
-                      chunk: int = 16384, codebook: str = UNIFORM):
+                      chunk: int = 16384, codebook: str = UNIFORM, group: int | None = None):
     """Demote tokens of one tensor (K or V) of one layer into INT2 pages, in place.
 
     x_bits   bf16 [n_src][n_kv][d]
@@ -172,8 +188,9 @@ def quantize_pack_ref(kind: str, x_bits: np.ndarray, rot: np.ndarray, clip, dst_
              [0, n_pages*64) are skipped
     src_idx  int32 [n_tok] rows of x, or None for rows 0..n_tok-1; rows
              outside [0, n_src) are skipped
-    codes_pool uint8 [n_pages][n_kv][64*d/4]; sz_pool uint16 [n_pages][n_kv][64][2]
+    codes_pool uint8 [n_pages][n_kv][64*d/4]; sz_pool uint16 [n_pages][n_kv][64*d/group][2]
     codebook "uniform" (min-max) or "lloyd_max"
+    group    channels per quantisation group (None: the whole head)
 
     Returns a dict of per-(token, head) diagnostics for the written tokens
     (arrays [n_written][n_kv]...) used by the parity checker."""
@@ -185,6 +202,10 @@ def quantize_pack_ref(kind: str, x_bits: np.ndarray, rot: np.ndarray, clip, dst_
     if d % 16:
         raise ValueError("head_dim must be a multiple of 16")
     quantize = {UNIFORM: quantize_group, LLOYD_MAX: quantize_group_lloyd_max}[codebook]
+    group = d if group is None else int(group)
+    if group < 1 or d % group or sz_pool.shape[2] != PAGE * (d // group):
+        raise ValueError("group must divide head_dim, and sz_pool hold 64 * head_dim/group pairs per head")
+    ng = d // group
     n_pages = codes_pool.shape[0]
     dst = np.asarray(dst_slot, dtype=np.int64).ravel()
     src = np.arange(dst.size) if src_idx is None else np.asarray(src_idx, dtype=np.int64).ravel()
@@ -200,10 +221,14 @@ def quantize_pack_ref(kind: str, x_bits: np.ndarray, rot: np.ndarray, clip, dst_
         yc_h, mn_h, mx_h, r3_h, cd_h, sc_h, zr_h = ([] for _ in range(7))
         for g in range(n_kv):
             y = rotate_round_f32(x_bits[ss, g, :], rot[g])
-            codes, s16, z16, info = quantize(y, tau)
+            codes, s16, z16, info = quantize_rows_grouped(quantize, y, tau, group)
             codes_pool[page[:, None], g, pos] = pack_codes_row(codes)
-            sz_pool[page, g, off, 0] = s16
-            sz_pool[page, g, off, 1] = z16
+            for j in range(ng):
+                sz_pool[page, g, j * PAGE + off, 0] = s16[:, j]
+                sz_pool[page, g, j * PAGE + off, 1] = z16[:, j]
+            if ng == 1:   # one group per head: per-token diagnostics
+                s16, z16 = s16[:, 0], z16[:, 0]
+                info = {k: (v if k == "yc" else v[:, 0]) for k, v in info.items()}
             yc_h.append(info["yc"]); mn_h.append(info["mn"]); mx_h.append(info["mx"])
             r3_h.append(info["range3"]); cd_h.append(codes); sc_h.append(s16); zr_h.append(z16)
         diag["slot"].append(dd)
@@ -216,8 +241,15 @@ def quantize_pack_ref(kind: str, x_bits: np.ndarray, rot: np.ndarray, clip, dst_
 
 def read_history_codes(kind: str, codes_pool: np.ndarray, sz_pool: np.ndarray, pages: np.ndarray,
                        offsets: np.ndarray, g: int, d: int):
-    """Codes [n][d] and fp16 (scale, zero) bits [n] of the tokens at the given
-    (physical page, offset) pairs of KV head g."""
+    """Codes [n][d] and fp16 (scale, zero) bits [n][ng] of the tokens at the
+    given (physical page, offset) pairs of KV head g (ng groups per head, from
+    the pool's shape; [n] when ng = 1)."""
     pos = _offsets(kind, offsets, d)
     rows = codes_pool[np.asarray(pages)[:, None], g, pos]
-    return unpack_codes_row(rows), sz_pool[pages, g, offsets, 0], sz_pool[pages, g, offsets, 1]
+    ng = sz_pool.shape[2] // PAGE
+    pages, offsets = np.asarray(pages), np.asarray(offsets)
+    idx = offsets[:, None] + PAGE * np.arange(ng)[None, :]
+    s16, z16 = sz_pool[pages[:, None], g, idx, 0], sz_pool[pages[:, None], g, idx, 1]
+    if ng == 1:
+        s16, z16 = s16[:, 0], z16[:, 0]
+    return unpack_codes_row(rows), s16, z16

@@ -210,10 +210,13 @@ def check_quantize_pack_slots(seed: int = 6):
 # decode pins
 # --------------------------------------------------------------------------
 def _write_pages_bruteforce(codes, scale, zero, slots, n_pages, d, nkv):
-    """Place codes [n][nkv][d] into K and V pools bit by bit (pure loops)."""
+    """Place codes [n][nkv][d] into K and V pools bit by bit (pure loops).
+    scale / zero are [n][nkv] (one group per head) or [n][nkv][ng] (group j
+    of token o stored at j*64 + o)."""
+    ng = 1 if scale[0].ndim == 2 else scale[0].shape[2]
     kc = np.zeros((n_pages, nkv, PAGE * d // 4), np.uint8)
     vc = np.zeros_like(kc)
-    ks = np.zeros((n_pages, nkv, PAGE, 2), np.uint16)
+    ks = np.zeros((n_pages, nkv, PAGE * ng, 2), np.uint16)
     vs = np.zeros_like(ks)
     w = d // 16
     for t, slot in enumerate(slots):
@@ -223,8 +226,10 @@ def _write_pages_bruteforce(codes, scale, zero, slots, n_pages, d, nkv):
                 i, j = divmod(c, 4)
                 kc[p, g, (i // w) * PAGE * w + o * w + i % w] |= np.uint8(int(codes[0][t, g, c]) << (2 * j))
                 vc[p, g, i * PAGE + o] |= np.uint8(int(codes[1][t, g, c]) << (2 * j))
-            ks[p, g, o] = (scale[0][t, g], zero[0][t, g])
-            vs[p, g, o] = (scale[1][t, g], zero[1][t, g])
+            for j in range(ng):
+                pick = (lambda a: a[t, g]) if ng == 1 else (lambda a: a[t, g, j])
+                ks[p, g, j * PAGE + o] = (pick(scale[0]), pick(zero[0]))
+                vs[p, g, j * PAGE + o] = (pick(scale[1]), pick(zero[1]))
     return kc, vc, ks, vs
 
 
@@ -234,7 +239,7 @@ CODE_LEVELS = {"uniform": (0.0, 1.0, 2.0, 3.0), "lloyd_max": (-10.0, -3.0, 3.0, 
 
 
 def make_small_cache(seed=7, B=2, Hq=6, nkv=3, d=32, sink=(5, 0), hist=(70, 9), recent=(3, 11),
-                     sink_cap=6, recent_cap=12, rot="orth", codebook="uniform"):
+                     sink_cap=6, recent_cap=12, rot="orth", codebook="uniform", groups=1):
     """A small three-segment cache with directly drawn codes and fp16
     scale/zero (no quantisation step).  Returns (cfg, pools, truth) where truth
     holds the materialised float64 K/V of every (b, g) in context order."""
@@ -255,10 +260,11 @@ def make_small_cache(seed=7, B=2, Hq=6, nkv=3, d=32, sink=(5, 0), hist=(70, 9), 
     slots = np.concatenate(slots)
     ck = rng.integers(0, 4, size=(n_hist, nkv, d)).astype(np.uint8)
     cv = rng.integers(0, 4, size=(n_hist, nkv, d)).astype(np.uint8)
-    sk = rng.uniform(0.2, 2.0, size=(n_hist, nkv)).astype(np.float16)
-    zk = rng.uniform(-3.0, -0.5, size=(n_hist, nkv)).astype(np.float16)
-    sv = rng.uniform(0.2, 2.0, size=(n_hist, nkv)).astype(np.float16)
-    zv = rng.uniform(-3.0, -0.5, size=(n_hist, nkv)).astype(np.float16)
+    gshape = (n_hist, nkv) if groups == 1 else (n_hist, nkv, groups)   # one (scale, zero) per group
+    sk = rng.uniform(0.2, 2.0, size=gshape).astype(np.float16)
+    zk = rng.uniform(-3.0, -0.5, size=gshape).astype(np.float16)
+    sv = rng.uniform(0.2, 2.0, size=gshape).astype(np.float16)
+    zv = rng.uniform(-3.0, -0.5, size=gshape).astype(np.float16)
     kc, vc, ks, vs = _write_pages_bruteforce((ck, cv), (sk.view(np.uint16), sv.view(np.uint16)),
                                              (zk.view(np.uint16), zv.view(np.uint16)), slots, n_pages, d, nkv)
     if rot == "orth":
@@ -286,8 +292,10 @@ def make_small_cache(seed=7, B=2, Hq=6, nkv=3, d=32, sink=(5, 0), hist=(70, 9), 
         sl = slice(off, off + hist[b])
         off += hist[b]
         for g in range(nkv):
-            xk = zk[sl, g].astype(np.float64)[:, None] + lv[ck[sl, g]] * sk[sl, g].astype(np.float64)[:, None]
-            xv = zv[sl, g].astype(np.float64)[:, None] + lv[cv[sl, g]] * sv[sl, g].astype(np.float64)[:, None]
+            # the (scale, zero) of each channel: its group's, channel c in group c // (d / groups)
+            per_ch = lambda a: np.repeat(a[sl, g].astype(np.float64).reshape(hist[b], groups), d // groups, axis=1)
+            xk = per_ch(zk) + lv[ck[sl, g]] * per_ch(sk)
+            xv = per_ch(zv) + lv[cv[sl, g]] * per_ch(sv)
             K = np.concatenate([synth.bf16_bits_to_f32(cfg["sink_k"][b, g, :sink[b]]).astype(np.float64),
                                 xk @ rk[g].astype(np.float64).T,
                                 synth.bf16_bits_to_f32(cfg["recent_k"][b, g, :recent[b]]).astype(np.float64)])
@@ -319,6 +327,15 @@ def sdpa_reference(cfg, truth):
 
 def check_decode_vs_sdpa(seed=7, rot="orth"):
     cfg, pools, truth = make_small_cache(seed=seed, rot=rot)
+    out = oracle.decode_attn_ref(cfg, *pools)
+    ref = sdpa_reference(cfg, truth)
+    assert np.abs(out - ref).max() <= 1e-5 * max(1.0, np.abs(ref).max()), np.abs(out - ref).max()
+
+
+def check_decode_vs_sdpa_grouped(seed=9):
+    """Two (scale, zero) groups per head: the dequantisation must take each
+    channel's own group."""
+    cfg, pools, truth = make_small_cache(seed=seed, groups=2)
     out = oracle.decode_attn_ref(cfg, *pools)
     ref = sdpa_reference(cfg, truth)
     assert np.abs(out - ref).max() <= 1e-5 * max(1.0, np.abs(ref).max()), np.abs(out - ref).max()

@@ -43,7 +43,8 @@ QUANT_PINS = [pins.check_quant_closed_forms, pins.check_quant_bruteforce, pins.c
               pins.check_quantize_pack_slots]
 DECODE_PINS = [pins.check_decode_vs_sdpa, pins.check_inverse_rotation_direction,
                pins.check_rotated_space_identity, pins.check_decode_special_cases,
-               pins.check_decode_invariances, pins.check_partition_merge, pins.check_bf16_paged_vs_sdpa]
+               pins.check_decode_invariances, pins.check_partition_merge, pins.check_bf16_paged_vs_sdpa,
+               pins.check_decode_vs_sdpa_grouped]
 
 MUTANTS = [
     # (module, function, anchor, replacement, pins)
@@ -55,8 +56,10 @@ MUTANTS = [
     (oq, "pack_codes_row", "(c[..., 1::4] << 2)", "(c[..., 1::4] << 4)", QUANT_PINS),
     (oq, "k_byte_offsets", "(i // w) * (PAGE * w) + o * w + (i % w)", "o * (d // 4) + i", QUANT_PINS),
     (oq, "v_byte_offsets", "i * PAGE + o", "o * (d // 4) + i", QUANT_PINS),
-    (oatt, "dequant_history", "f16_bits_to_f64(z16)[:, None] + ", "0 * f16_bits_to_f64(z16)[:, None] + ", DECODE_PINS),
+    (oatt, "dequant_history", "return z + code_levels", "return 0 * z + code_levels", DECODE_PINS),
     (oatt, "dequant_history", "t % PAGE, g, d)", "(t + 1) % PAGE, g, d)", DECODE_PINS),
+    (oatt, "dequant_history", "np.repeat(z, d // ng, axis=1), np.repeat(s, d // ng, axis=1)",
+     "np.tile(z, (1, d // ng)), np.tile(s, (1, d // ng))", DECODE_PINS),
     (oatt, "decode_attn_ref", "xk @ Rk.T", "xk @ Rk", DECODE_PINS),
     (oatt, "decode_attn_ref", "xv @ Rv.T", "xv @ Rv", DECODE_PINS),
     (oatt, "decode_attn_ref", "range(g * G, (g + 1) * G)", "range(g, Hq, n_kv)", DECODE_PINS),
