@@ -23,6 +23,8 @@ PAGE = 64
 KIND_K, KIND_V = 0, 1
 # INT2 codebooks (oscar.h); the Lloyd-Max flag is OR'ed into a demotion's kind
 CODEBOOK_UNIFORM, CODEBOOK_LLOYD_MAX = 0, 0x100
+# 64-channel quantisation groups (oscar.h); OR'ed into a demotion's kind
+GROUPS_64 = 0x200
 # arithmetic the kernels of this build compute in (reported by bench.py)
 COMPUTE_DTYPE = "i8 MFMA (exact integer digits) + f32 softmax; f64 rotation in demotion"
 OSCAR_OK, OSCAR_EINVAL, OSCAR_EUNSUPPORTED, OSCAR_EWORKSPACE, OSCAR_EHIP = range(5)
@@ -40,7 +42,7 @@ class DecodeArgs(ctypes.Structure):
                 ("recent_len", _vp), ("hist_len", _vp), ("max_hist_len", _i32), ("k_codes", _vp),
                 ("v_codes", _vp), ("k_sz", _vp), ("v_sz", _vp), ("n_pages", _i64),
                 ("block_table", _vp), ("max_pages", _i32), ("r_k", _vp), ("r_v", _vp), ("out", _vp),
-                ("shared_pages", _i32), ("codebook", _i32)]
+                ("shared_pages", _i32), ("codebook", _i32), ("group_channels", _i32)]
 
 
 class DemoteArgs(ctypes.Structure):
@@ -133,7 +135,7 @@ def oscar_quantize_pack(kind: int, x, rot, clip: float, dst_slot, codes, scale_z
                         n_src=None, x_tok_stride=None, x_head_stride=None, stream=None) -> None:
     """Demote tokens of one tensor into INT2 pages (see oscar_quantize_pack in oscar.h).
 
-    kind: KIND_K or KIND_V, optionally | CODEBOOK_LLOYD_MAX.
+    kind: KIND_K or KIND_V, optionally | CODEBOOK_LLOYD_MAX and / or | GROUPS_64.
 
     x: bf16 bits; by default a contiguous [n_src][n_kv][d] tensor.  For other
     layouts pass n_src, x_tok_stride and x_head_stride (elements).
@@ -147,7 +149,8 @@ def oscar_quantize_pack(kind: int, x, rot, clip: float, dst_slot, codes, scale_z
     n_tok = dst_slot.numel()
     if src_idx is not None and src_idx.numel() != n_tok:
         raise ValueError("src_idx and dst_slot lengths differ")
-    if codes.shape[1:] != (n_kv, PAGE * d // 4) or scale_zero.shape[1:] != (n_kv, PAGE, 2):
+    ng = d // 64 if int(kind) & GROUPS_64 else 1
+    if codes.shape[1:] != (n_kv, PAGE * d // 4) or scale_zero.shape[1:] != (n_kv, PAGE * ng, 2):
         raise ValueError("pool shapes do not match [n_pages][n_kv][...]")
     if dst_slot.dtype.itemsize != 4 or (src_idx is not None and src_idx.dtype.itemsize != 4):
         raise ValueError("dst_slot / src_idx must be int32")
@@ -167,7 +170,8 @@ def oscar_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, max_his
 
 def decode_args(*, q, sink_k, sink_v, recent_k, recent_v, sink_len, recent_len, hist_len, max_hist_len: int,
                 k_codes, v_codes, k_sz, v_sz, block_table, r_k, r_v, out, workspace,
-                sm_scale: float | None = None, shared_pages: int = 0, codebook: int = CODEBOOK_UNIFORM):
+                sm_scale: float | None = None, shared_pages: int = 0, codebook: int = CODEBOOK_UNIFORM,
+                group_channels: int = 0):
     """Marshal tensors into (DecodeArgs, workspace pointer, workspace bytes).
 
     q bf16 [B][Hq][d]; sink_k/v bf16 [B][n_kv][sink_cap][d]; recent_k/v bf16
@@ -175,7 +179,8 @@ def decode_args(*, q, sink_k, sink_v, recent_k, recent_v, sink_len, recent_len, 
     block_table int32 [B][max_pages]; r_k/r_v fp32 [n_kv][d][d]; out fp32
     [B][Hq][d]; workspace uint8 device tensor (size from oscar_decode_workspace_bytes);
     shared_pages: leading history pages every request holds at the same ids (0: none);
-    codebook: CODEBOOK_UNIFORM or CODEBOOK_LLOYD_MAX, as the pools were demoted.
+    codebook: CODEBOOK_UNIFORM or CODEBOOK_LLOYD_MAX, as the pools were demoted;
+    group_channels: 0 (whole-head groups) or 64, as the pools were demoted.
     The tensors must stay alive while the call (or a captured graph) uses them."""
     B, Hq, d = q.shape
     n_kv = sink_k.shape[1]
@@ -192,7 +197,7 @@ def decode_args(*, q, sink_k, sink_v, recent_k, recent_v, sink_len, recent_len, 
                    k_sz=_ptr(k_sz, 2, "k_sz"), v_sz=_ptr(v_sz, 2, "v_sz"), n_pages=k_codes.shape[0],
                    block_table=_ptr(block_table, 4, "block_table"), max_pages=block_table.shape[1],
                    r_k=_ptr(r_k, 4, "r_k"), r_v=_ptr(r_v, 4, "r_v"), out=_ptr(out, 4, "out"),
-                   shared_pages=int(shared_pages), codebook=int(codebook))
+                   shared_pages=int(shared_pages), codebook=int(codebook), group_channels=int(group_channels))
     return a, _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size()
 
 
@@ -237,7 +242,9 @@ def demote_args(*, x, rot, clip: float, dst_slot, codes, scale_zero, src_idx=Non
     n_tok = dst_slot.numel()
     if src_idx is not None and src_idx.numel() != n_tok:
         raise ValueError("src_idx and dst_slot lengths differ")
-    if codes.shape[1:] != (n_kv, PAGE * d // 4) or scale_zero.shape[1:] != (n_kv, PAGE, 2):
+    # the step decides the groups: a whole-head or a 64-channel-group scale/zero pool
+    if codes.shape[1:] != (n_kv, PAGE * d // 4) or scale_zero.shape[1:] not in ((n_kv, PAGE, 2),
+                                                                               (n_kv, PAGE * max(1, d // 64), 2)):
         raise ValueError("pool shapes do not match [n_pages][n_kv][...]")
     if dst_slot.dtype.itemsize != 4 or (src_idx is not None and src_idx.dtype.itemsize != 4):
         raise ValueError("dst_slot / src_idx must be int32")

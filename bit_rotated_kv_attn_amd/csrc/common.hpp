@@ -125,7 +125,7 @@ inline DecodePlan make_decode_plan(int B, int Hq, int n_kv, int d, int max_hist_
   size_t off = 0;
   p.off_qdig = off;  off = align256(off + (size_t)B * n_kv * NB * (d / 64) * 64 * 16);
   p.off_qa = off;    off = align256(off + (size_t)B * Hq * sizeof(float));
-  p.off_qb = off;    off = align256(off + (size_t)B * Hq * sizeof(float));
+  p.off_qb = off;    off = align256(off + (size_t)B * Hq * 2 * sizeof(float));   // per (scale, zero) group
   p.off_hpart = off; off = align256(off + (size_t)B * n_kv * p.splits * part);
   p.off_bpart = off; off = align256(off + (size_t)B * n_kv * p.chunks * part);
   p.total = off;

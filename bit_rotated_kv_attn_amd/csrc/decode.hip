@@ -64,6 +64,7 @@ struct DecodeDev {
   // prefix and are read once for each of the `pairs` request pairs (2i, 2i+1)
   int n_pref, pairs;
   int lm;   // the pools hold Lloyd-Max codes (oscar.h OSCAR_CODEBOOK_LLOYD_MAX)
+  int ng;   // (scale, zero) groups per head: 1, or 2 with 64-channel groups at d = 128
   float sm_log2;
   int64_t n_pages;
   const uint16_t *q, *sink_k, *sink_v, *recent_k, *recent_v;
@@ -73,7 +74,8 @@ struct DecodeDev {
   const float *r_k, *r_v;
   float* out;
   uint8_t* qdig;     // [B][n_kv][NB][D/64][64 lanes][16 bytes] QK A operands
-  float *qa, *qb;    // [B][Hq] logit constants: sm_log2/(16 kq), sm_log2*sum(q_rot)
+  float *qa, *qb;    // logit constants: qa [B][Hq] = sm_log2/(16 kq); qb [B][Hq][2] = sm_log2 * sum(q_rot)
+                     // over the whole head (qb[..][1] = 0), or over channels 0..63 and 64..127
   float *hpart, *bpart;
 };
 
@@ -492,10 +494,10 @@ __device__ __forceinline__ void wait_page(int ahead) {
 // reads (16*l + 1024*c) are free of LDS bank conflicts:
 //   K copy c, lane (q = l/16, n = l%16): plane q, tokens 4n..4n+3, bytes 16c..16c+15
 //   V copy c, lane (q, n): byte column (D/64)*n + c, tokens 16q..16q+15
-template <int D>
-struct Stage {
-  static constexpr int kK = 0, kV = 16 * D, kKsz = 32 * D, kVsz = 32 * D + 256, kBytes = 32 * D + 512;
-  static constexpr int kCopies = 2 * (D / 64) + 2;   // copy instructions per page
+template <int D, int NG>
+struct Stage {   // NG (scale, zero) groups per head, group-planar
+  static constexpr int kK = 0, kV = 16 * D, kKsz = 32 * D, kVsz = 32 * D + 256 * NG, kBytes = 32 * D + 512 * NG;
+  static constexpr int kCopies = 2 * (D / 64) + 2 * NG;   // copy instructions per page
 };
 
 // Lane byte offsets of the copies inside a (page, head) block (see Stage).
@@ -503,28 +505,38 @@ struct StageOffsets {
   uint32_t k, v, sz;
 };
 
-template <int D>
+// V: lane (n, q) of LDS chunk c gets byte column 2n + c (NG = 1: PV column n
+// of a chunk is channels 8n + 4c + field) or 16c + n (NG = 2: the chunk's
+// products cover channels 64c .. 64c + 63 only, one group), tokens 16q..16q+15.
+template <int D, int NG>
 __device__ __forceinline__ StageOffsets stage_offsets(int lane) {
   constexpr int NCH = D / 64, PLANE = D / 16;
   const int q = lane >> 4, n = lane & 15;
-  return StageOffsets{(uint32_t)(q * kPage * PLANE + 4 * n * PLANE), (uint32_t)(NCH * n * kPage + 16 * q),
+  const int vcol = NG == 2 ? n : NCH * n;
+  return StageOffsets{(uint32_t)(q * kPage * PLANE + 4 * n * PLANE), (uint32_t)(vcol * kPage + 16 * q),
                       (uint32_t)(4 * lane)};
 }
 
 // blk (the (page, head) block index) is wave-uniform, so the block addresses
 // stay in scalar registers; the second K / V copies of d = 128 differ only in
 // their lane offsets
-template <int D>
+template <int D, int NG>
 __device__ __forceinline__ void stage_page(const DecodeDev& p, size_t blk, uint32_t stage_lds, StageOffsets o) {
-  using S = Stage<D>;
+  using S = Stage<D, NG>;
+  // the stage address is wave-uniform (ring base and slot index); say so, so that
+  // it stays in a scalar register for the copies' M0 operand
+  stage_lds = __builtin_amdgcn_readfirstlane(stage_lds);
   const uint8_t* kb = p.k_codes + blk * (16 * D);
   const uint8_t* vb = p.v_codes + blk * (16 * D);
   copy16_to_lds(kb, o.k, stage_lds + S::kK);
   if constexpr (D == 128) copy16_to_lds(kb, o.k + 16, stage_lds + S::kK + 1024);
   copy16_to_lds(vb, o.v, stage_lds + S::kV);
-  if constexpr (D == 128) copy16_to_lds(vb, o.v + kPage, stage_lds + S::kV + 1024);
-  copy4_to_lds(p.k_sz + blk * kPage, o.sz, stage_lds + S::kKsz);
-  copy4_to_lds(p.v_sz + blk * kPage, o.sz, stage_lds + S::kVsz);
+  if constexpr (D == 128) copy16_to_lds(vb, o.v + (NG == 2 ? 16 * kPage : kPage), stage_lds + S::kV + 1024);
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    copy4_to_lds(p.k_sz + (blk * NG + j) * kPage, o.sz, stage_lds + S::kKsz + 256 * j);
+    copy4_to_lds(p.v_sz + (blk * NG + j) * kPage, o.sz, stage_lds + S::kVsz + 256 * j);
+  }
 }
 
 // Per-wave LDS: a ring of page stages and the weight-digit planes (unless
@@ -533,16 +545,17 @@ __device__ __forceinline__ void stage_page(const DecodeDev& p, size_t blk, uint3
 // of copies are outstanding, enough to keep HBM busy; deeper rings only
 // lengthen the memory queues, and a wave then stalls issuing its copies
 // instead of computing.
-template <int D, int NB>
+template <int D, int NB, int NG = 1>
 struct Ring {
-  static constexpr bool kPlanesInK = NB * 1024 <= 16 * D;   // planes reuse the consumed K codes
+  // weight-digit planes: one per (head block, group); they reuse the consumed K codes when they fit
+  static constexpr bool kPlanesInK = NB * NG * 1024 <= 16 * D;
 #ifdef OSCAR_SCAN_STAGES
   static constexpr int kStages = OSCAR_SCAN_STAGES;
 #else
   static constexpr int kStages = 2;
 #endif
-  static constexpr int kPlaneBytes = kPlanesInK ? 0 : NB * 1024;
-  static constexpr int kWaveBytes = kStages * Stage<D>::kBytes + kPlaneBytes;
+  static constexpr int kPlaneBytes = kPlanesInK ? 0 : NB * NG * 1024;
+  static constexpr int kWaveBytes = kStages * Stage<D, NG>::kBytes + kPlaneBytes;
 };
 
 // Lane roles (lane = 16*grp + n):
@@ -559,7 +572,7 @@ template <int D, int G>
 struct HistOperands {
   static constexpr int NB = (G + 3) / 4, NCH = D / 64;
   v4i qa[NB][NCH];
-  float ca[NB], cb[NB];
+  float ca[NB], cb[NB][2];   // cb per (scale, zero) group (the second is 0 with one group)
 };
 
 template <int D, int G>
@@ -571,7 +584,8 @@ __device__ __forceinline__ void load_hist_operands(const DecodeDev& p, int b, in
   for (int nb = 0; nb < NB; ++nb) {
     const int hout = 4 * nb + grp;        // head whose results this lane holds
     o.ca[nb] = hout < G ? p.qa[h_base + hout] : 0.0f;
-    o.cb[nb] = hout < G ? p.qb[h_base + hout] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) o.cb[nb][j] = hout < G ? p.qb[2 * (h_base + hout) + j] : 0.0f;
     const bool row_ok = 4 * nb + (n >> 2) < G;   // head of the A row this lane supplies
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -592,7 +606,8 @@ __device__ __forceinline__ void load_pair_operands(const DecodeDev& p, int b, in
   for (int nb = 0; nb < 2; ++nb) {
     const int unit = (b + nb) * p.n_kv + g;
     o.ca[nb] = p.qa[(size_t)(b + nb) * p.Hq + g * 4 + grp];
-    o.cb[nb] = p.qb[(size_t)(b + nb) * p.Hq + g * 4 + grp];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) o.cb[nb][j] = p.qb[2 * ((size_t)(b + nb) * p.Hq + g * 4 + grp) + j];
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
       o.qa[nb][c] = reinterpret_cast<const v4i*>(p.qdig)[((size_t)unit * NCH + c) * kWave + lane];
@@ -603,20 +618,29 @@ __device__ __forceinline__ void load_pair_operands(const DecodeDev& p, int b, in
 // holds the page id of page pg_begin + lane, and qo the QK operands; both were
 // loaded by the caller together with the history length, and this wave's
 // vector loads have completed.
-template <int D, int G, bool LM>
+template <int D, int G, bool LM, int NG>
 __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begin, int count, int hl, int pid_lane,
                                           const HistOperands<D, G>& qo, uint8_t* ring, float* mw, bool& poison,
                                           int lane) {
   constexpr int NB = (G + 3) / 4;
   constexpr int NCH = D / 64;   // code words per token per K plane; V byte columns per lane
   constexpr int NU = 4 * NCH;   // PV result column blocks per head block
-  using S = Stage<D>;
-  using RG = Ring<D, NB>;
+  using S = Stage<D, NG>;
+  using RG = Ring<D, NB, NG>;
   constexpr int NS = RG::kStages;
   const int n = lane & 15, grp = lane >> 4;
   const auto& qa = qo.qa;
   const auto& ca = qo.ca;
   const auto& cb = qo.cb;
+  // With two (scale, zero) groups the QK dot is also needed over channels
+  // 0..63 alone: K operand block grp holds channels 32grp..32grp+31 of both
+  // chunks, so group 0's q operand keeps blocks 0 and 1 and zeroes 2 and 3.
+  // Group 1's dot is the full one minus group 0's (exact in int32).
+  v4i qa0[NB][NCH];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) qa0[nb][c] = (NG == 2 && grp < 2) ? qa[nb][c] : v4i{0, 0, 0, 0};
   const uint64_t page_ok = __ballot(pid_lane >= 0 && (int64_t)pid_lane < p.n_pages);
 
   // pv: integer digit sums of the PV products since the last rescale; facc:
@@ -626,12 +650,13 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
   // mref: reference maximum (log2 units) of each head block; logits are kept
   // relative to it.  thr: rescale when a relative logit exceeds it (-inf until
   // the first page has set the references).
-  float mref[NB], lsum[NB], zsum[NB];
+  float mref[NB], lsum[NB], zsum[NB][NG];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     mref[nb] = 0.0f;
     lsum[nb] = 0.0f;
-    zsum[nb] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NG; ++j) zsum[nb][j] = 0.0f;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       pv[nb][u] = v4i{0, 0, 0, 0};
@@ -650,9 +675,9 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
     const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(blk_lane >> 32), i);
     return ((size_t)hi << 32) | lo;
   };
-  const StageOffsets soff = stage_offsets<D>(lane);
+  const StageOffsets soff = stage_offsets<D, NG>(lane);
   const int pre = count < NS - 1 ? count : NS - 1;
-  for (int i = 0; i < pre; ++i) stage_page<D>(p, page_blk(i), ring_lds + i * S::kBytes, soff);
+  for (int i = 0; i < pre; ++i) stage_page<D, NG>(p, page_blk(i), ring_lds + i * S::kBytes, soff);
   int slot_use = 0, slot_fill = pre;   // ring slots of page i and of page i + NS - 1
 
   // Issue priority falls with the wave's relative progress through its range
@@ -671,7 +696,7 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
       prio_next = ((4 - prio) * count + 3) / 4;
     }
     if (i + NS - 1 < count) {
-      stage_page<D>(p, page_blk(i + NS - 1), ring_lds + slot_fill * S::kBytes, soff);
+      stage_page<D, NG>(p, page_blk(i + NS - 1), ring_lds + slot_fill * S::kBytes, soff);
       slot_fill = slot_fill == NS - 1 ? 0 : slot_fill + 1;
     }
     wait_page<S::kCopies, NS - 1>(count - 1 - i);
@@ -686,8 +711,11 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
       // slots past the history end hold undefined bytes: give them zero
       // scales and zeros, so only the logit mask below has to exclude them
       if (lane >= nv) {
-        reinterpret_cast<uint32_t*>(st + S::kKsz)[lane] = 0u;
-        reinterpret_cast<uint32_t*>(st + S::kVsz)[lane] = 0u;
+#pragma unroll
+        for (int j = 0; j < NG; ++j) {
+          reinterpret_cast<uint32_t*>(st + S::kKsz + 256 * j)[lane] = 0u;
+          reinterpret_cast<uint32_t*>(st + S::kVsz + 256 * j)[lane] = 0u;
+        }
       }
       __builtin_amdgcn_wave_barrier();
     }
@@ -701,18 +729,21 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
     uint4 vpre[NCH];
 #pragma unroll
     for (int bs = 0; bs < NCH; ++bs) vpre[bs] = *reinterpret_cast<const uint4*>(st + S::kV + 1024 * bs + 16 * lane);
-    const uint4 ksz = *reinterpret_cast<const uint4*>(st + S::kKsz + 16 * n);
-    const uint4 vsz = *reinterpret_cast<const uint4*>(st + S::kVsz + 16 * n);
-    const uint32_t kw4[4] = {ksz.x, ksz.y, ksz.z, ksz.w};
-    const uint32_t vw4[4] = {vsz.x, vsz.y, vsz.z, vsz.w};
-    // token 4n+tb
-    float sk[4], zk[4], sv[4], zv[4];
+    // token 4n+tb, group j
+    float sk[NG][4], zk[NG][4], sv[NG][4], zv[NG][4];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      sk[tb] = f16_to_f32(kw4[tb] & 0xffffu);
-      zk[tb] = f16_to_f32(kw4[tb] >> 16);
-      sv[tb] = f16_to_f32(vw4[tb] & 0xffffu);
-      zv[tb] = f16_to_f32(vw4[tb] >> 16);
+    for (int j = 0; j < NG; ++j) {
+      const uint4 ksz = *reinterpret_cast<const uint4*>(st + S::kKsz + 256 * j + 16 * n);
+      const uint4 vsz = *reinterpret_cast<const uint4*>(st + S::kVsz + 256 * j + 16 * n);
+      const uint32_t kw4[4] = {ksz.x, ksz.y, ksz.z, ksz.w};
+      const uint32_t vw4[4] = {vsz.x, vsz.y, vsz.z, vsz.w};
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        sk[j][tb] = f16_to_f32(kw4[tb] & 0xffffu);
+        zk[j][tb] = f16_to_f32(kw4[tb] >> 16);
+        sv[j][tb] = f16_to_f32(vw4[tb] & 0xffffu);
+        zv[j][tb] = f16_to_f32(vw4[tb] >> 16);
+      }
     }
 
     // ---- QK, one head block at a time: token block tb holds token 4n+tb.
@@ -724,20 +755,30 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
       const bool hok = 4 * nb + grp < G;
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        v4i dq;
+        v4i dq, dq0;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
           const uint32_t w = kword[tb * NCH + c];
           const v4i bop = v4i{code_operand<LM>(w, 0), code_operand<LM>(w, 1), code_operand<LM>(w, 2),
                               code_operand<LM>(w, 3)};
           dq = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[nb][c], bop, c == 0 ? v4i{0, 0, 0, 0} : dq, 0, 0, 0);
+          if constexpr (NG == 2)
+            dq0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa0[nb][c], bop, c == 0 ? v4i{0, 0, 0, 0} : dq0, 0, 0, 0);
         }
         // digits: d0 + 2^8 d1 and d2 + 2^8 d3 are exact in int32
-        const int lo = dq.x + dq.y * 256, hi = dq.z + dq.w * 256;
-        const float dot = fmaf((float)hi, 65536.0f, (float)lo);
-        // an invalid head gets fma(0, dot, -inf) = -inf (dot is finite)
-        const float off = hok ? fmaf(zk[tb], cb[nb], -mref[nb]) : -INFINITY;
-        lg[nb][tb] = fmaf(sk[tb] * ca[nb], dot, off);
+        auto dot_of = [](v4i v) {
+          const int lo = v.x + v.y * 256, hi = v.z + v.w * 256;
+          return fmaf((float)hi, 65536.0f, (float)lo);
+        };
+        if constexpr (NG == 1) {
+          // an invalid head gets fma(0, dot, -inf) = -inf (dot is finite)
+          const float off = hok ? fmaf(zk[0][tb], cb[nb][0], -mref[nb]) : -INFINITY;
+          lg[nb][tb] = fmaf(sk[0][tb] * ca[nb], dot_of(dq), off);
+        } else {
+          const v4i dq1 = dq - dq0;
+          const float off = hok ? fmaf(zk[0][tb], cb[nb][0], fmaf(zk[1][tb], cb[nb][1], -mref[nb])) : -INFINITY;
+          lg[nb][tb] = fmaf(sk[0][tb] * ca[nb], dot_of(dq0), fmaf(sk[1][tb] * ca[nb], dot_of(dq1), off));
+        }
       }
     }
     if (nv < kPage) {   // tokens past the history end (the last page only)
@@ -752,15 +793,17 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
       lmax[nb] = fmaxf(fmaxf(lg[nb][0], lg[nb][1]), fmaxf(lg[nb][2], lg[nb][3]));
       need |= lmax[nb] > thr;
     }
-    need |= fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])) > sthr;
+    float svmax = fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3]));
+#pragma unroll
+    for (int j = 1; j < NG; ++j) svmax = fmaxf(svmax, fmaxf(fmaxf(sv[j][0], sv[j][1]), fmaxf(sv[j][2], sv[j][3])));
+    need |= svmax > sthr;
 
     __builtin_amdgcn_sched_barrier(0);
     if (__any(need)) {
       // raise the references and the V-scale bound; fold the integer
       // accumulators into fp32 under the old ones first
       const bool first = !(kw_inv > 0.0f);   // nothing accumulated yet
-      float s_new = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-      s_new = fmaxf(smax, group16_max(s_new));
+      const float s_new = fmaxf(smax, group16_max(svmax));
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const float t = group16_max(lmax[nb]);
@@ -774,7 +817,8 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
             clear_in_place(pv[nb][u]);
           }
           lsum[nb] *= alpha;
-          zsum[nb] *= alpha;
+#pragma unroll
+          for (int j = 0; j < NG; ++j) zsum[nb][j] *= alpha;
         }
         mref[nb] += delta;
 #pragma unroll
@@ -795,33 +839,43 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
     // ---- weights p*scale_V as 30-bit fixed point, balanced digits,
     // transposed into the LDS digit planes of the PV A operands
     uint8_t* pl = RG::kPlanesInK ? st + S::kK : planes;
-    float svk[4];
+    float svk[NG][4];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) svk[tb] = sv[tb] * kw;
+    for (int j = 0; j < NG; ++j)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) svk[j][tb] = sv[j][tb] * kw;
     __builtin_amdgcn_wave_barrier();   // every lane has read its K words
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      uint32_t dg[4];
+      float pr[4];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        const float pr = __builtin_amdgcn_exp2f(lg[nb][tb]);   // exp2(-inf) = 0
-        lsum[nb] += pr;
-        zsum[nb] = fmaf(pr, zv[tb], zsum[nb]);
-        dg[tb] = balanced_digits((uint32_t)fmaf(pr, svk[tb], 0.5f));
+        pr[tb] = __builtin_amdgcn_exp2f(lg[nb][tb]);   // exp2(-inf) = 0
+        lsum[nb] += pr[tb];
       }
-      // 4x4 byte transpose: t_j byte tb = digit j of token 4n+tb
-      const uint32_t x01l = __builtin_amdgcn_perm(dg[1], dg[0], 0x05010400u);
-      const uint32_t x01h = __builtin_amdgcn_perm(dg[1], dg[0], 0x07030602u);
-      const uint32_t x23l = __builtin_amdgcn_perm(dg[3], dg[2], 0x05010400u);
-      const uint32_t x23h = __builtin_amdgcn_perm(dg[3], dg[2], 0x07030602u);
-      // word j is row (head 4nb+grp, digit j), tokens 4n..4n+3: it goes to the
-      // chunk the PV reader lane (4grp+j, n/4) loads (see plane_chunk)
-      uint8_t* plane = pl + nb * 1024 + 256 * (n >> 2) + 4 * (n & 3);
-      const int sw = 4 * (n >> 2);
-      *reinterpret_cast<uint32_t*>(plane + 16 * ((4 * grp + 0) ^ sw)) = __builtin_amdgcn_perm(x23l, x01l, 0x05040100u);
-      *reinterpret_cast<uint32_t*>(plane + 16 * ((4 * grp + 1) ^ sw)) = __builtin_amdgcn_perm(x23l, x01l, 0x07060302u);
-      *reinterpret_cast<uint32_t*>(plane + 16 * ((4 * grp + 2) ^ sw)) = __builtin_amdgcn_perm(x23h, x01h, 0x05040100u);
-      *reinterpret_cast<uint32_t*>(plane + 16 * ((4 * grp + 3) ^ sw)) = __builtin_amdgcn_perm(x23h, x01h, 0x07060302u);
+      // one plane per (head block, group): group j's weights p*scale_V[j]
+#pragma unroll
+      for (int j = 0; j < NG; ++j) {
+        uint32_t dg[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          zsum[nb][j] = fmaf(pr[tb], zv[j][tb], zsum[nb][j]);
+          dg[tb] = balanced_digits((uint32_t)fmaf(pr[tb], svk[j][tb], 0.5f));
+        }
+        // 4x4 byte transpose: t_j byte tb = digit j of token 4n+tb
+        const uint32_t x01l = __builtin_amdgcn_perm(dg[1], dg[0], 0x05010400u);
+        const uint32_t x01h = __builtin_amdgcn_perm(dg[1], dg[0], 0x07030602u);
+        const uint32_t x23l = __builtin_amdgcn_perm(dg[3], dg[2], 0x05010400u);
+        const uint32_t x23h = __builtin_amdgcn_perm(dg[3], dg[2], 0x07030602u);
+        // word j is row (head 4nb+grp, digit j), tokens 4n..4n+3: it goes to the
+        // chunk the PV reader lane (4grp+j, n/4) loads (see plane_chunk)
+        uint8_t* plane = pl + (nb * NG + j) * 1024 + 256 * (n >> 2) + 4 * (n & 3);
+        const int sw = 4 * (n >> 2);
+        *reinterpret_cast<uint32_t*>(plane + 16 * ((4 * grp + 0) ^ sw)) = __builtin_amdgcn_perm(x23l, x01l, 0x05040100u);
+        *reinterpret_cast<uint32_t*>(plane + 16 * ((4 * grp + 1) ^ sw)) = __builtin_amdgcn_perm(x23l, x01l, 0x07060302u);
+        *reinterpret_cast<uint32_t*>(plane + 16 * ((4 * grp + 2) ^ sw)) = __builtin_amdgcn_perm(x23h, x01h, 0x05040100u);
+        *reinterpret_cast<uint32_t*>(plane + 16 * ((4 * grp + 3) ^ sw)) = __builtin_amdgcn_perm(x23h, x01h, 0x07060302u);
+      }
     }
     __builtin_amdgcn_wave_barrier();
 
@@ -834,7 +888,9 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
       for (int nb = 0; nb < NB; ++nb) {
         // A lane (n, grp): row (head 4nb + n/4, digit n%4), tokens 16grp..16grp+15;
         // plane nb holds 4 token blocks of 256 bytes, chunk n ^ 4grp of block grp
-        const v4i wa = *reinterpret_cast<const v4i*>(pl + nb * 1024 + 256 * grp + 16 * (n ^ (4 * grp)));
+        // with two groups, chunk bs of V is group bs (see stage_offsets)
+        const v4i wa =
+            *reinterpret_cast<const v4i*>(pl + (nb * NG + (NG == 2 ? bs : 0)) * 1024 + 256 * grp + 16 * (n ^ (4 * grp)));
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) {
           const v4i bop = v4i{code_operand<LM>(r[0], pp), code_operand<LM>(r[1], pp), code_operand<LM>(r[2], pp),
@@ -850,11 +906,12 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
 
   // ---- fold, reduce over the 16 lanes of each head; each head's (m, l, acc)
   // slot overlays the start of the wave's ring
-  float acc[NB][NU], lz[NB][2];
+  float acc[NB][NU], lz[NB], zs[NB][NG];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    lz[nb][0] = group16_sum(lsum[nb]);
-    lz[nb][1] = group16_sum(zsum[nb]);
+    lz[nb] = group16_sum(lsum[nb]);
+#pragma unroll
+    for (int j = 0; j < NG; ++j) zs[nb][j] = group16_sum(zsum[nb][j]);
 #pragma unroll
     for (int u = 0; u < NU; ++u)
       acc[nb][u] = facc[nb][u] + digits_to_f32(pv[nb][u]) * (code_scale<LM>(u & 3) * kw_inv);
@@ -866,10 +923,15 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
       float* mh = mw + h * part_row(D);
       if (n == 0) {
         mh[0] = kw_inv > 0.0f ? mref[nb] : -INFINITY;   // no page processed: empty partial
-        mh[1] = lz[nb][0];
+        mh[1] = lz[nb];
       }
+      // result u = (chunk u/4, field u%4) of column n: channel NU*n + u, or with
+      // two groups 64*(u/4) + 4n + u%4 (chunk u/4 is group u/4)
 #pragma unroll
-      for (int u = 0; u < NU; ++u) mh[kPartAcc + NU * n + u] = acc[nb][u] + lz[nb][1];
+      for (int u = 0; u < NU; ++u) {
+        if constexpr (NG == 1) mh[kPartAcc + NU * n + u] = acc[nb][u] + zs[nb][0];
+        else mh[kPartAcc + 64 * (u >> 2) + 4 * n + (u & 3)] = acc[nb][u] + zs[nb][u >> 2];
+      }
     }
   }
 }
@@ -940,7 +1002,9 @@ __device__ __forceinline__ void rotate_query_block(const DecodeDev& p, int bh) {
   }
   if (tid == 0) {
     p.qa[bh] = p.sm_log2 / (16.0f * kq);
-    p.qb[bh] = p.sm_log2 * qsum;
+    // sum of q_rot over the head, or over each 64-channel group (one wave each)
+    p.qb[2 * bh] = p.sm_log2 * (p.ng == 2 ? red[1][0] : qsum);
+    p.qb[2 * bh + 1] = p.ng == 2 ? p.sm_log2 * red[1][1] : 0.0f;
   }
 }
 
@@ -957,7 +1021,8 @@ __global__ __launch_bounds__(kBlock) void prepare_kernel(DecodeDev p, int n_rot,
   id -= n_rot;
   const int64_t nk = dk.n_tok * p.n_kv;
   const DemoteDev& dm = id < nk ? dk : dv;
-  const int kind = (id < nk ? OSCAR_KIND_K : OSCAR_KIND_V) | (p.lm ? OSCAR_CODEBOOK_LLOYD_MAX : 0);
+  const int kind = (id < nk ? OSCAR_KIND_K : OSCAR_KIND_V) | (p.lm ? OSCAR_CODEBOOK_LLOYD_MAX : 0) |
+                   (p.ng == 2 ? OSCAR_GROUPS_64 : 0);
   if (id >= nk) id -= (int)nk;
   demote_token_block<D>(kind, dm.x, dm.n_src, dm.tok_stride, dm.head_stride, dm.src_idx, id / p.n_kv, id % p.n_kv,
                         p.n_kv, dm.rot, dm.clip, dm.dst_slot, dm.codes, dm.sz, dm.n_pages);
@@ -969,13 +1034,13 @@ __global__ __launch_bounds__(kBlock) void prepare_kernel(DecodeDev p, int n_rot,
 #ifndef OSCAR_SCAN_WAVES_PER_SIMD
 #define OSCAR_SCAN_WAVES_PER_SIMD 2
 #endif
-template <int D, int G, bool LM>
+template <int D, int G, bool LM, int NG>
 __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) void decode_main_kernel(DecodeDev p) {
   constexpr int NB = (G + 3) / 4;
-  using RG = Ring<D, NB>;
+  using RG = Ring<D, NB, NG>;
   // a group-4 kernel also runs 8-head waves (two requests) on shared-prefix splits
   constexpr int kHistOwn = 4 * RG::kWaveBytes;
-  constexpr int kHistPair = G == 4 ? 4 * Ring<D, 2>::kWaveBytes : 0;
+  constexpr int kHistPair = G == 4 ? 4 * Ring<D, 2, NG>::kWaveBytes : 0;
   constexpr int kHistBytes = kHistOwn > kHistPair ? kHistOwn : kHistPair;
   constexpr int kBf16Bytes = 4 * bf16_lds_bytes<D, G>();
   constexpr int kSmem = kHistBytes > kBf16Bytes ? kHistBytes : kBf16Bytes;
@@ -1050,7 +1115,7 @@ __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) vo
     if (id < n_packed) {
       // ---- a split inside the shared prefix for requests b and b+1: one
       // 8-head wave reads each page once for both
-      using RP = Ring<D, 2>;
+      using RP = Ring<D, 2, NG>;
       static_assert(8 * part_row(D) * 4 <= RP::kWaveBytes, "merge slot must fit in the wave's ring");
       const int per_split = p.pairs * p.n_kv;
       const int split = id / per_split, pair = (id % per_split) / p.n_kv, g = id % p.n_kv;
@@ -1072,7 +1137,8 @@ __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) vo
       const int count =
           __builtin_amdgcn_readfirstlane(poison ? 0 : max(0, min(ws0 + per_wave, pe) - ws0));
       uint8_t* ring = smem + wave * RP::kWaveBytes;
-      hist_wave<D, 8, LM>(p, g, ws0, count, full, pid_lane, qo, ring, reinterpret_cast<float*>(ring), poison, lane);
+      hist_wave<D, 8, LM, NG>(p, g, ws0, count, full, pid_lane, qo, ring, reinterpret_cast<float*>(ring), poison,
+                              lane);
       if (lane == 0) flags[wave] = poison ? 1 : 0;
       __syncthreads();
       const size_t rows = (size_t)4 * part_row(D);
@@ -1120,7 +1186,7 @@ __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) vo
   const int count = max(0, min(ws0 + per_wave, pe) - ws0);
   uint8_t* ring = smem + wave * RG::kWaveBytes;
   // the wave's merge slot [G][D+2] = (m, l, acc) overlays its own ring once the scan is done
-  hist_wave<D, G, LM>(p, g, ws0, count, hl, pid_lane, qo, ring, reinterpret_cast<float*>(ring), poison, lane);
+  hist_wave<D, G, LM, NG>(p, g, ws0, count, hl, pid_lane, qo, ring, reinterpret_cast<float*>(ring), poison, lane);
   if (lane == 0) flags[wave] = poison ? 1 : 0;
   __syncthreads();
   combine_block<G, D>(reinterpret_cast<const float*>(smem), RG::kWaveBytes / 4, flags,
@@ -1432,8 +1498,16 @@ void launch_main(const DecodeDev& dv, hipStream_t stream) {
   const long blocks = (long)dv.n_pref * dv.pairs * dv.n_kv + (long)(dv.splits - dv.n_pref) * units +
                       (long)dv.n_pref * (dv.B & 1) * dv.n_kv + units * dv.bf_blocks;
   if (blocks == 0) return;
-  if (dv.lm) decode_main_kernel<D, G, true><<<dim3((unsigned)blocks), kBlock, 0, stream>>>(dv);
-  else decode_main_kernel<D, G, false><<<dim3((unsigned)blocks), kBlock, 0, stream>>>(dv);
+  const dim3 grid((unsigned)blocks);
+  if constexpr (D == 128) {
+    if (dv.ng == 2) {   // 64-channel (scale, zero) groups
+      if (dv.lm) decode_main_kernel<D, G, true, 2><<<grid, kBlock, 0, stream>>>(dv);
+      else decode_main_kernel<D, G, false, 2><<<grid, kBlock, 0, stream>>>(dv);
+      return;
+    }
+  }
+  if (dv.lm) decode_main_kernel<D, G, true, 1><<<grid, kBlock, 0, stream>>>(dv);
+  else decode_main_kernel<D, G, false, 1><<<grid, kBlock, 0, stream>>>(dv);
 }
 
 template <int D>
@@ -1474,6 +1548,7 @@ DecodeDev make_dev(const oscar_decode_args& a, const DecodePlan& plan, char* ws)
   dv.chunks = plan.chunks; dv.sink_chunks = plan.sink_chunks;
   dv.bf_blocks = plan.chunks;
   dv.lm = a.codebook == OSCAR_CODEBOOK_LLOYD_MAX ? 1 : 0;
+  dv.ng = (a.group_channels == 64 && a.head_dim == 128) ? 2 : 1;
   // pack the splits that lie wholly inside a shared prefix (group size 4, two or more requests)
   dv.pairs = a.batch / 2;
   dv.n_pref = (dv.G == 4 && dv.pairs > 0 && plan.splits > 0) ? std::min(plan.splits, a.shared_pages / plan.pages_per_split)

@@ -4,7 +4,9 @@
 // an fp64 dot product rounded once to fp32; zero = fp16(min), scale =
 // fp16((max - min) / 3); code = rint((y - zero) / scale) clamped to [0, 3]
 // (or the Lloyd-Max statistics and thresholds of oscar.h when kind carries
-// OSCAR_CODEBOOK_LLOYD_MAX).
+// OSCAR_CODEBOOK_LLOYD_MAX), over the whole head or over each 64-channel group
+// (OSCAR_GROUPS_64; the scale/zero block of a (page, head) is then
+// group-planar).
 // Source: the demotion step of the serving pipeline in the myzaker.com article
 // on OSCAR; R and the clip threshold from the gist.science OSCAR technical
 // summary, section 2.2A.
@@ -33,10 +35,12 @@ __device__ __forceinline__ void demote_token_block(int kind, const uint16_t* __r
   __shared__ double parts[P][D];
   __shared__ float ys[D];
   __shared__ float red[2][kBlock / kWave];
-  __shared__ double dred[kBlock / kWave];
+  __shared__ double dred[2][kBlock / kWave];
+  __shared__ float gzs[2][D / kWave];   // (zero, scale) of each group
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const bool lm = (kind & OSCAR_CODEBOOK_LLOYD_MAX) != 0;
-  const bool k_layout = (kind & ~OSCAR_CODEBOOK_LLOYD_MAX) == OSCAR_KIND_K;
+  const bool grouped = (kind & OSCAR_GROUPS_64) != 0;   // 64-channel groups
+  const bool k_layout = (kind & ~(OSCAR_CODEBOOK_LLOYD_MAX | OSCAR_GROUPS_64)) == OSCAR_KIND_K;
   const int64_t src = src_idx ? (int64_t)src_idx[t] : t;
   const int64_t slot = dst_slot[t];
   if (src < 0 || src >= n_src || slot < 0 || slot >= n_pages * kPage) return;   // block-uniform
@@ -73,45 +77,55 @@ __device__ __forceinline__ void demote_token_block(int kind, const uint16_t* __r
     mn = yc;
     mx = yc;
   }
+  // per-wave (64-channel) extremes; a group is GW consecutive waves
+  constexpr int kWaves = D / kWave;
+  const int ng = grouped ? kWaves : 1, gw = kWaves / ng;
   mn = wave_min(mn);
   mx = wave_max(mx);
   if (lane == 0) {
     red[0][wave] = mn;
     red[1][wave] = mx;
   }
-  __syncthreads();
-#pragma unroll
-  for (int w = 0; w < kBlock / kWave; ++w) {
-    mn = fminf(mn, red[0][w]);
-    mx = fmaxf(mx, red[1][w]);
-  }
-  __half zh = __float2half_rn(mn);
-  __half sh = __float2half_rn(__fdiv_rn(mx - mn, 3.0f));
-  if (lm) {   // block-uniform: mean, then the sum of squared deviations, in fp64
-    double v = wave_sum_f64(tid < D ? (double)ys[tid] : 0.0);
-    if (lane == 0) dred[wave] = v;
+  if (lm) {   // block-uniform: the group means, then the sums of squared deviations, in fp64
+    const double v = wave_sum_f64(tid < D ? (double)ys[tid] : 0.0);
+    if (lane == 0) dred[0][wave] = v;
     __syncthreads();
     double tot = 0.0;
-#pragma unroll
-    for (int w = 0; w < kBlock / kWave; ++w) tot += dred[w];
-    const double mean = tot / D;
-    __syncthreads();
-    const double dv = tid < D ? (double)ys[tid] - mean : 0.0;
-    v = wave_sum_f64(__dmul_rn(dv, dv));
-    if (lane == 0) dred[wave] = v;
-    __syncthreads();
-    double sq = 0.0;
-#pragma unroll
-    for (int w = 0; w < kBlock / kWave; ++w) sq += dred[w];
-    lm_scale_zero(mean, sq, D, sh, zh);
+    const int g0 = (wave < kWaves ? wave / gw : 0) * gw;   // first wave of this thread's group
+    for (int w = g0; w < g0 + gw; ++w) tot += dred[0][w];
+    const double dv = tid < D ? (double)ys[tid] - tot / (D / ng) : 0.0;
+    const double sq = wave_sum_f64(__dmul_rn(dv, dv));
+    if (lane == 0) dred[1][wave] = sq;
   }
-  const float z = __half2float(zh), s = __half2float(sh);
-  const int64_t page = slot / kPage;
-  const int o = (int)(slot % kPage);
-  if (tid == 0)
-    sz[(page * n_kv + g) * kPage + o] = (uint32_t)__half_as_ushort(sh) | ((uint32_t)__half_as_ushort(zh) << 16);
+  __syncthreads();
+  if (tid < ng) {   // thread j: (scale, zero) of group j
+    float gmn = INFINITY, gmx = -INFINITY;
+    double sum = 0.0, sq = 0.0;
+    for (int w = tid * gw; w < (tid + 1) * gw; ++w) {
+      gmn = fminf(gmn, red[0][w]);
+      gmx = fmaxf(gmx, red[1][w]);
+      if (lm) {
+        sum += dred[0][w];
+        sq += dred[1][w];
+      }
+    }
+    __half zh = __float2half_rn(gmn);
+    __half sh = __float2half_rn(__fdiv_rn(gmx - gmn, 3.0f));
+    if (lm) lm_scale_zero(sum / (D / ng), sq, D / ng, sh, zh);
+    gzs[0][tid] = __half2float(zh);
+    gzs[1][tid] = __half2float(sh);
+    const int64_t page = slot / kPage;
+    const int o = (int)(slot % kPage);
+    sz[((page * n_kv + g) * ng + tid) * kPage + o] =
+        (uint32_t)__half_as_ushort(sh) | ((uint32_t)__half_as_ushort(zh) << 16);
+  }
+  __syncthreads();
   if (tid < kRowBytes) {
     const int i = tid;
+    const int j = (4 * i) / (D / ng);   // the group of channels 4i..4i+3
+    const float z = gzs[0][j], s = gzs[1][j];
+    const int64_t page = slot / kPage;
+    const int o = (int)(slot % kPage);
     uint32_t byte = 0;
     if (lm) {
 #pragma unroll

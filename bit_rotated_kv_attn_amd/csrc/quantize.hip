@@ -34,13 +34,15 @@ __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(
   __shared__ float ys[kQTok][D + 1];     // clipped rotated values
   __shared__ int64_t src_s[kQTok];
   __shared__ int64_t dst_s[kQTok];       // -1: skip this token
-  __shared__ float zf[kQTok], sf[kQTok];
+  constexpr int kPer = D / kWave;        // channels per lane in the statistics (channel lane + 64k)
+  __shared__ float zf[kQTok][kPer], sf[kQTok][kPer];   // per token and group
 
   const int g = blockIdx.y;
   const int64_t t0 = (int64_t)blockIdx.x * kQTok;
   const int tid = threadIdx.x;
   const bool lm = (kind & OSCAR_CODEBOOK_LLOYD_MAX) != 0;
-  const bool k_layout = (kind & ~OSCAR_CODEBOOK_LLOYD_MAX) == OSCAR_KIND_K;
+  const int ng = (kind & OSCAR_GROUPS_64) ? kPer : 1;   // 64-channel groups: group k holds channels 64k..
+  const bool k_layout = (kind & ~(OSCAR_CODEBOOK_LLOYD_MAX | OSCAR_GROUPS_64)) == OSCAR_KIND_K;
 
   if (tid < kQTok) {
     const int64_t t = t0 + tid;
@@ -84,38 +86,45 @@ __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(
   __syncthreads();
 
   // per-token group statistics: zero = fp16(min), scale = fp16((max - min) / 3),
-  // or the Lloyd-Max mean and deviation (fp64)
+  // or the Lloyd-Max mean and deviation (fp64); lane holds channels lane + 64k,
+  // and with 64-channel groups element k is group k's
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   for (int t = wave; t < kQTok; t += kBlock / kWave) {
-    float mn = INFINITY, mx = -INFINITY;
-    for (int c = lane; c < D; c += kWave) {
-      mn = fminf(mn, ys[t][c]);
-      mx = fmaxf(mx, ys[t][c]);
-    }
-    mn = wave_min(mn);
-    mx = wave_max(mx);
-    __half z = __float2half_rn(mn);
-    __half s = __float2half_rn(__fdiv_rn(mx - mn, 3.0f));
-    if (lm) {
-      double s1 = 0.0;
-      for (int c = lane; c < D; c += kWave) s1 += (double)ys[t][c];
-      const double mean = wave_sum_f64(s1) / D;
-      double s2 = 0.0;
-      for (int c = lane; c < D; c += kWave) {
-        const double dv = (double)ys[t][c] - mean;
-        s2 = __dadd_rn(s2, __dmul_rn(dv, dv));
+    float v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) v[k] = ys[t][lane + kWave * k];
+    const int per = kPer / ng;   // elements of one group in this lane
+    for (int j = 0; j < ng; ++j) {
+      float mn = INFINITY, mx = -INFINITY;
+      for (int k = j * per; k < (j + 1) * per; ++k) {
+        mn = fminf(mn, v[k]);
+        mx = fmaxf(mx, v[k]);
       }
-      lm_scale_zero(mean, wave_sum_f64(s2), D, s, z);
-    }
-    if (lane == 0) {
-      zf[t] = __half2float(z);
-      sf[t] = __half2float(s);
-      const int64_t slot = dst_s[t];
-      if (slot >= 0) {
-        const int64_t page = slot / kPage;
-        const int o = (int)(slot % kPage);
-        sz[(page * n_kv + g) * kPage + o] =
-            (uint32_t)__half_as_ushort(s) | ((uint32_t)__half_as_ushort(z) << 16);
+      mn = wave_min(mn);
+      mx = wave_max(mx);
+      __half z = __float2half_rn(mn);
+      __half s = __float2half_rn(__fdiv_rn(mx - mn, 3.0f));
+      if (lm) {
+        double s1 = 0.0;
+        for (int k = j * per; k < (j + 1) * per; ++k) s1 += (double)v[k];
+        const double mean = wave_sum_f64(s1) / (D / ng);
+        double s2 = 0.0;
+        for (int k = j * per; k < (j + 1) * per; ++k) {
+          const double dv = (double)v[k] - mean;
+          s2 = __dadd_rn(s2, __dmul_rn(dv, dv));
+        }
+        lm_scale_zero(mean, wave_sum_f64(s2), D / ng, s, z);
+      }
+      if (lane == 0) {
+        zf[t][j] = __half2float(z);
+        sf[t][j] = __half2float(s);
+        const int64_t slot = dst_s[t];
+        if (slot >= 0) {
+          const int64_t page = slot / kPage;
+          const int o = (int)(slot % kPage);
+          sz[((page * n_kv + g) * ng + j) * kPage + o] =
+              (uint32_t)__half_as_ushort(s) | ((uint32_t)__half_as_ushort(z) << 16);
+        }
       }
     }
   }
@@ -126,7 +135,8 @@ __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(
     const int t = e / kRowBytes, i = e % kRowBytes;
     const int64_t slot = dst_s[t];
     if (slot < 0) continue;
-    const float z = zf[t], s = sf[t];
+    const int j = (4 * i) / (D / ng);   // the group of channels 4i..4i+3
+    const float z = zf[t][j], s = sf[t][j];
     uint32_t byte = 0;
     if (lm) {
 #pragma unroll

@@ -86,6 +86,16 @@ typedef enum oscar_kind { OSCAR_KIND_K = 0, OSCAR_KIND_V = 1 } oscar_kind;
 #define OSCAR_CODEBOOK_UNIFORM 0
 #define OSCAR_CODEBOOK_LLOYD_MAX 0x100
 
+/* Quantisation groups: by default one group is all head_dim channels of a
+ * (token, head).  With 64-channel groups every block of 64 consecutive
+ * channels has its own (scale, zero) (head_dim 128: two groups; head_dim 64:
+ * one, the same as the default), which is where the bit-reversal permutation
+ * of R balances the groups (gist.science summary, section 2.2A).  The
+ * scale/zero pool is then [n_pages][n_kv][64*head_dim/64][2], group-planar:
+ * group j of token o at j*64 + o.  OR'ed into a demotion's kind; the decode
+ * args carry the group size. */
+#define OSCAR_GROUPS_64 0x200
+
 /* ABI version of the loaded library (OSCAR_ABI_VERSION). */
 OSCAR_API int oscar_abi_version(void);
 
@@ -106,7 +116,8 @@ OSCAR_API const char* oscar_status_str(int status);
  *   row and (scale, zero) into slot dst_slot = page*64 + offset.
  *
  *  kind          OSCAR_KIND_K or OSCAR_KIND_V (selects the in-page layout),
- *                optionally OR'ed with OSCAR_CODEBOOK_LLOYD_MAX
+ *                optionally OR'ed with OSCAR_CODEBOOK_LLOYD_MAX and / or
+ *                OSCAR_GROUPS_64 (then scale_zero holds 64*head_dim/64 pairs per head)
  *  x             bf16; element (token s, head g, channel c) is at
  *                x[s*x_tok_stride + g*x_head_stride + c]; the caller
  *                guarantees that address is valid for every s in [0, n_src)
@@ -186,6 +197,8 @@ typedef struct oscar_decode_args {
   int32_t codebook;         /* OSCAR_CODEBOOK_UNIFORM or OSCAR_CODEBOOK_LLOYD_MAX: the
                                codebook the pools were demoted with (a decode step also
                                demotes with it)                                        */
+  int32_t group_channels;   /* 0 (a group is the whole head) or 64 (OSCAR_GROUPS_64
+                               pools); a decode step demotes with the same groups      */
 } oscar_decode_args;
 
 /* Workspace bytes oscar_decode_attn needs for these sizes (0 on invalid sizes).
@@ -224,7 +237,8 @@ OSCAR_API oscar_status oscar_decode_merge(const oscar_decode_args* args, void* w
 /*
  * One tensor's demotion inside a decode step: the arguments of
  * oscar_quantize_pack except kind, n_kv and head_dim (taken from the step:
- * demote_k is K and demote_v is V, both with the step's args->codebook).
+ * demote_k is K and demote_v is V, both with the step's args->codebook and
+ * args->group_channels).
  * n_tok in [0, 2^24 / n_kv]; the other rules are those of oscar_quantize_pack.
  */
 typedef struct oscar_demote_args {

@@ -32,9 +32,9 @@ def host(t: torch.Tensor, np_dtype=None) -> np.ndarray:
     return a.view(np_dtype) if np_dtype is not None else a
 
 
-def empty_pools(n_pages: int, n_kv: int, d: int, device="cuda"):
+def empty_pools(n_pages: int, n_kv: int, d: int, device="cuda", ng: int = 1):
     codes = torch.zeros((n_pages, n_kv, PAGE * d // 4), dtype=torch.uint8, device=device)
-    sz = torch.zeros((n_pages, n_kv, PAGE, 2), dtype=torch.int16, device=device)
+    sz = torch.zeros((n_pages, n_kv, PAGE * ng, 2), dtype=torch.int16, device=device)
     return codes, sz
 
 
@@ -44,15 +44,19 @@ CODEBOOK_FLAG = {"uniform": hip.CODEBOOK_UNIFORM, "lloyd_max": hip.CODEBOOK_LLOY
 
 def oracle_pools(cfg: dict):
     """K/V pools of a decode config filled by the oracle quantiser (with the
-    config's codebook, uniform by default)."""
+    config's codebook, uniform by default, and its group_channels, 0 = whole
+    head by default)."""
     cb = cfg.get("codebook", "uniform")
     d, nkv, P = cfg["head_dim"], cfg["n_kv"], cfg["n_pages"]
+    group = cfg.get("group_channels", 0) or d
     kc = np.zeros((P, nkv, PAGE * d // 4), np.uint8)
     vc = np.zeros_like(kc)
-    ks = np.zeros((P, nkv, PAGE, 2), np.uint16)
+    ks = np.zeros((P, nkv, PAGE * (d // group), 2), np.uint16)
     vs = np.zeros_like(ks)
-    oracle.quantize_pack_ref("k", cfg["hist_k"], cfg["r_k"], cfg["tau_k"], cfg["hist_slot"], kc, ks, codebook=cb)
-    oracle.quantize_pack_ref("v", cfg["hist_v"], cfg["r_v"], cfg["tau_v"], cfg["hist_slot"], vc, vs, codebook=cb)
+    oracle.quantize_pack_ref("k", cfg["hist_k"], cfg["r_k"], cfg["tau_k"], cfg["hist_slot"], kc, ks, codebook=cb,
+                             group=group)
+    oracle.quantize_pack_ref("v", cfg["hist_v"], cfg["r_v"], cfg["tau_v"], cfg["hist_slot"], vc, vs, codebook=cb,
+                             group=group)
     return kc, vc, ks, vs
 
 
@@ -75,7 +79,8 @@ def gpu_decode(cfg: dict, pools, *, block_table=None, hist_len=None, sink_len=No
                 hist_len=dev(hl), max_hist_len=mh, k_codes=kc, v_codes=vc, k_sz=ks, v_sz=vs,
                 block_table=dev(table), r_k=dev(cfg["r_k"]), r_v=dev(cfg["r_v"]), out=out, workspace=ws,
                 sm_scale=float(cfg["sm_scale"]), shared_pages=shared_pages,
-                codebook=CODEBOOK_FLAG[cfg.get("codebook", "uniform")])
+                codebook=CODEBOOK_FLAG[cfg.get("codebook", "uniform")],
+                group_channels=int(cfg.get("group_channels", 0)))
     for _ in range(reps):
         hip.oscar_decode_attn(**args)
     torch.cuda.synchronize()
@@ -83,10 +88,11 @@ def gpu_decode(cfg: dict, pools, *, block_table=None, hist_len=None, sink_len=No
 
 
 def gpu_quantize(kind: str, x: np.ndarray, rot: np.ndarray, clip, dst_slot: np.ndarray, n_pages: int,
-                 src_idx=None, pools=None, codebook: str = "uniform"):
+                 src_idx=None, pools=None, codebook: str = "uniform", groups64: bool = False):
     n_kv, d = rot.shape[0], rot.shape[-1]
-    codes, sz = pools if pools is not None else empty_pools(n_pages, n_kv, d)
-    hip.oscar_quantize_pack((hip.KIND_K if kind == "k" else hip.KIND_V) | CODEBOOK_FLAG[codebook], dev(x), dev(rot),
+    codes, sz = pools if pools is not None else empty_pools(n_pages, n_kv, d, ng=d // 64 if groups64 else 1)
+    flags = CODEBOOK_FLAG[codebook] | (hip.GROUPS_64 if groups64 else 0)
+    hip.oscar_quantize_pack((hip.KIND_K if kind == "k" else hip.KIND_V) | flags, dev(x), dev(rot),
                             float(clip),
                             dev(dst_slot.astype(np.int32)), codes, sz,
                             src_idx=None if src_idx is None else dev(src_idx.astype(np.int32)))
@@ -130,8 +136,11 @@ def compare_quant(kind: str, gpu_codes, gpu_sz, ref_codes, ref_sz, diag, d: int,
         for t, c in diff:
             a, b = int(gc[t, c]), int(rc[t, c])
             assert abs(a - b) == 1, f"code differs by more than one level (token {t}, head {g}, ch {c})"
-            z = float(np.array(diag["zero16"][t, g]).view(np.float16))
-            s = float(np.array(diag["scale16"][t, g]).view(np.float16))
+            zd, sd = diag["zero16"][t, g], diag["scale16"][t, g]
+            if np.ndim(zd):   # per-group diagnostics: the group of channel c
+                zd, sd = zd[c * len(zd) // d], sd[c * len(sd) // d]
+            z = float(np.array(zd).view(np.float16))
+            s = float(np.array(sd).view(np.float16))
             if codebook == "uniform":
                 e = z + (min(a, b) + 0.5) * s
             else:   # the threshold between Lloyd-Max codes a and b

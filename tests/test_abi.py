@@ -52,7 +52,7 @@ def _qp(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(kind=2), hip.OSCAR_EINVAL),
-    (dict(kind=0x200), hip.OSCAR_EINVAL),                            # an unknown codebook flag
+    (dict(kind=0x400), hip.OSCAR_EINVAL),                            # an unknown flag
     (dict(kind=0x102), hip.OSCAR_EINVAL),
     (dict(d=96), hip.OSCAR_EUNSUPPORTED),
     (dict(clip=0.0), hip.OSCAR_EINVAL),
@@ -97,6 +97,7 @@ def _decode_args(**kw):
     (dict(shared_pages=-1), hip.OSCAR_EINVAL),
     (dict(shared_pages=2), hip.OSCAR_EINVAL),                        # 2 pages > max_hist_len 100
     (dict(codebook=1), hip.OSCAR_EINVAL),
+    (dict(group_channels=32), hip.OSCAR_EINVAL),
     (dict(batch=0, q=None, out=None), hip.OSCAR_OK),
 ])
 def test_decode_validation(kw, status):

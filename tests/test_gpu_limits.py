@@ -18,7 +18,7 @@ from gpu_util import PAGE, compare_out, gpu_decode
 pytestmark = pytest.mark.gpu
 
 
-def _limit_cache(codebook):
+def _limit_cache(codebook, groups=1):
     rng = np.random.default_rng(404)
     B, n_kv, G, d, hp = 11, 8, 1, 128, 256
     Hq = n_kv * G
@@ -40,6 +40,11 @@ def _limit_cache(codebook):
     vs = np.zeros((hp, n_kv, PAGE, 2), np.uint16)
     vs[..., 0] = np.float16(0.75).view(np.uint16)
     vs[..., 1] = np.float16(-1.0).view(np.uint16)
+    if groups == 2:   # 64-channel groups: the same K pairs for both, V group 1 at a smaller scale
+        ks = np.concatenate([ks, ks], axis=2)
+        vs2 = vs.copy()
+        vs2[..., 0] = np.float16(0.5).view(np.uint16)
+        vs = np.concatenate([vs, vs2], axis=2)
     table = np.tile(rng.permutation(hp).astype(np.int32), (B, 1))
     eye = np.stack([np.eye(d, dtype=np.float32)] * n_kv)
     cfg = dict(q=q, sink_k=np.zeros((B, n_kv, 64, d), np.uint16), sink_v=np.zeros((B, n_kv, 64, d), np.uint16),
@@ -48,15 +53,18 @@ def _limit_cache(codebook):
                hist_len=np.full(B, hl, np.int32), block_table=table, r_k=eye, r_v=eye, sm_scale=sm)
     if codebook != "uniform":
         cfg["codebook"] = codebook
+    if groups == 2:
+        cfg["group_channels"] = 64
     return cfg, (kc, vc, ks, vs)
 
 
+@pytest.mark.parametrize("groups", [1, 2])
 @pytest.mark.parametrize("codebook", ["uniform", "lloyd_max"])
-def test_longest_wave_range_at_the_integer_bound(codebook):
-    cfg, pools = _limit_cache(codebook)
+def test_longest_wave_range_at_the_integer_bound(codebook, groups):
+    cfg, pools = _limit_cache(codebook, groups)
     B, Hq, d = cfg["q"].shape
     got = gpu_decode(cfg, pools)
     ref = oracle.decode_attn_ref(cfg, *pools, heads=[(0, h) for h in range(Hq)])
-    compare_out(got[:1], ref[:1], what=f"64-page waves at the integer bound ({codebook})")
+    compare_out(got[:1], ref[:1], what=f"64-page waves at the integer bound ({codebook}, {groups} groups)")
     # every request holds the same pages and query: the same partials, bit for bit
     assert np.array_equal(got, np.broadcast_to(got[:1], got.shape))

@@ -37,11 +37,13 @@ def _pools_with_room(cfg):
     return kc, vc, ks, vs
 
 
+@pytest.mark.parametrize("groups", [0, 64])
 @pytest.mark.parametrize("codebook", ["uniform", "lloyd_max"])
 @pytest.mark.parametrize("shape", SHAPES, ids=[s.name for s in SHAPES])
-def test_decode_step_matches_separate_oracle_steps(shape, codebook):
+def test_decode_step_matches_separate_oracle_steps(shape, codebook, groups):
     cfg, slot = _with_free_slots(synth.make_decode_config(0, shape=shape, seed_index=7))
     cfg["codebook"] = codebook
+    cfg["group_channels"] = groups
     B, Hq, d = cfg["q"].shape
     n_kv, cap = cfg["n_kv"], cfg["recent_k"].shape[2]
     kc, vc, ks, vs = _pools_with_room(cfg)
@@ -51,9 +53,9 @@ def test_decode_step_matches_separate_oracle_steps(shape, codebook):
     src = (np.arange(B) * n_kv * cap + ring).astype(np.int32)
     kc_ref, vc_ref, ks_ref, vs_ref = kc.copy(), vc.copy(), ks.copy(), vs.copy()
     dk_ref = oracle.quantize_pack_ref("k", cfg["recent_k"][:, :, ring, :], cfg["r_k"], cfg["tau_k"], slot,
-                                      kc_ref, ks_ref, codebook=codebook)
+                                      kc_ref, ks_ref, codebook=codebook, group=groups or None)
     dv_ref = oracle.quantize_pack_ref("v", cfg["recent_v"][:, :, ring, :], cfg["r_v"], cfg["tau_v"], slot,
-                                      vc_ref, vs_ref, codebook=codebook)
+                                      vc_ref, vs_ref, codebook=codebook, group=groups or None)
 
     pools = [dev(p) for p in (kc, vc, ks, vs)]
     ws = torch.zeros(hip.oscar_decode_workspace_bytes(B, Hq, n_kv, d, int(cfg["hist_len"].max()), 64, cap),
@@ -66,7 +68,7 @@ def test_decode_step_matches_separate_oracle_steps(shape, codebook):
                            hist_len=dev(cfg["hist_len"]), max_hist_len=int(cfg["hist_len"].max()),
                            k_codes=pools[0], v_codes=pools[1], k_sz=pools[2], v_sz=pools[3],
                            block_table=dev(cfg["block_table"]), r_k=rk, r_v=rv, out=out, workspace=ws,
-                           sm_scale=float(cfg["sm_scale"]), codebook=CODEBOOK_FLAG[codebook])
+                           sm_scale=float(cfg["sm_scale"]), codebook=CODEBOOK_FLAG[codebook], group_channels=groups)
     common = dict(src_idx=src_t, n_src=B * n_kv * cap, x_tok_stride=d, x_head_stride=cap * d)
     dk = hip.demote_args(x=rec_k, rot=rk, clip=float(cfg["tau_k"]), dst_slot=slot_t, codes=pools[0],
                          scale_zero=pools[2], **common)
