@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas (0: enough for >= 1 GiB)")
     ap.add_argument("--codebook", default="uniform", choices=("uniform", "lloyd-max"),
                     help="INT2 codebook the history is demoted with and read by (oscar.h)")
+    ap.add_argument("--groups", type=int, default=0, choices=(0, 64),
+                    help="channels per (scale, zero) group: 0 = the whole head, 64 = 64-channel groups")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -81,6 +83,8 @@ def main():
     cfg_index = WORKLOADS[args.workload]
     lm = args.codebook == "lloyd-max"
     cb_flag = hip.CODEBOOK_LLOYD_MAX if lm else hip.CODEBOOK_UNIFORM
+    grouped = args.groups == 64
+    q_flags = cb_flag | (hip.GROUPS_64 if grouped else 0)
     shape = synth.DECODE_SHAPES[cfg_index]
     t0 = time.time()
     cfg = ensure_free_slot(synth.make_decode_config(cfg_index))
@@ -111,11 +115,13 @@ def main():
     # algorithmic bytes: every history token of a physical page once (a page
     # shared by several requests' tables needs reading only once), the BF16
     # windows and the block-table entries
-    hist_bytes = unique_tokens(cfg["block_table"], cfg["hist_len"]) * n_kv * (2 * d // 4 + 2 * 4)
+    ng = d // 64 if args.groups == 64 else 1   # (scale, zero) pairs per token and head
+    hist_bytes = unique_tokens(cfg["block_table"], cfg["hist_len"]) * n_kv * (2 * d // 4 + 2 * 4 * ng)
     win_bytes = int((cfg["sink_len"] + cfg["recent_len"]).sum()) * n_kv * 4 * d
     table_bytes = int(sum(-(-int(h) // 64) for h in cfg["hist_len"])) * 4
     scan_bytes = hist_bytes + win_bytes + table_bytes
-    per_replica = (P * n_kv * 64 * (2 * d // 4 + 8)) + 2 * cfg["sink_k"].nbytes + 2 * cfg["recent_k"].nbytes
+    per_replica = (P * n_kv * 64 * (2 * d // 4 + 8 * (d // 64 if args.groups == 64 else 1))
+                   + 2 * cfg["sink_k"].nbytes + 2 * cfg["recent_k"].nbytes)
     R = args.replicas or max(2, math.ceil((1 << 30) / per_replica))
     log(f"replicas: {R} x {per_replica / 1e6:.1f} MB = {R * per_replica / 2**30:.2f} GiB "
         f"(MALL {MALL_BYTES >> 20} MiB)")
@@ -126,10 +132,10 @@ def main():
     for r in range(R):
         kc = torch.zeros((P, n_kv, 64 * d // 4), dtype=torch.uint8, device=dev)
         vc = torch.zeros_like(kc)
-        ks = torch.zeros((P, n_kv, 64, 2), dtype=torch.int16, device=dev)
+        ks = torch.zeros((P, n_kv, 64 * (d // 64 if grouped else 1), 2), dtype=torch.int16, device=dev)
         vs = torch.zeros_like(ks)
-        hip.oscar_quantize_pack(hip.KIND_K | cb_flag, hist_k, r_k, float(cfg["tau_k"]), hist_slot, kc, ks)
-        hip.oscar_quantize_pack(hip.KIND_V | cb_flag, hist_v, r_v, float(cfg["tau_v"]), hist_slot, vc, vs)
+        hip.oscar_quantize_pack(hip.KIND_K | q_flags, hist_k, r_k, float(cfg["tau_k"]), hist_slot, kc, ks)
+        hip.oscar_quantize_pack(hip.KIND_V | q_flags, hist_v, r_v, float(cfg["tau_v"]), hist_slot, vc, vs)
         rep = dict(k_codes=kc, v_codes=vc, k_sz=ks, v_sz=vs, sink_k=t(cfg["sink_k"]), sink_v=t(cfg["sink_v"]),
                    recent_k=t(cfg["recent_k"]), recent_v=t(cfg["recent_v"]),
                    out=torch.empty((B, Hq, d), dtype=torch.float32, device=dev))
@@ -146,7 +152,7 @@ def main():
                              hist_len=hist_len, max_hist_len=hl, k_codes=rp["k_codes"], v_codes=rp["v_codes"],
                              k_sz=rp["k_sz"], v_sz=rp["v_sz"], block_table=table, r_k=r_k, r_v=r_v,
                              out=rp["out"], workspace=ws, sm_scale=float(cfg["sm_scale"]),
-                             shared_pages=shared, codebook=cb_flag) for rp in reps]
+                             shared_pages=shared, codebook=cb_flag, group_channels=args.groups) for rp in reps]
 
     # the step demotes ring slot 0 of every request's recent window (K and V) in
     # the decode's first launch
@@ -235,11 +241,12 @@ def main():
         "config": {"workload": shape.name, "batch": B, "context": shape.context, "n_q_heads": Hq,
                    "n_kv_heads": n_kv, "head_dim": d, "sink": int(cfg["sink_len"][0]),
                    "history": hl, "recent": int(cfg["recent_len"][0]), "page_tokens": 64,
-                   "cache_replicas": R, "shared_prefix_pages": shared, "codebook": args.codebook,
+                   "cache_replicas": R, "shared_prefix_pages": shared, "codebook": args.codebook, "group_channels": args.groups,
                    "step": "oscar_decode_step: demote K,V of 1 token/request + decode attention"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(args.workload + ("-lloyd-max" if lm else "")),
+                     "traffic": measured_traffic(args.workload + ("-lloyd-max" if lm else "") +
+                                                 ("-groups64" if grouped else "")),
                      "kernel": "decode_main_kernel (oscar_decode_scan)", "kernel_us": scan_us,
                      "bytes_per_launch": scan_bytes},
         "kv_tokens_per_s": float(cfg["hist_len"].sum() + cfg["sink_len"].sum() + cfg["recent_len"].sum())
@@ -280,7 +287,8 @@ def main():
 
     # ---- CPU oracle on a bounded sample (reported baseline, not a target)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, "lloyd_max" if lm else "uniform")
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, "lloyd_max" if lm else "uniform",
+                                              args.groups or None)
     print(json.dumps(result), flush=True)
 
 
@@ -348,7 +356,7 @@ def ensure_free_slot(cfg):
     return cfg
 
 
-def cpu_baseline(cfg, budget_s: float, codebook: str = "uniform"):
+def cpu_baseline(cfg, budget_s: float, codebook: str = "uniform", group=None):
     """Time the oracle (as it stands) on whole KV heads of the same workload:
     one step's demotion of the new token plus decode attention for the G
     query heads of a KV head over the full context.  KV heads are added until
@@ -378,12 +386,12 @@ def cpu_baseline(cfg, budget_s: float, codebook: str = "uniform"):
                        recent_v=cfg["recent_v"][:, g:g + 1], r_k=cfg["r_k"][g:g + 1], r_v=cfg["r_v"][g:g + 1])
             kc = np.zeros((P, 1, 64 * d // 4), np.uint8)
             vc = np.zeros_like(kc)
-            ks = np.zeros((P, 1, 64, 2), np.uint16)
+            ks = np.zeros((P, 1, 64 * (d // group if group else 1), 2), np.uint16)
             vs = np.zeros_like(ks)
             oracle.quantize_pack_ref("k", cfg["hist_k"][:, g:g + 1], sub["r_k"], cfg["tau_k"], cfg["hist_slot"], kc, ks,
-                                     codebook=codebook)
+                                     codebook=codebook, group=group)
             oracle.quantize_pack_ref("v", cfg["hist_v"][:, g:g + 1], sub["r_v"], cfg["tau_v"], cfg["hist_slot"], vc, vs,
-                                     codebook=codebook)
+                                     codebook=codebook, group=group)
             sub["codebook"] = codebook
             setup[g] = (sub, kc, vc, ks, vs)
         sub, kc, vc, ks, vs = setup[g]
@@ -391,9 +399,9 @@ def cpu_baseline(cfg, budget_s: float, codebook: str = "uniform"):
         slot = (cfg["block_table"][np.arange(B), nxt // 64] * 64 + nxt % 64).astype(np.int32)
         w0 = time.perf_counter()
         oracle.quantize_pack_ref("k", sub["recent_k"][:, :, 0, :], sub["r_k"], cfg["tau_k"], slot, kc.copy(), ks.copy(),
-                                 codebook=codebook)
+                                 codebook=codebook, group=group)
         oracle.quantize_pack_ref("v", sub["recent_v"][:, :, 0, :], sub["r_v"], cfg["tau_v"], slot, vc.copy(), vs.copy(),
-                                 codebook=codebook)
+                                 codebook=codebook, group=group)
         oracle.decode_attn_ref(sub, kc, vc, ks, vs)
         spent += time.perf_counter() - w0
         done += 1
