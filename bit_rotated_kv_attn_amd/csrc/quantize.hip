@@ -26,11 +26,9 @@ __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(
     int64_t head_stride, const int32_t* __restrict__ src_idx, int64_t n_tok, int n_kv,
     const float* __restrict__ rot, float clip, const int32_t* __restrict__ dst_slot,
     uint8_t* __restrict__ codes, uint32_t* __restrict__ sz, int64_t n_pages) {
-  constexpr int kParts = kBlock / D;     // token groups (2 for d=128, 4 for d=64)
-  constexpr int kPerThr = kQTok / kParts;
   constexpr int kRowBytes = D / 4;       // code bytes per token
   constexpr int kPlane = D / 16;         // bytes per token in one K plane
-  __shared__ float xs[D][kQTok];         // x tile, channel-major (broadcast reads)
+  __shared__ __attribute__((aligned(16))) float xs[D][kQTok];   // x tile, channel-major (broadcast reads)
   __shared__ float ys[kQTok][D + 1];     // clipped rotated values
   __shared__ int64_t src_s[kQTok];
   __shared__ int64_t dst_s[kQTok];       // -1: skip this token
@@ -67,22 +65,36 @@ __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(
   }
   __syncthreads();
 
-  // y[t][j] = sum_i x[t][i] * R[i][j]
-  const int j = tid % D, part = tid / D;
-  const float* R = rot + (size_t)g * D * D;
-  double acc[kPerThr];
+  // y[t][j] = sum_i x[t][i] * R[i][j], each output accumulated over i in
+  // order with fp64 FMAs.  Thread (cg, tg) owns columns C*cg .. C*cg+C-1 of
+  // tokens 4tg .. 4tg+3, so each converted R and x value feeds C or 4 FMAs.
+  constexpr int C = D / 32;              // columns per thread (4 for d = 128, 2 for d = 64)
+  static_assert(32 * (kQTok / 4) == kBlock, "32 column groups x 8 token groups");
+  const int cg = tid % 32, tg = tid / 32;
+  const float* R = rot + (size_t)g * D * D + C * cg;
+  double acc[C][4];
 #pragma unroll
-  for (int k = 0; k < kPerThr; ++k) acc[k] = 0.0;
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[c][t] = 0.0;
   for (int i = 0; i < D; ++i) {
-    const double r = (double)R[i * D + j];
+    double rd[C], xd[4];
 #pragma unroll
-    for (int k = 0; k < kPerThr; ++k) acc[k] = fma((double)xs[i][part * kPerThr + k], r, acc[k]);
+    for (int c = 0; c < C; ++c) rd[c] = (double)R[(size_t)i * D + c];
+    const float4 xv = *reinterpret_cast<const float4*>(&xs[i][4 * tg]);
+    xd[0] = (double)xv.x;
+    xd[1] = (double)xv.y;
+    xd[2] = (double)xv.z;
+    xd[3] = (double)xv.w;
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[c][t] = fma(xd[t], rd[c], acc[c][t]);
   }
 #pragma unroll
-  for (int k = 0; k < kPerThr; ++k) {
-    const float y = (float)acc[k];
-    ys[part * kPerThr + k][j] = fminf(fmaxf(y, -clip), clip);
-  }
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) ys[4 * tg + t][C * cg + c] = fminf(fmaxf((float)acc[c][t], -clip), clip);
   __syncthreads();
 
   // per-token group statistics: zero = fp16(min), scale = fp16((max - min) / 3),
