@@ -186,6 +186,10 @@ def decode_args(*, q, sink_k, sink_v, recent_k, recent_v, sink_len, recent_len, 
     n_kv = sink_k.shape[1]
     if tuple(out.shape) != (B, Hq, d):
         raise ValueError("out must be [B][Hq][d] fp32")
+    pairs = PAGE * (d // 64 if group_channels == 64 else 1)   # (scale, zero) pairs per (page, head)
+    for name, sz in (("k_sz", k_sz), ("v_sz", v_sz)):
+        if sz.dim() != 4 or sz.shape[2:] != (pairs, 2):
+            raise ValueError(f"{name} must be [n_pages][n_kv][{pairs}][2] for group_channels={group_channels}")
     a = DecodeArgs(batch=B, n_q_heads=Hq, n_kv_heads=n_kv, head_dim=d,
                    sm_scale=float(1.0 / math.sqrt(d) if sm_scale is None else sm_scale),
                    q=_ptr(q, 2, "q"), sink_k=_ptr(sink_k, 2, "sink_k"), sink_v=_ptr(sink_v, 2, "sink_v"),
@@ -242,17 +246,19 @@ def demote_args(*, x, rot, clip: float, dst_slot, codes, scale_zero, src_idx=Non
     n_tok = dst_slot.numel()
     if src_idx is not None and src_idx.numel() != n_tok:
         raise ValueError("src_idx and dst_slot lengths differ")
-    # the step decides the groups: a whole-head or a 64-channel-group scale/zero pool
+    # the step decides the groups (its args' group_channels); oscar_decode_step checks this pool against them
     if codes.shape[1:] != (n_kv, PAGE * d // 4) or scale_zero.shape[1:] not in ((n_kv, PAGE, 2),
                                                                                (n_kv, PAGE * max(1, d // 64), 2)):
         raise ValueError("pool shapes do not match [n_pages][n_kv][...]")
     if dst_slot.dtype.itemsize != 4 or (src_idx is not None and src_idx.dtype.itemsize != 4):
         raise ValueError("dst_slot / src_idx must be int32")
-    return DemoteArgs(x=_ptr(x, 2, "x"), n_src=int(n_src), x_tok_stride=int(x_tok_stride),
-                      x_head_stride=int(x_head_stride), src_idx=_ptr(src_idx, 4, "src_idx"), n_tok=int(n_tok),
-                      rot=_ptr(rot, 4, "rot"), clip=float(clip), dst_slot=_ptr(dst_slot, 4, "dst_slot"),
-                      codes=_ptr(codes, 1, "codes"), scale_zero=_ptr(scale_zero, 2, "scale_zero"),
-                      n_pages=int(codes.shape[0]))
+    a = DemoteArgs(x=_ptr(x, 2, "x"), n_src=int(n_src), x_tok_stride=int(x_tok_stride),
+                   x_head_stride=int(x_head_stride), src_idx=_ptr(src_idx, 4, "src_idx"), n_tok=int(n_tok),
+                   rot=_ptr(rot, 4, "rot"), clip=float(clip), dst_slot=_ptr(dst_slot, 4, "dst_slot"),
+                   codes=_ptr(codes, 1, "codes"), scale_zero=_ptr(scale_zero, 2, "scale_zero"),
+                   n_pages=int(codes.shape[0]))
+    a.sz_pairs = int(scale_zero.shape[2])   # (scale, zero) pairs per (page, head) of this pool
+    return a
 
 
 def oscar_decode_step(*, args, demote_k=None, demote_v=None, stream=None) -> None:
@@ -260,6 +266,11 @@ def oscar_decode_step(*, args, demote_k=None, demote_v=None, stream=None) -> Non
     (:func:`demote_args` results, or None) run in the decode's first launch.
     ``args`` is a :func:`decode_args` tuple."""
     a, ws, nbytes = args
+    pairs = PAGE * (a.head_dim // 64 if a.group_channels == 64 else 1)
+    for name, dm in (("demote_k", demote_k), ("demote_v", demote_v)):
+        if dm is not None and getattr(dm, "sz_pairs", pairs) != pairs:
+            raise ValueError(f"{name}: its scale/zero pool holds {dm.sz_pairs} pairs per (page, head); "
+                             f"group_channels={a.group_channels} writes {pairs}")
     st = lib().oscar_decode_step(ctypes.byref(a), ctypes.byref(demote_k) if demote_k is not None else None,
                                  ctypes.byref(demote_v) if demote_v is not None else None, ws, nbytes,
                                  _stream(stream))
