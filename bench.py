@@ -155,7 +155,7 @@ def main():
                              shared_pages=shared, codebook=cb_flag, group_channels=args.groups) for rp in reps]
 
     # the step demotes ring slot 0 of every request's recent window (K and V) in
-    # the decode's first launch
+    # the decode's last launch
     dem = []
     for r in range(R):
         rp = reps[r]

@@ -263,7 +263,7 @@ def demote_args(*, x, rot, clip: float, dst_slot, codes, scale_zero, src_idx=Non
 
 def oscar_decode_step(*, args, demote_k=None, demote_v=None, stream=None) -> None:
     """One decode step (see oscar_decode_step in oscar.h): the demotions
-    (:func:`demote_args` results, or None) run in the decode's first launch.
+    (:func:`demote_args` results, or None) run in the decode's last launch.
     ``args`` is a :func:`decode_args` tuple."""
     a, ws, nbytes = args
     pairs = PAGE * (a.head_dim // 64 if a.group_channels == 64 else 1)

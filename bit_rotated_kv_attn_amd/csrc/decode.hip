@@ -27,15 +27,15 @@
 //
 // Launches (all on the caller's stream):
 //   1. prepare_kernel       q_rot = q R_K[g] per query head -> MFMA digit
-//                           operands; in a decode step also the step's K / V
-//                           demotions
+//                           operands
 //   2. decode_main_kernel   one grid: INT2 history splits (those inside a
 //                           declared shared prefix read once per request
 //                           pair), then the BF16 sink / recent chunks; each
 //                           block writes an (m, l, acc) partial per head
 //   3. merge_kernel         LSE merge of the history partials, * R_V^T, LSE merge
 //      (merge_unit_kernel)  with the BF16 partials, normalise (one block per
-//                           head, or per (request, KV head) in large batches)
+//                           head, or per (request, KV head) in large batches);
+//                           in a decode step also the step's K / V demotions
 // Softmax state uses base-2 exponents (logits pre-scaled by log2 e).
 #include "common.hpp"
 #include "demote.hpp"
@@ -1008,17 +1008,19 @@ __device__ __forceinline__ void rotate_query_block(const DecodeDev& p, int bh) {
   }
 }
 
-// Launch 1 of a decode: one block per query head rotates q; in a decode step
-// the same launch also demotes the step's K and V tokens (one block per
-// token and KV head), which the decode does not read.
+// Launch 1 of a decode: one block per query head rotates q.
 template <int D>
-__global__ __launch_bounds__(kBlock) void prepare_kernel(DecodeDev p, int n_rot, DemoteDev dk, DemoteDev dv) {
-  int id = blockIdx.x;
-  if (id < n_rot) {
-    rotate_query_block<D>(p, id);
-    return;
-  }
-  id -= n_rot;
+__global__ __launch_bounds__(kBlock) void prepare_kernel(DecodeDev p) {
+  rotate_query_block<D>(p, blockIdx.x);
+}
+
+// Block `id` of a decode step's demotions: the step's K tokens first, then
+// its V tokens, one block per (token, KV head).  They run in the decode's
+// last launch, on the compute units its merge leaves idle: the demoted slots
+// lie past every hist_len, so no launch of this decode reads them.
+template <int D>
+__device__ __forceinline__ void demote_step_block(const DecodeDev& p, int id, const DemoteDev& dk,
+                                                  const DemoteDev& dv) {
   const int64_t nk = dk.n_tok * p.n_kv;
   const DemoteDev& dm = id < nk ? dk : dv;
   const int kind = (id < nk ? OSCAR_KIND_K : OSCAR_KIND_V) | (p.lm ? OSCAR_CODEBOOK_LLOYD_MAX : 0) |
@@ -1290,11 +1292,15 @@ __device__ __forceinline__ float2 merge_head(PartPtr part_ptr, int n_rot, int nt
 // The R_V row segments are requested first, so their loads overlap the
 // partials'.
 template <int D>
-__global__ __launch_bounds__(kBlock) void merge_kernel(DecodeDev p) {
+__global__ __launch_bounds__(kBlock) void merge_kernel(DecodeDev p, int n_merge, DemoteDev dk, DemoteDev dv) {
   constexpr int TPO = kBlock / D;   // threads per output channel
   constexpr int SEG = D / TPO;      // R_V row segment per thread
   __shared__ MergeShared<D> sh;
   const int bh = blockIdx.x;
+  if (bh >= n_merge) {
+    demote_step_block<D>(p, bh - n_merge, dk, dv);
+    return;
+  }
   const int b = bh / p.Hq, h = bh % p.Hq, g = h / p.G, kh = h % p.G;
   const int tid = threadIdx.x;
   const size_t stride = (size_t)p.G * part_row(D);
@@ -1339,12 +1345,16 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(DecodeDev p) {
 constexpr int kUnitRound = 16;
 
 template <int D, int G>
-__global__ __launch_bounds__(kBlock) void merge_unit_kernel(DecodeDev p) {
+__global__ __launch_bounds__(kBlock) void merge_unit_kernel(DecodeDev p, int n_merge, DemoteDev dk, DemoteDev dv) {
   constexpr int QPR = D / 4, R = part_row(D), TPO = kBlock / D, SEG = D / TPO;
   static_assert(G * QPR <= kBlock, "one (head, channel quad) per thread");
   __shared__ __attribute__((aligned(16))) float arot[G][D];
   __shared__ __attribute__((aligned(16))) float aplain[G][D];
   __shared__ float Ls[G];
+  if ((int)blockIdx.x >= n_merge) {
+    demote_step_block<D>(p, blockIdx.x - n_merge, dk, dv);
+    return;
+  }
   const int unit = blockIdx.x, b = unit / p.n_kv, g = unit % p.n_kv;
   const int tid = threadIdx.x;
   const int i = tid / TPO, seg = tid % TPO;   // output channel and R_V row segment of this thread
@@ -1414,22 +1424,34 @@ __global__ __launch_bounds__(kBlock) void merge_unit_kernel(DecodeDev p) {
 }
 
 // The per-unit merge when each head's partials fit in one round and the G
-// heads' channel quads fit in one block.
+// heads' channel quads fit in one block.  n_dem demotion blocks follow the
+// merge blocks.
 template <int D>
-bool launch_merge_unit(const DecodeDev& dv, hipStream_t stream) {
+bool launch_merge_unit(const DecodeDev& dv, unsigned n_dem, const DemoteDev& mk, const DemoteDev& mv,
+                       hipStream_t stream) {
   if (dv.splits + dv.chunks > kUnitRound || dv.G * (D / 4) > kBlock) return false;
-  const unsigned units = (unsigned)dv.B * (unsigned)dv.n_kv;
+  const int units = dv.B * dv.n_kv;
+  const unsigned grid = (unsigned)units + n_dem;
   switch (dv.G) {
-    case 1: merge_unit_kernel<D, 1><<<units, kBlock, 0, stream>>>(dv); break;
-    case 2: merge_unit_kernel<D, 2><<<units, kBlock, 0, stream>>>(dv); break;
-    case 4: merge_unit_kernel<D, 4><<<units, kBlock, 0, stream>>>(dv); break;
-    case 8: merge_unit_kernel<D, 8><<<units, kBlock, 0, stream>>>(dv); break;
+    case 1: merge_unit_kernel<D, 1><<<grid, kBlock, 0, stream>>>(dv, units, mk, mv); break;
+    case 2: merge_unit_kernel<D, 2><<<grid, kBlock, 0, stream>>>(dv, units, mk, mv); break;
+    case 4: merge_unit_kernel<D, 4><<<grid, kBlock, 0, stream>>>(dv, units, mk, mv); break;
+    case 8: merge_unit_kernel<D, 8><<<grid, kBlock, 0, stream>>>(dv, units, mk, mv); break;
     default:
-      if constexpr (16 * (D / 4) <= kBlock) merge_unit_kernel<D, 16><<<units, kBlock, 0, stream>>>(dv);
+      if constexpr (16 * (D / 4) <= kBlock) merge_unit_kernel<D, 16><<<grid, kBlock, 0, stream>>>(dv, units, mk, mv);
       else return false;
       break;
   }
   return true;
+}
+
+// Launch 3: the merge (none with batch 0), then the step's demotions.
+template <int D>
+void launch_merge(const DecodeDev& dv, const DemoteDev& mk, const DemoteDev& mv, hipStream_t stream) {
+  const unsigned n_dem = (unsigned)((mk.n_tok + mv.n_tok) * dv.n_kv);
+  if (dv.B > 0 && launch_merge_unit<D>(dv, n_dem, mk, mv, stream)) return;
+  const int nbh = dv.B * dv.Hq;
+  if (nbh + n_dem > 0) merge_kernel<D><<<(unsigned)nbh + n_dem, kBlock, 0, stream>>>(dv, nbh, mk, mv);
 }
 
 template <int D, int G>
@@ -1579,22 +1601,17 @@ hipError_t launch_decode_phase(int phase, const oscar_decode_args& a, const Deco
   const unsigned nbh = (unsigned)a.batch * (unsigned)a.n_q_heads;
   const bool d128 = a.head_dim == 128;
   if (phase == kPhaseRotate) {
-    const int n_rot = plan.splits > 0 ? (int)nbh : 0;
-    const DemoteDev mk = make_demote(demote_k), mv = make_demote(demote_v);
-    const int64_t blocks = n_rot + (mk.n_tok + mv.n_tok) * a.n_kv_heads;
-    if (blocks > 0) {
-      if (d128) prepare_kernel<128><<<(unsigned)blocks, kBlock, 0, stream>>>(dv, n_rot, mk, mv);
-      else prepare_kernel<64><<<(unsigned)blocks, kBlock, 0, stream>>>(dv, n_rot, mk, mv);
+    if (plan.splits > 0 && nbh > 0) {
+      if (d128) prepare_kernel<128><<<nbh, kBlock, 0, stream>>>(dv);
+      else prepare_kernel<64><<<nbh, kBlock, 0, stream>>>(dv);
     }
-  } else if (a.batch == 0) {
-    return hipSuccess;
-  } else if (phase == kPhaseScan) {
+  } else if (phase == kPhaseMerge) {
+    const DemoteDev mk = make_demote(demote_k), mv = make_demote(demote_v);
+    if (d128) launch_merge<128>(dv, mk, mv, stream);
+    else launch_merge<64>(dv, mk, mv, stream);
+  } else if (a.batch > 0) {
     if (d128) launch_main_g<128>(dv, stream);
     else launch_main_g<64>(dv, stream);
-  } else if (d128) {
-    if (!launch_merge_unit<128>(dv, stream)) merge_kernel<128><<<nbh, kBlock, 0, stream>>>(dv);
-  } else {
-    if (!launch_merge_unit<64>(dv, stream)) merge_kernel<64><<<nbh, kBlock, 0, stream>>>(dv);
   }
   return hipGetLastError();
 }

@@ -259,7 +259,7 @@ typedef struct oscar_demote_args {
 /*
  * One steady-state decode step (the serving pipeline of the myzaker.com
  * article on OSCAR): demote the step's K and V tokens into INT2 history and
- * run decode attention, with the demotions folded into the decode's first
+ * run decode attention, with the demotions folded into the decode's last
  * launch (three launches in all instead of five).  demote_k / demote_v may
  * be NULL.  They may write into the pools this decode reads, but only into
  * slots the decode does not attend (at or past hist_len of their request): the

@@ -1,5 +1,5 @@
 """GPU parity of oscar_decode_step: the step's K and V demotions run in the
-decode's first launch.  The decode must equal the oracle decode of the cache
+decode's last launch.  The decode must equal the oracle decode of the cache
 as given (the demoted slots lie past hist_len), and the demoted slots must
 equal the oracle quantiser's output for the demoted tokens."""
 import numpy as np
