@@ -1286,16 +1286,59 @@ __device__ __forceinline__ float2 merge_head(PartPtr part_ptr, int n_rot, int nt
   return make_float2(M, L);
 }
 
+// The output rotation out_i = sum_j A_j R_V[i][j] with R_V read in whole
+// rows: thread t holds columns 4c..4c+3 (c = t % (D/4)) of rows
+// RPT*rb .. RPT*rb + RPT-1 (rb = t / (D/4)), so each load instruction of a
+// wave covers whole 512-byte rows (per-thread row segments would put every
+// lane of an instruction on its own cache line).  The dot products over a
+// row's column quads are then summed through LDS.
+template <int D>
+struct RvRows {
+  static constexpr int QPR = D / 4, RB = kBlock / QPR, RPT = D / RB, TPO = kBlock / D;
+  static constexpr int kStride = D + 1;   // red[c][row]: conflict-free writes and sums
+  float4 v[RPT];
+};
+
+template <int D>
+__device__ __forceinline__ void load_rv_rows(RvRows<D>& r, const float* __restrict__ rv, int tid) {
+  using T = RvRows<D>;
+  const int c = tid % T::QPR, rb = tid / T::QPR;
+  const float4* src = reinterpret_cast<const float4*>(rv + (size_t)(T::RPT * rb) * D) + c;
+#pragma unroll
+  for (int k = 0; k < T::RPT; ++k) r.v[k] = src[(size_t)k * T::QPR];
+}
+
+// out row i = tid / TPO of A (D floats in LDS) times R_V^T; every thread of
+// the row gets the value.  red: QPR * (D + 1) floats of LDS.  Contains one
+// barrier; the caller synchronises before red or A is written again.
+template <int D>
+__device__ __forceinline__ float rv_product(const RvRows<D>& r, const float* A, float* red, int tid) {
+  using T = RvRows<D>;
+  const int c = tid % T::QPR, rb = tid / T::QPR;
+  const float4 a = reinterpret_cast<const float4*>(A)[c];
+  float* dst = red + c * T::kStride + T::RPT * rb;
+#pragma unroll
+  for (int k = 0; k < T::RPT; ++k)
+    dst[k] = fmaf(a.x, r.v[k].x, fmaf(a.y, r.v[k].y, fmaf(a.z, r.v[k].z, a.w * r.v[k].w)));
+  __syncthreads();
+  const int i = tid / T::TPO, h = tid % T::TPO;
+  constexpr int CPT = T::QPR / T::TPO;   // column quads summed per thread
+  float o = 0.0f;
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) o += red[(h * CPT + j) * T::kStride + i];
+#pragma unroll
+  for (int off = 1; off < T::TPO; off <<= 1) o += __shfl_xor(o, off, kWave);
+  return o;
+}
+
 // One query head per block:
 //   out = (sum_hist f_s acc_s R_V^T + sum_bf16 f_s acc_s) / sum_all f_s l_s,
 //   f_s = exp2(m_s - M) with M the maximum over every partial.
-// The R_V row segments are requested first, so their loads overlap the
-// partials'.
+// The R_V rows are requested first, so their loads overlap the partials'.
 template <int D>
 __global__ __launch_bounds__(kBlock) void merge_kernel(DecodeDev p, int n_merge, DemoteDev dk, DemoteDev dv) {
-  constexpr int TPO = kBlock / D;   // threads per output channel
-  constexpr int SEG = D / TPO;      // R_V row segment per thread
   __shared__ MergeShared<D> sh;
+  __shared__ float red[RvRows<D>::QPR * RvRows<D>::kStride];
   const int bh = blockIdx.x;
   if (bh >= n_merge) {
     demote_step_block<D>(p, bh - n_merge, dk, dv);
@@ -1307,27 +1350,14 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(DecodeDev p, int n_merge,
   const float* hp = p.hpart + ((size_t)b * p.n_kv + g) * p.splits * stride + (size_t)kh * part_row(D);
   const float* bp = p.bpart + ((size_t)b * p.n_kv + g) * p.chunks * stride + (size_t)kh * part_row(D);
   const int n = p.splits, nt = p.splits + p.chunks;
-  // this thread's segment of output row i of the R_V product
-  const int i = tid / TPO, seg = tid % TPO;
-  float4 rv[SEG / 4];
-  {
-    const float4* Rrow = reinterpret_cast<const float4*>(p.r_v + ((size_t)g * D + i) * D + seg * SEG);
-#pragma unroll
-    for (int k = 0; k < SEG / 4; ++k) rv[k] = Rrow[k];
-  }
+  RvRows<D> rv;
+  load_rv_rows<D>(rv, p.r_v + (size_t)g * D * D, tid);
   const float2 ML = merge_head<D>(
       [&](int s) { return s < n ? hp + (size_t)s * stride : bp + (size_t)(s - n) * stride; }, n, nt, sh, tid);
   // out_hist[i] = sum_j A_hist[j] R_V[g][i][j]
-  float o = 0.0f;
-  const float4* a4 = reinterpret_cast<const float4*>(sh.rot + seg * SEG);
-#pragma unroll
-  for (int k = 0; k < SEG / 4; ++k) {
-    const float4 a = a4[k];
-    o = fmaf(a.x, rv[k].x, fmaf(a.y, rv[k].y, fmaf(a.z, rv[k].z, fmaf(a.w, rv[k].w, o))));
-  }
-#pragma unroll
-  for (int off = 1; off < TPO; off <<= 1) o += __shfl_xor(o, off, kWave);
-  if (seg == 0) {
+  const float o = rv_product<D>(rv, sh.rot, red, tid);
+  const int i = tid / RvRows<D>::TPO;
+  if (tid % RvRows<D>::TPO == 0) {
     const float L = ML.y;
     float out;
     if (isnan(L)) out = NAN;
@@ -1346,24 +1376,21 @@ constexpr int kUnitRound = 16;
 
 template <int D, int G>
 __global__ __launch_bounds__(kBlock) void merge_unit_kernel(DecodeDev p, int n_merge, DemoteDev dk, DemoteDev dv) {
-  constexpr int QPR = D / 4, R = part_row(D), TPO = kBlock / D, SEG = D / TPO;
+  constexpr int QPR = D / 4, R = part_row(D), TPO = RvRows<D>::TPO;
   static_assert(G * QPR <= kBlock, "one (head, channel quad) per thread");
   __shared__ __attribute__((aligned(16))) float arot[G][D];
   __shared__ __attribute__((aligned(16))) float aplain[G][D];
   __shared__ float Ls[G];
+  __shared__ float red[RvRows<D>::QPR * RvRows<D>::kStride];
   if ((int)blockIdx.x >= n_merge) {
     demote_step_block<D>(p, blockIdx.x - n_merge, dk, dv);
     return;
   }
   const int unit = blockIdx.x, b = unit / p.n_kv, g = unit % p.n_kv;
   const int tid = threadIdx.x;
-  const int i = tid / TPO, seg = tid % TPO;   // output channel and R_V row segment of this thread
-  float4 rv[SEG / 4];
-  {
-    const float4* Rrow = reinterpret_cast<const float4*>(p.r_v + ((size_t)g * D + i) * D + seg * SEG);
-#pragma unroll
-    for (int k = 0; k < SEG / 4; ++k) rv[k] = Rrow[k];
-  }
+  const int i = tid / TPO;   // output channel of this thread
+  RvRows<D> rv;
+  load_rv_rows<D>(rv, p.r_v + (size_t)g * D * D, tid);
   const size_t stride = (size_t)G * R;
   const int n = p.splits, nt = p.splits + p.chunks;
   const float* hb = p.hpart + (size_t)unit * n * stride;
@@ -1402,18 +1429,10 @@ __global__ __launch_bounds__(kBlock) void merge_unit_kernel(DecodeDev p, int n_m
   }
   __syncthreads();
   // out[h][i] = (sum_j A_hist[h][j] R_V[g][i][j] + A_bf16[h][i]) / L[h]
-#pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float4* a4 = reinterpret_cast<const float4*>(&arot[h][seg * SEG]);
-    float o = 0.0f;
-#pragma unroll
-    for (int k = 0; k < SEG / 4; ++k) {
-      const float4 a = a4[k];
-      o = fmaf(a.x, rv[k].x, fmaf(a.y, rv[k].y, fmaf(a.z, rv[k].z, fmaf(a.w, rv[k].w, o))));
-    }
-#pragma unroll
-    for (int off = 1; off < TPO; off <<= 1) o += __shfl_xor(o, off, kWave);
-    if (seg == 0) {
+    if (h > 0) __syncthreads();   // every thread has read red for head h - 1
+    const float o = rv_product<D>(rv, arot[h], red, tid);
+    if (tid % TPO == 0) {
       const float L = Ls[h];
       float out;
       if (isnan(L)) out = NAN;
