@@ -20,7 +20,7 @@
 // fixed-point integers split into four balanced 8-bit digits, one MFMA row per
 // (head, digit), so 4 heads fill the 16 rows.  Products and sums are exact;
 // the only roundings are the fixed-point conversions (a query element to
-// 2^-26 of the largest, a weight to 2^-18 of the reference weight) and the
+// 2^-25 of the query's norm, a weight to 2^-18 of the reference weight) and the
 // fp32 combination of the digit results.  PV accumulates in int32 across a
 // wave's pages; the softmax reference maximum is only raised when a logit
 // exceeds it by 2^12 (then the integer accumulator is folded into fp32).
@@ -939,6 +939,14 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
 // ---------------------------------------------------------------------------
 // 1. rotate the query: q_rot = q R_K[g]; MFMA digit operands and constants
 // ---------------------------------------------------------------------------
+// Sum over the 64 lanes of a wave (every lane active), in every lane: DPP row
+// sums, then the four rows read into scalar registers.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v = group16_sum(v);
+  auto lane_val = [&](int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); };
+  return (lane_val(0) + lane_val(16)) + (lane_val(32) + lane_val(48));
+}
+
 template <int D>
 __device__ __forceinline__ void rotate_query_block(const DecodeDev& p, int bh) {
   constexpr int NCH = D / 64, PLANE = D / 16;
@@ -947,15 +955,30 @@ __device__ __forceinline__ void rotate_query_block(const DecodeDev& p, int bh) {
   constexpr int QPR = D / 4, P = kBlock / QPR, IP = D / P;
   __shared__ float qs[D];
   __shared__ __attribute__((aligned(16))) float part_s[P][D];
-  __shared__ float red[2][kBlock / kWave];
+  __shared__ float wsum[kBlock / kWave];
   const int b = bh / p.Hq, h = bh % p.Hq, g = h / p.G, hl = h % p.G;
   const int tid = threadIdx.x, jq = tid % QPR, part = tid / QPR;
+  // q is requested before R, so waiting for it leaves the R loads in flight
+  const float qv = tid < D ? bf16_to_f32(p.q[(size_t)bh * D + tid]) : 0.0f;
   const float4* R = reinterpret_cast<const float4*>(p.r_k + (size_t)g * D * D + (size_t)part * IP * D) + jq;
   float4 r[IP];
 #pragma unroll
   for (int k = 0; k < IP; ++k) r[k] = R[(size_t)k * QPR];
-  if (tid < D) qs[tid] = bf16_to_f32(p.q[(size_t)bh * D + tid]);
+  if (tid < D) qs[tid] = qv;
   __syncthreads();
+  // Fixed-point scale of the digits, from |q|_2 while R is still arriving:
+  // every |q_rot_j| <= |q|_2 |R e_j|_2 = |q|_2 for an orthogonal R, and the
+  // factor 2 covers the rounding of R and of the sums.  kq is the power of
+  // two with 16 * 2|q|_2 * kq <= 2^30; products are clamped to that range.
+  float sq = 0.0f;
+#pragma unroll
+  for (int i = tid % kWave; i < D; i += kWave) sq = fmaf(qs[i], qs[i], sq);
+  const float bound = 2.0f * sqrtf(wave_sum_dpp(sq));
+  float kq = 1.0f;
+  if (bound > 0.0f) {
+    kq = exp2f(floorf(log2f(kFix / (16.0f * bound))));
+    if (16.0f * bound * kq > kFix) kq *= 0.5f;
+  }
   float4 a4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
   for (int k = 0; k < IP; ++k) a4 = f4_fma(qs[part * IP + k], r[k], a4);
@@ -965,31 +988,11 @@ __device__ __forceinline__ void rotate_query_block(const DecodeDev& p, int bh) {
   if (tid < D) {
 #pragma unroll
     for (int q = 0; q < P; ++q) acc += part_s[q][tid];
-  }
-  const float amax = wave_max(tid < D ? fabsf(acc) : 0.0f);
-  const float asum = wave_sum(tid < D ? acc : 0.0f);
-  if ((tid & (kWave - 1)) == 0) {
-    red[0][tid / kWave] = amax;
-    red[1][tid / kWave] = asum;
-  }
-  __syncthreads();
-  float maxabs = 0.0f, qsum = 0.0f;
-#pragma unroll
-  for (int w = 0; w < D / kWave; ++w) {
-    maxabs = fmaxf(maxabs, red[0][w]);
-    qsum += red[1][w];
-  }
-  // kq: power of two with 16 * maxabs * kq <= 2^30
-  float kq = 1.0f;
-  if (maxabs > 0.0f) {
-    kq = exp2f(floorf(log2f(kFix / (16.0f * maxabs))));
-    if (16.0f * maxabs * kq > kFix) kq *= 0.5f;
-  }
-  if (tid < D) {
     const int pp = tid & 3;                     // mask index of channel tid
     // the plane factor cancels the operand's in-place weight (Lloyd-Max operands carry none)
     const float scale = kq * ((pp == 0 || p.lm) ? 16.0f : pp == 1 ? 4.0f : 1.0f);
-    const uint32_t U = balanced_digits((uint32_t)(int)rintf(acc * scale));
+    const float fx = fminf(fmaxf(rintf(acc * scale), -kFix), kFix);
+    const uint32_t U = balanced_digits((uint32_t)(int)fx);
     const int ib = tid >> 2;                    // code-row byte of channel tid
     const int kb = ib / PLANE, rem = ib % PLANE, c = rem >> 2, bb = rem & 3;
     const int nb = hl >> 2, hr = hl & 3;
@@ -1000,11 +1003,18 @@ __device__ __forceinline__ void rotate_query_block(const DecodeDev& p, int bh) {
       base[lane * 16 + 4 * pp + bb] = (uint8_t)(U >> (8 * dj));
     }
   }
+  // sum of q_rot over each wave's 64 channels (a 64-channel group), after the digit stores
+  const float ws = wave_sum_dpp(acc);
+  if (tid < D && (tid & (kWave - 1)) == 0) wsum[tid / kWave] = ws;
+  __syncthreads();
   if (tid == 0) {
+    float qsum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < D / kWave; ++w) qsum += wsum[w];
     p.qa[bh] = p.sm_log2 / (16.0f * kq);
-    // sum of q_rot over the head, or over each 64-channel group (one wave each)
-    p.qb[2 * bh] = p.sm_log2 * (p.ng == 2 ? red[1][0] : qsum);
-    p.qb[2 * bh + 1] = p.ng == 2 ? p.sm_log2 * red[1][1] : 0.0f;
+    // sum of q_rot over the head, or over each 64-channel group
+    p.qb[2 * bh] = p.sm_log2 * (p.ng == 2 ? wsum[0] : qsum);
+    p.qb[2 * bh + 1] = p.ng == 2 ? p.sm_log2 * wsum[1] : 0.0f;
   }
 }
 
