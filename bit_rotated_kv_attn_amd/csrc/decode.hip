@@ -939,12 +939,18 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
 // ---------------------------------------------------------------------------
 // 1. rotate the query: q_rot = q R_K[g]; MFMA digit operands and constants
 // ---------------------------------------------------------------------------
-// Sum over the 64 lanes of a wave (every lane active), in every lane: DPP row
-// sums, then the four rows read into scalar registers.
+// Sum / maximum over the 64 lanes of a wave (every lane active), in every
+// lane: DPP row reductions, then the four rows read into scalar registers.
 __device__ __forceinline__ float wave_sum_dpp(float v) {
   v = group16_sum(v);
   auto lane_val = [&](int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); };
   return (lane_val(0) + lane_val(16)) + (lane_val(32) + lane_val(48));
+}
+
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = group16_max(v);
+  auto lane_val = [&](int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); };
+  return fmaxf(fmaxf(lane_val(0), lane_val(16)), fmaxf(lane_val(32), lane_val(48)));
 }
 
 template <int D>
@@ -968,15 +974,25 @@ __device__ __forceinline__ void rotate_query_block(const DecodeDev& p, int bh) {
   __syncthreads();
   // Fixed-point scale of the digits, from |q|_2 while R is still arriving:
   // every |q_rot_j| <= |q|_2 |R e_j|_2 = |q|_2 for an orthogonal R, and the
-  // factor 2 covers the rounding of R and of the sums.  kq is the power of
-  // two with 16 * 2|q|_2 * kq <= 2^30; products are clamped to that range.
-  float sq = 0.0f;
+  // factor 2 covers the rounding of R and of the sums.  The norm is taken as
+  // 2^e |q 2^-e|_2 with 2^e <= max|q_i| < 2^(e+1), so its square neither
+  // overflows nor underflows.  kq is the power of two with
+  // 16 * 2|q|_2 * kq <= 2^30 (at most 2^100); products are clamped to that range.
+  float qm = 0.0f;
 #pragma unroll
-  for (int i = tid % kWave; i < D; i += kWave) sq = fmaf(qs[i], qs[i], sq);
-  const float bound = 2.0f * sqrtf(wave_sum_dpp(sq));
+  for (int i = tid % kWave; i < D; i += kWave) qm = fmaxf(qm, fabsf(qs[i]));
+  qm = wave_max_dpp(qm);
   float kq = 1.0f;
-  if (bound > 0.0f) {
-    kq = exp2f(floorf(log2f(kFix / (16.0f * bound))));
+  if (qm > 0.0f) {
+    const int e = ilogbf(qm);
+    float sq = 0.0f;
+#pragma unroll
+    for (int i = tid % kWave; i < D; i += kWave) {
+      const float t = ldexpf(qs[i], -e);
+      sq = fmaf(t, t, sq);
+    }
+    const float bound = 2.0f * ldexpf(sqrtf(wave_sum_dpp(sq)), e);
+    kq = fminf(exp2f(floorf(log2f(kFix / (16.0f * bound)))), 0x1p100f);
     if (16.0f * bound * kq > kFix) kq *= 0.5f;
   }
   float4 a4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);

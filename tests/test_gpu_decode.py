@@ -66,6 +66,21 @@ def test_large_batch_merge(G, d):
     compare_out(got, ref, what=f"large batch G={G} d={d}")
 
 
+@pytest.mark.parametrize("log2_scale", [-100, 0, 64])
+def test_query_scale_extremes(log2_scale):
+    """q scaled by a power of two far from 1 (exact in bf16): the fixed-point
+    scale of the rotated query is taken from the query's norm, which must
+    neither overflow (|q| near 2^64: |q|^2 is past the fp32 range) nor
+    underflow (|q| near 2^-100).  At 2^64 the softmax is one-hot."""
+    cfg, pools = ragged_cache(5, B=2, n_kv=2, G=4, d=128, sink=(64, 3), hist=(300, 130), recent=(256, 7))
+    q = (cfg["q"].astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** log2_scale)
+    cfg["q"] = (q.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.isfinite(q).all() and (q[q != 0] != 0).all()
+    ref = oracle.decode_attn_ref(cfg, *pools)
+    got = gpu_decode(cfg, pools)
+    compare_out(got, ref, what=f"q scaled by 2^{log2_scale}")
+
+
 def test_empty_context_rows_are_zero():
     cfg, pools = ragged_cache(3, B=2, n_kv=1, G=4, d=64, sink=(0, 3), hist=(0, 70), recent=(0, 2))
     got = gpu_decode(cfg, pools)
