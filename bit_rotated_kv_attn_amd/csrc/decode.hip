@@ -75,7 +75,7 @@ struct DecodeDev {
   float* out;
   uint8_t* qdig;     // [B][n_kv][NB][D/64][64 lanes][16 bytes] QK A operands
   float *qa, *qb;    // logit constants: qa [B][Hq] = sm_log2/(16 kq); qb [B][Hq][2] = sm_log2 * sum(q_rot)
-                     // over the whole head (qb[..][1] = 0), or over channels 0..63 and 64..127
+                     // over channels 0..D/2-1 and D/2..D-1 (the two 64-channel groups when D = 128)
   float *hpart, *bpart;
 };
 
@@ -586,6 +586,10 @@ __device__ __forceinline__ void load_hist_operands(const DecodeDev& p, int b, in
     o.ca[nb] = hout < G ? p.qa[h_base + hout] : 0.0f;
 #pragma unroll
     for (int j = 0; j < 2; ++j) o.cb[nb][j] = hout < G ? p.qb[2 * (h_base + hout) + j] : 0.0f;
+    if (p.ng == 1) {   // one group: the sum over both halves of the head
+      o.cb[nb][0] += o.cb[nb][1];
+      o.cb[nb][1] = 0.0f;
+    }
     const bool row_ok = 4 * nb + (n >> 2) < G;   // head of the A row this lane supplies
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -608,6 +612,10 @@ __device__ __forceinline__ void load_pair_operands(const DecodeDev& p, int b, in
     o.ca[nb] = p.qa[(size_t)(b + nb) * p.Hq + g * 4 + grp];
 #pragma unroll
     for (int j = 0; j < 2; ++j) o.cb[nb][j] = p.qb[2 * ((size_t)(b + nb) * p.Hq + g * 4 + grp) + j];
+    if (p.ng == 1) {
+      o.cb[nb][0] += o.cb[nb][1];
+      o.cb[nb][1] = 0.0f;
+    }
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
       o.qa[nb][c] = reinterpret_cast<const v4i*>(p.qdig)[((size_t)unit * NCH + c) * kWave + lane];
@@ -953,23 +961,28 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
   return fmaxf(fmaxf(lane_val(0), lane_val(16)), fmaxf(lane_val(32), lane_val(48)));
 }
 
+// Two blocks per query head, one per half of the output channels (half = 0
+// or 1): each reads half of R_K, and the digit scale needs no exchange
+// between them (it comes from |q|_2).  qb[2 bh + half] is the sum of q_rot
+// over the half's channels (a 64-channel group when head_dim is 128).
 template <int D>
-__device__ __forceinline__ void rotate_query_block(const DecodeDev& p, int bh) {
+__device__ __forceinline__ void rotate_query_block(const DecodeDev& p, int bh, int half) {
   constexpr int NCH = D / 64, PLANE = D / 16;
-  // thread (jq, part): columns 4jq..4jq+3 of rows part*IP .. part*IP+IP-1,
-  // loaded as IP 16-byte vectors all in flight at once
-  constexpr int QPR = D / 4, P = kBlock / QPR, IP = D / P;
+  constexpr int DH = D / 2;   // output channels of this block
+  // thread (jq, part): columns 4jq..4jq+3 of the half, rows part*IP ..
+  // part*IP+IP-1, loaded as IP 16-byte vectors all in flight at once
+  constexpr int QPR = DH / 4, P = kBlock / QPR, IP = D / P;
   __shared__ float qs[D];
-  __shared__ __attribute__((aligned(16))) float part_s[P][D];
-  __shared__ float wsum[kBlock / kWave];
+  __shared__ __attribute__((aligned(16))) float part_s[P][DH];
   const int b = bh / p.Hq, h = bh % p.Hq, g = h / p.G, hl = h % p.G;
   const int tid = threadIdx.x, jq = tid % QPR, part = tid / QPR;
   // q is requested before R, so waiting for it leaves the R loads in flight
   const float qv = tid < D ? bf16_to_f32(p.q[(size_t)bh * D + tid]) : 0.0f;
-  const float4* R = reinterpret_cast<const float4*>(p.r_k + (size_t)g * D * D + (size_t)part * IP * D) + jq;
+  const float4* R =
+      reinterpret_cast<const float4*>(p.r_k + (size_t)g * D * D + (size_t)part * IP * D + half * DH) + jq;
   float4 r[IP];
 #pragma unroll
-  for (int k = 0; k < IP; ++k) r[k] = R[(size_t)k * QPR];
+  for (int k = 0; k < IP; ++k) r[k] = R[(size_t)k * (D / 4)];
   if (tid < D) qs[tid] = qv;
   __syncthreads();
   // Fixed-point scale of the digits, from |q|_2 while R is still arriving:
@@ -1001,15 +1014,16 @@ __device__ __forceinline__ void rotate_query_block(const DecodeDev& p, int bh) {
   reinterpret_cast<float4*>(part_s[part])[jq] = a4;
   __syncthreads();
   float acc = 0.0f;
-  if (tid < D) {
+  if (tid < DH) {
+    const int ch = half * DH + tid;             // output channel of this thread
 #pragma unroll
     for (int q = 0; q < P; ++q) acc += part_s[q][tid];
-    const int pp = tid & 3;                     // mask index of channel tid
+    const int pp = ch & 3;                      // mask index of channel ch
     // the plane factor cancels the operand's in-place weight (Lloyd-Max operands carry none)
     const float scale = kq * ((pp == 0 || p.lm) ? 16.0f : pp == 1 ? 4.0f : 1.0f);
     const float fx = fminf(fmaxf(rintf(acc * scale), -kFix), kFix);
     const uint32_t U = balanced_digits((uint32_t)(int)fx);
-    const int ib = tid >> 2;                    // code-row byte of channel tid
+    const int ib = ch >> 2;                     // code-row byte of channel ch
     const int kb = ib / PLANE, rem = ib % PLANE, c = rem >> 2, bb = rem & 3;
     const int nb = hl >> 2, hr = hl & 3;
     uint8_t* base = p.qdig + ((((size_t)b * p.n_kv + g) * p.NB + nb) * NCH + c) * kWave * 16;
@@ -1019,25 +1033,18 @@ __device__ __forceinline__ void rotate_query_block(const DecodeDev& p, int bh) {
       base[lane * 16 + 4 * pp + bb] = (uint8_t)(U >> (8 * dj));
     }
   }
-  // sum of q_rot over each wave's 64 channels (a 64-channel group), after the digit stores
+  // sum of q_rot over the half's channels (tid < DH <= 64: wave 0), after the digit stores
   const float ws = wave_sum_dpp(acc);
-  if (tid < D && (tid & (kWave - 1)) == 0) wsum[tid / kWave] = ws;
-  __syncthreads();
   if (tid == 0) {
-    float qsum = 0.0f;
-#pragma unroll
-    for (int w = 0; w < D / kWave; ++w) qsum += wsum[w];
-    p.qa[bh] = p.sm_log2 / (16.0f * kq);
-    // sum of q_rot over the head, or over each 64-channel group
-    p.qb[2 * bh] = p.sm_log2 * (p.ng == 2 ? wsum[0] : qsum);
-    p.qb[2 * bh + 1] = p.ng == 2 ? p.sm_log2 * wsum[1] : 0.0f;
+    if (half == 0) p.qa[bh] = p.sm_log2 / (16.0f * kq);
+    p.qb[2 * bh + half] = p.sm_log2 * ws;
   }
 }
 
-// Launch 1 of a decode: one block per query head rotates q.
+// Launch 1 of a decode: two blocks per query head rotate q.
 template <int D>
 __global__ __launch_bounds__(kBlock) void prepare_kernel(DecodeDev p) {
-  rotate_query_block<D>(p, blockIdx.x);
+  rotate_query_block<D>(p, blockIdx.x >> 1, blockIdx.x & 1);
 }
 
 // Block `id` of a decode step's demotions: the step's K tokens first, then
@@ -1647,8 +1654,8 @@ hipError_t launch_decode_phase(int phase, const oscar_decode_args& a, const Deco
   const bool d128 = a.head_dim == 128;
   if (phase == kPhaseRotate) {
     if (plan.splits > 0 && nbh > 0) {
-      if (d128) prepare_kernel<128><<<nbh, kBlock, 0, stream>>>(dv);
-      else prepare_kernel<64><<<nbh, kBlock, 0, stream>>>(dv);
+      if (d128) prepare_kernel<128><<<2 * nbh, kBlock, 0, stream>>>(dv);
+      else prepare_kernel<64><<<2 * nbh, kBlock, 0, stream>>>(dv);
     }
   } else if (phase == kPhaseMerge) {
     const DemoteDev mk = make_demote(demote_k), mv = make_demote(demote_v);
