@@ -63,12 +63,14 @@ def test_decode_step_matches_separate_oracle_steps(shape, codebook, groups):
     out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
     rk, rv, rec_k, rec_v = dev(cfg["r_k"]), dev(cfg["r_v"]), dev(cfg["recent_k"]), dev(cfg["recent_v"])
     src_t, slot_t = dev(src), dev(slot)
-    args = hip.decode_args(q=dev(cfg["q"]), sink_k=dev(cfg["sink_k"]), sink_v=dev(cfg["sink_v"]), recent_k=rec_k,
-                           recent_v=rec_v, sink_len=dev(cfg["sink_len"]), recent_len=dev(cfg["recent_len"]),
-                           hist_len=dev(cfg["hist_len"]), max_hist_len=int(cfg["hist_len"].max()),
-                           k_codes=pools[0], v_codes=pools[1], k_sz=pools[2], v_sz=pools[3],
-                           block_table=dev(cfg["block_table"]), r_k=rk, r_v=rv, out=out, workspace=ws,
-                           sm_scale=float(cfg["sm_scale"]), codebook=CODEBOOK_FLAG[codebook], group_channels=groups)
+    # decode_args and demote_args keep raw pointers: every tensor stays referenced until the step ran
+    t = {k: dev(cfg[k]) for k in ("q", "sink_k", "sink_v", "sink_len", "recent_len", "hist_len", "block_table")}
+    args = hip.decode_args(q=t["q"], sink_k=t["sink_k"], sink_v=t["sink_v"], recent_k=rec_k, recent_v=rec_v,
+                           sink_len=t["sink_len"], recent_len=t["recent_len"], hist_len=t["hist_len"],
+                           max_hist_len=int(cfg["hist_len"].max()), k_codes=pools[0], v_codes=pools[1],
+                           k_sz=pools[2], v_sz=pools[3], block_table=t["block_table"], r_k=rk, r_v=rv, out=out,
+                           workspace=ws, sm_scale=float(cfg["sm_scale"]), codebook=CODEBOOK_FLAG[codebook],
+                           group_channels=groups)
     common = dict(src_idx=src_t, n_src=B * n_kv * cap, x_tok_stride=d, x_head_stride=cap * d)
     dk = hip.demote_args(x=rec_k, rot=rk, clip=float(cfg["tau_k"]), dst_slot=slot_t, codes=pools[0],
                          scale_zero=pools[2], **common)
@@ -89,15 +91,17 @@ def test_decode_step_without_demotion_equals_decode():
     ws = torch.zeros(hip.oscar_decode_workspace_bytes(B, Hq, cfg["n_kv"], d, int(cfg["hist_len"].max()), 64, cap),
                      dtype=torch.uint8, device="cuda")
     outs = []
+    # decode_args keeps raw pointers: the tensors stay referenced until the calls ran
+    t = {k: dev(cfg[k]) for k in ("q", "sink_k", "sink_v", "recent_k", "recent_v", "sink_len", "recent_len",
+                                  "hist_len", "block_table", "r_k", "r_v")}
     for use_step in (False, True):
         out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
-        args = hip.decode_args(q=dev(cfg["q"]), sink_k=dev(cfg["sink_k"]), sink_v=dev(cfg["sink_v"]),
-                               recent_k=dev(cfg["recent_k"]), recent_v=dev(cfg["recent_v"]),
-                               sink_len=dev(cfg["sink_len"]), recent_len=dev(cfg["recent_len"]),
-                               hist_len=dev(cfg["hist_len"]), max_hist_len=int(cfg["hist_len"].max()),
+        args = hip.decode_args(q=t["q"], sink_k=t["sink_k"], sink_v=t["sink_v"], recent_k=t["recent_k"],
+                               recent_v=t["recent_v"], sink_len=t["sink_len"], recent_len=t["recent_len"],
+                               hist_len=t["hist_len"], max_hist_len=int(cfg["hist_len"].max()),
                                k_codes=pools[0], v_codes=pools[1], k_sz=pools[2], v_sz=pools[3],
-                               block_table=dev(cfg["block_table"]), r_k=dev(cfg["r_k"]), r_v=dev(cfg["r_v"]),
-                               out=out, workspace=ws, sm_scale=float(cfg["sm_scale"]))
+                               block_table=t["block_table"], r_k=t["r_k"], r_v=t["r_v"], out=out, workspace=ws,
+                               sm_scale=float(cfg["sm_scale"]))
         if use_step:
             hip.oscar_decode_step(args=args)
         else:
@@ -105,3 +109,44 @@ def test_decode_step_without_demotion_equals_decode():
         torch.cuda.synchronize()
         outs.append(host(out))
     assert np.array_equal(outs[0], outs[1])
+
+
+def test_decode_step_with_no_requests_only_demotes():
+    """Batch 0: the q-rotation and scan launches have no blocks, and the merge
+    launch holds only the demotion blocks.  The pools must equal the oracle
+    quantiser's output for the demoted tokens."""
+    cfg = synth.make_decode_config(0)
+    n_kv, d, P = cfg["n_kv"], cfg["head_dim"], cfg["n_pages"]
+    Hq = cfg["q"].shape[1]
+    n_tok = 7
+    pick = np.array([0, 5, 64, 65, 130, 300, 703], dtype=np.int32)[:n_tok]
+    slot = cfg["hist_slot"][pick].astype(np.int32)
+    kc_ref = np.zeros((P, n_kv, PAGE * d // 4), np.uint8)
+    vc_ref = np.zeros_like(kc_ref)
+    ks_ref = np.zeros((P, n_kv, PAGE, 2), np.uint16)
+    vs_ref = np.zeros_like(ks_ref)
+    dk_ref = oracle.quantize_pack_ref("k", cfg["hist_k"][pick], cfg["r_k"], cfg["tau_k"], slot, kc_ref, ks_ref)
+    dv_ref = oracle.quantize_pack_ref("v", cfg["hist_v"][pick], cfg["r_v"], cfg["tau_v"], slot, vc_ref, vs_ref)
+
+    pools = [dev(np.zeros_like(a)) for a in (kc_ref, vc_ref, ks_ref, vs_ref)]
+    rk, rv = dev(cfg["r_k"]), dev(cfg["r_v"])
+    e16 = lambda *s: torch.zeros(s, dtype=torch.int16, device="cuda")
+    e32 = lambda *s: torch.zeros(s, dtype=torch.int32, device="cuda")
+    out = torch.zeros((0, Hq, d), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(max(1, hip.oscar_decode_workspace_bytes(0, Hq, n_kv, d, 0, 64, 256)), dtype=torch.uint8,
+                     device="cuda")
+    args = hip.decode_args(q=e16(0, Hq, d), sink_k=e16(0, n_kv, 64, d), sink_v=e16(0, n_kv, 64, d),
+                           recent_k=e16(0, n_kv, 256, d), recent_v=e16(0, n_kv, 256, d), sink_len=e32(0),
+                           recent_len=e32(0), hist_len=e32(0), max_hist_len=0, k_codes=pools[0],
+                           v_codes=pools[1], k_sz=pools[2], v_sz=pools[3], block_table=e32(0, 1), r_k=rk,
+                           r_v=rv, out=out, workspace=ws)
+    # demote_args keeps raw pointers: the tensors must outlive the call
+    xk, xv, slot_t = dev(cfg["hist_k"][pick]), dev(cfg["hist_v"][pick]), dev(slot)
+    dk = hip.demote_args(x=xk, rot=rk, clip=float(cfg["tau_k"]), dst_slot=slot_t, codes=pools[0],
+                         scale_zero=pools[2])
+    dv = hip.demote_args(x=xv, rot=rv, clip=float(cfg["tau_v"]), dst_slot=slot_t, codes=pools[1],
+                         scale_zero=pools[3])
+    hip.oscar_decode_step(args=args, demote_k=dk, demote_v=dv)
+    torch.cuda.synchronize()
+    compare_quant("k", host(pools[0]), host(pools[2], np.uint16), kc_ref, ks_ref, dk_ref, d)
+    compare_quant("v", host(pools[1]), host(pools[3], np.uint16), vc_ref, vs_ref, dv_ref, d)
