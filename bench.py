@@ -182,6 +182,16 @@ def main():
         torch.cuda.synchronize()
         return g
 
+    def timed_fn(fn):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3, time.perf_counter() - w0
+
     def timed(graph_all, graph_rem, n_full):
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -284,6 +294,21 @@ def main():
         result["speedup_int2_vs_bf16_decode"] = bf_us / dec_us
         log(f"bf16 comparator: {bf_us:.2f} us/decode; INT2 decode speedup {bf_us / dec_us:.2f}x")
         del bre, kp0, vp0
+
+    # ---- what this part's HBM sustains for a plain stream: a 1 GiB device copy
+    # (512 MiB read + 512 MiB written per torch.neg), beside the spec peak of the roofline
+    n = (512 << 20) // 4
+    src = torch.randn(n, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        torch.neg(src, out=dst)
+    reps_copy = 10
+    copy_sec, _ = timed_fn(lambda: [torch.neg(src, out=dst) for _ in range(reps_copy)])
+    copy_gbs = 2 * n * 4 * reps_copy / copy_sec / 1e9
+    result["hbm_copy_probe"] = {"GBps": copy_gbs, "bytes_per_copy": 2 * n * 4, "kernel": "torch.neg",
+                                "scan_frac_of_copy": achieved / copy_gbs}
+    log(f"copy probe: {copy_gbs:.0f} GB/s; the scan reaches {achieved / copy_gbs:.1%} of it")
+    del src, dst
 
     # ---- CPU oracle on a bounded sample (reported baseline, not a target)
     if not args.no_cpu_baseline:
