@@ -119,29 +119,6 @@ struct Bf16Dev {
   float *out, *part;
 };
 
-// Reductions over the 16 lanes of a DPP row (lanes 16k..16k+15), every lane
-// receiving the result: quad permutes (lane ^ 1, lane ^ 2), then the half-row
-// and row mirrors.  VALU data movement, no LDS round trips.
-template <int kCtrl>
-__device__ __forceinline__ float dpp_f32(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
-}
-constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
-
-__device__ __forceinline__ float group16_max(float v) {
-  v = fmaxf(v, dpp_f32<kDppXor1>(v));
-  v = fmaxf(v, dpp_f32<kDppXor2>(v));
-  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
-  return fmaxf(v, dpp_f32<kDppMirror>(v));
-}
-
-__device__ __forceinline__ float group16_sum(float v) {
-  v += dpp_f32<kDppXor1>(v);
-  v += dpp_f32<kDppXor2>(v);
-  v += dpp_f32<kDppHalfMirror>(v);
-  return v + dpp_f32<kDppMirror>(v);
-}
-
 // operand mask p of a raw code word: bytes hold field p of each byte (x1, x4, x16, x16)
 __device__ __forceinline__ int code_mask(uint32_t w, int p) {
   return (int)(p == 0 ? (w & kMask0) : p == 1 ? (w & kMask1) : p == 2 ? (w & kMask2) : ((w >> 2) & kMask2));
@@ -947,20 +924,6 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
 // ---------------------------------------------------------------------------
 // 1. rotate the query: q_rot = q R_K[g]; MFMA digit operands and constants
 // ---------------------------------------------------------------------------
-// Sum / maximum over the 64 lanes of a wave (every lane active), in every
-// lane: DPP row reductions, then the four rows read into scalar registers.
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-  v = group16_sum(v);
-  auto lane_val = [&](int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); };
-  return (lane_val(0) + lane_val(16)) + (lane_val(32) + lane_val(48));
-}
-
-__device__ __forceinline__ float wave_max_dpp(float v) {
-  v = group16_max(v);
-  auto lane_val = [&](int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); };
-  return fmaxf(fmaxf(lane_val(0), lane_val(16)), fmaxf(lane_val(32), lane_val(48)));
-}
-
 // Two blocks per query head, one per half of the output channels (half = 0
 // or 1): each reads half of R_K, and the digit scale needs no exchange
 // between them (it comes from |q|_2).  qb[2 bh + half] is the sum of q_rot
@@ -994,7 +957,7 @@ __device__ __forceinline__ void rotate_query_block(const DecodeDev& p, int bh, i
   float qm = 0.0f;
 #pragma unroll
   for (int i = tid % kWave; i < D; i += kWave) qm = fmaxf(qm, fabsf(qs[i]));
-  qm = wave_max_dpp(qm);
+  qm = wave_max(qm);
   float kq = 1.0f;
   if (qm > 0.0f) {
     const int e = ilogbf(qm);
@@ -1004,7 +967,7 @@ __device__ __forceinline__ void rotate_query_block(const DecodeDev& p, int bh, i
       const float t = ldexpf(qs[i], -e);
       sq = fmaf(t, t, sq);
     }
-    const float bound = 2.0f * ldexpf(sqrtf(wave_sum_dpp(sq)), e);
+    const float bound = 2.0f * ldexpf(sqrtf(wave_sum(sq)), e);
     kq = fminf(exp2f(floorf(log2f(kFix / (16.0f * bound)))), 0x1p100f);
     if (16.0f * bound * kq > kFix) kq *= 0.5f;
   }
@@ -1034,7 +997,7 @@ __device__ __forceinline__ void rotate_query_block(const DecodeDev& p, int bh, i
     }
   }
   // sum of q_rot over the half's channels (tid < DH <= 64: wave 0), after the digit stores
-  const float ws = wave_sum_dpp(acc);
+  const float ws = wave_sum(acc);
   if (tid == 0) {
     if (half == 0) p.qa[bh] = p.sm_log2 / (16.0f * kq);
     p.qb[2 * bh + half] = p.sm_log2 * ws;

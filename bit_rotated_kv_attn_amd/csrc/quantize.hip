@@ -8,10 +8,10 @@
 // technical summary, section 2.2A.
 //
 // Block = (tile of 32 tokens, one KV head).  R[g] columns are read once per
-// block and reused for the tile.  The rotation accumulates in fp64 (the
-// bf16 x fp32 products are exact in fp64) and rounds once to fp32, so every
-// later decision (clip, min/max, fp16 rounding of scale/zero, the code) is
-// taken on the correctly rounded fp32 rotated value.
+// block and reused for the tile.  The rotation accumulates in fp64 on the
+// matrix cores (the bf16 x fp32 products are exact in fp64) and rounds once
+// to fp32, so every later decision (clip, min/max, fp16 rounding of
+// scale/zero, the code) is taken on the correctly rounded fp32 rotated value.
 #include "common.hpp"
 #include "demote.hpp"
 
@@ -19,6 +19,8 @@ namespace oscar {
 namespace {
 
 constexpr int kQTok = 32;  // tokens per block
+
+typedef double v4d __attribute__((ext_vector_type(4)));
 
 template <int D>
 __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(
@@ -28,7 +30,7 @@ __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(
     uint8_t* __restrict__ codes, uint32_t* __restrict__ sz, int64_t n_pages) {
   constexpr int kRowBytes = D / 4;       // code bytes per token
   constexpr int kPlane = D / 16;         // bytes per token in one K plane
-  __shared__ __attribute__((aligned(16))) float xs[D][kQTok];   // x tile, channel-major (broadcast reads)
+  __shared__ float xs[D][kQTok + 1];     // x tile, channel-major (padded: conflict-free transposed writes)
   __shared__ float ys[kQTok][D + 1];     // clipped rotated values
   __shared__ int64_t src_s[kQTok];
   __shared__ int64_t dst_s[kQTok];       // -1: skip this token
@@ -58,43 +60,64 @@ __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(
   }
   __syncthreads();
 
-  for (int e = tid; e < kQTok * D; e += kBlock) {
-    const int t = e / D, c = e % D;
+  // x tile: thread (t, chunk) loads channels 8 chunk .. 8 chunk + 7 of token t
+  // as one 16-byte vector when the row is 16-byte aligned, else element by element
+  for (int e = tid; e < kQTok * (D / 8); e += kBlock) {
+    const int t = e / (D / 8), c0 = 8 * (e % (D / 8));
     const int64_t s = src_s[t];
-    xs[c][t] = (s >= 0) ? bf16_to_f32(x[s * tok_stride + (int64_t)g * head_stride + c]) : 0.0f;
+    float v[8];
+    if (s < 0) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = 0.0f;
+    } else {
+      const uint16_t* src = x + s * tok_stride + (int64_t)g * head_stride + c0;
+      if ((reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+        const uint4 w = *reinterpret_cast<const uint4*>(src);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          v[2 * k] = bf16_to_f32(ww[k] & 0xffffu);
+          v[2 * k + 1] = bf16_to_f32(ww[k] >> 16);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = bf16_to_f32(src[k]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) xs[c0 + k][t] = v[k];
   }
   __syncthreads();
 
-  // y[t][j] = sum_i x[t][i] * R[i][j], each output accumulated over i in
-  // order with fp64 FMAs.  Thread (cg, tg) owns columns C*cg .. C*cg+C-1 of
-  // tokens 4tg .. 4tg+3, so each converted R and x value feeds C or 4 FMAs.
-  constexpr int C = D / 32;              // columns per thread (4 for d = 128, 2 for d = 64)
-  static_assert(32 * (kQTok / 4) == kBlock, "32 column groups x 8 token groups");
-  const int cg = tid % 32, tg = tid / 32;
-  const float* R = rot + (size_t)g * D * D + C * cg;
-  double acc[C][4];
+  // y[t][j] = sum_i x[t][i] * R[i][j] in fp64 on the matrix cores
+  // (v_mfma_f64_16x16x4_f64: A[row][k] in lane row + 16k, B[k][col] in lane
+  // col + 16k, D[row][col] in element row / 4 of lane col + 16 (row % 4)).
+  // The bf16 x fp32 products are exact in fp64, and the sums are fp64, then
+  // rounded once to fp32.  Wave w computes tokens 16 (w % 2) .. + 15 and the
+  // NT column tiles of 16 starting at NT (w / 2).
+  constexpr int NT = D / 32;             // column tiles per wave (4 for d = 128, 2 for d = 64)
+  static_assert(kQTok == 32 && kBlock == 256, "2 token tiles x 2 column halves, one per wave");
+  {
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    const int mt = wave & 1, nt0 = NT * (wave >> 1);
+    const int row = lane & 15, kk = lane >> 4;
+    const float* R = rot + (size_t)g * D * D + 16 * nt0 + row;
+    v4d acc[NT];
 #pragma unroll
-  for (int c = 0; c < C; ++c)
+    for (int n = 0; n < NT; ++n) acc[n] = v4d{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+    for (int k0 = 0; k0 < D; k0 += 4) {
+      const double a = (double)xs[k0 + kk][16 * mt + row];
+      const float* Rk = R + (size_t)(k0 + kk) * D;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[c][t] = 0.0;
-  for (int i = 0; i < D; ++i) {
-    double rd[C], xd[4];
+      for (int n = 0; n < NT; ++n) acc[n] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)Rk[16 * n], acc[n], 0, 0, 0);
+    }
 #pragma unroll
-    for (int c = 0; c < C; ++c) rd[c] = (double)R[(size_t)i * D + c];
-    const float4 xv = *reinterpret_cast<const float4*>(&xs[i][4 * tg]);
-    xd[0] = (double)xv.x;
-    xd[1] = (double)xv.y;
-    xd[2] = (double)xv.z;
-    xd[3] = (double)xv.w;
+    for (int n = 0; n < NT; ++n)
 #pragma unroll
-    for (int c = 0; c < C; ++c)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) acc[c][t] = fma(xd[t], rd[c], acc[c][t]);
+      for (int r = 0; r < 4; ++r)
+        ys[16 * mt + kk + 4 * r][16 * (nt0 + n) + row] = fminf(fmaxf((float)acc[n][r], -clip), clip);
   }
-#pragma unroll
-  for (int c = 0; c < C; ++c)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) ys[4 * tg + t][C * cg + c] = fminf(fmaxf((float)acc[c][t], -clip), clip);
   __syncthreads();
 
   // per-token group statistics: zero = fp16(min), scale = fp16((max - min) / 3),
