@@ -30,8 +30,13 @@ __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(
     uint8_t* __restrict__ codes, uint32_t* __restrict__ sz, int64_t n_pages) {
   constexpr int kRowBytes = D / 4;       // code bytes per token
   constexpr int kPlane = D / 16;         // bytes per token in one K plane
-  __shared__ float xs[D][kQTok + 1];     // x tile, channel-major (padded: conflict-free transposed writes)
-  __shared__ float ys[kQTok][D + 1];     // clipped rotated values
+  // The x tile (channel-major, padded so the transposed writes are conflict-free)
+  // and, once every wave's products are done, the clipped rotated values share
+  // one LDS buffer.
+  constexpr int kXs = D * (kQTok + 1), kYs = kQTok * (D + 1);
+  __shared__ float tile[kXs > kYs ? kXs : kYs];
+  float (*xs)[kQTok + 1] = reinterpret_cast<float (*)[kQTok + 1]>(tile);
+  float (*ys)[D + 1] = reinterpret_cast<float (*)[D + 1]>(tile);
   __shared__ int64_t src_s[kQTok];
   __shared__ int64_t dst_s[kQTok];       // -1: skip this token
   constexpr int kPer = D / kWave;        // channels per lane in the statistics (channel lane + 64k)
@@ -112,6 +117,7 @@ __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(
 #pragma unroll
       for (int n = 0; n < NT; ++n) acc[n] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)Rk[16 * n], acc[n], 0, 0, 0);
     }
+    __syncthreads();   // every wave has read the x tile: its LDS now takes the rotated values
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
