@@ -98,31 +98,40 @@ __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(
   // (v_mfma_f64_16x16x4_f64: A[row][k] in lane row + 16k, B[k][col] in lane
   // col + 16k, D[row][col] in element row / 4 of lane col + 16 (row % 4)).
   // The bf16 x fp32 products are exact in fp64, and the sums are fp64, then
-  // rounded once to fp32.  Wave w computes tokens 16 (w % 2) .. + 15 and the
-  // NT column tiles of 16 starting at NT (w / 2).
-  constexpr int NT = D / 32;             // column tiles per wave (4 for d = 128, 2 for d = 64)
-  static_assert(kQTok == 32 && kBlock == 256, "2 token tiles x 2 column halves, one per wave");
+  // rounded once to fp32.  Wave w computes both 16-token tiles for the NT
+  // column tiles of 16 starting at NT w, so each element of R is read by one
+  // wave of the block.
+  constexpr int NT = D / 64;             // column tiles per wave (2 for d = 128, 1 for d = 64)
+  static_assert(kQTok == 32 && kBlock == 256, "2 token tiles x 4 column quarters, one quarter per wave");
   {
     const int lane = tid & (kWave - 1), wave = tid / kWave;
-    const int mt = wave & 1, nt0 = NT * (wave >> 1);
+    const int nt0 = NT * wave;
     const int row = lane & 15, kk = lane >> 4;
     const float* R = rot + (size_t)g * D * D + 16 * nt0 + row;
-    v4d acc[NT];
+    v4d acc[2][NT];
 #pragma unroll
-    for (int n = 0; n < NT; ++n) acc[n] = v4d{0.0, 0.0, 0.0, 0.0};
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[m][n] = v4d{0.0, 0.0, 0.0, 0.0};
 #pragma unroll 4
     for (int k0 = 0; k0 < D; k0 += 4) {
-      const double a = (double)xs[k0 + kk][16 * mt + row];
+      const double a0 = (double)xs[k0 + kk][row], a1 = (double)xs[k0 + kk][16 + row];
       const float* Rk = R + (size_t)(k0 + kk) * D;
 #pragma unroll
-      for (int n = 0; n < NT; ++n) acc[n] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)Rk[16 * n], acc[n], 0, 0, 0);
+      for (int n = 0; n < NT; ++n) {
+        const double b = (double)Rk[16 * n];
+        acc[0][n] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b, acc[0][n], 0, 0, 0);
+        acc[1][n] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b, acc[1][n], 0, 0, 0);
+      }
     }
     __syncthreads();   // every wave has read the x tile: its LDS now takes the rotated values
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        ys[16 * mt + kk + 4 * r][16 * (nt0 + n) + row] = fminf(fmaxf((float)acc[n][r], -clip), clip);
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          ys[16 * m + kk + 4 * r][16 * (nt0 + n) + row] = fminf(fmaxf((float)acc[m][n][r], -clip), clip);
   }
   __syncthreads();
 
