@@ -93,6 +93,28 @@ def test_strided_source_recent_ring():
     compare_quant("k", host(codes), host(sz, np.uint16), ref[0], ref[1], ref[2], d)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_bulk_unaligned_source_rows(d):
+    """The 32-token tiles read a token's channels as 16-byte vectors only when
+    the row is 16-byte aligned: with a token stride of n_kv*d + 3 elements most
+    rows are not, and those are read element by element."""
+    import bit_rotated_kv_attn_amd as hip
+    n_tok, n_kv, n_pages = 150, 2, 4
+    rng, x, slots = _inputs(8, n_tok, n_kv, d, n_pages)
+    rot = np.stack([pins.random_orthogonal(d, rng) for _ in range(n_kv)])
+    stride = n_kv * d + 3
+    buf = np.zeros(n_tok * stride + 8, np.uint16)
+    for t in range(n_tok):
+        buf[t * stride: t * stride + n_kv * d] = x[t].reshape(-1)
+    codes, sz = empty_pools(n_pages, n_kv, d)
+    xb = dev(buf)
+    hip.oscar_quantize_pack(hip.KIND_V, xb, dev(rot), 3.0, dev(slots), codes, sz, n_src=n_tok,
+                            x_tok_stride=stride, x_head_stride=d)
+    torch.cuda.synchronize()
+    ref = _oracle("v", x, rot, 3.0, slots, n_pages)
+    compare_quant("v", host(codes), host(sz, np.uint16), ref[0], ref[1], ref[2], d)
+
+
 def test_zero_tokens_is_noop():
     import bit_rotated_kv_attn_amd as hip
     codes, sz = empty_pools(2, 1, 64)
