@@ -1282,34 +1282,36 @@ __device__ __forceinline__ float2 merge_head(PartPtr part_ptr, int n_rot, int nt
   return make_float2(M, L);
 }
 
-// The output rotation out_i = sum_j A_j R_V[i][j] with R_V read in whole
-// rows: thread t holds columns 4c..4c+3 (c = t % (D/4)) of rows
-// RPT*rb .. RPT*rb + RPT-1 (rb = t / (D/4)), so each load instruction of a
-// wave covers whole 512-byte rows (per-thread row segments would put every
-// lane of an instruction on its own cache line).  The dot products over a
-// row's column quads are then summed through LDS.
-template <int D>
+// The output rotation out_i = sum_j A_j R_V[i][j] for NR consecutive rows i
+// of R_V, read in whole rows: thread t holds columns 4c..4c+3 (c = t % (D/4))
+// of rows RPT*rb .. RPT*rb + RPT-1 (rb = t / (D/4)), so each load
+// instruction of a wave covers whole 512-byte rows (per-thread row segments
+// would put every lane of an instruction on its own cache line).  The dot
+// products over a row's column quads are then summed through LDS.
+template <int D, int NR = D>
 struct RvRows {
-  static constexpr int QPR = D / 4, RB = kBlock / QPR, RPT = D / RB, TPO = kBlock / D;
-  static constexpr int kStride = D + 1;   // red[c][row]: conflict-free writes and sums
+  static constexpr int QPR = D / 4, RB = kBlock / QPR, RPT = NR / RB, TPO = kBlock / NR;
+  static constexpr int kStride = NR + 1;   // red[c][row]: conflict-free writes and sums
   float4 v[RPT];
 };
 
-template <int D>
-__device__ __forceinline__ void load_rv_rows(RvRows<D>& r, const float* __restrict__ rv, int tid) {
-  using T = RvRows<D>;
+// rv: the first of the NR rows
+template <int D, int NR>
+__device__ __forceinline__ void load_rv_rows(RvRows<D, NR>& r, const float* __restrict__ rv, int tid) {
+  using T = RvRows<D, NR>;
   const int c = tid % T::QPR, rb = tid / T::QPR;
   const float4* src = reinterpret_cast<const float4*>(rv + (size_t)(T::RPT * rb) * D) + c;
 #pragma unroll
   for (int k = 0; k < T::RPT; ++k) r.v[k] = src[(size_t)k * T::QPR];
 }
 
-// out row i = tid / TPO of A (D floats in LDS) times R_V^T; every thread of
-// the row gets the value.  red: QPR * (D + 1) floats of LDS.  Contains one
-// barrier; the caller synchronises before red or A is written again.
-template <int D>
-__device__ __forceinline__ float rv_product(const RvRows<D>& r, const float* A, float* red, int tid) {
-  using T = RvRows<D>;
+// out row i = tid / TPO (of the NR rows) of A (D floats in LDS) times R_V^T;
+// every thread of the row gets the value.  red: QPR * (NR + 1) floats of
+// LDS.  Contains one barrier; the caller synchronises before red or A is
+// written again.
+template <int D, int NR>
+__device__ __forceinline__ float rv_product(const RvRows<D, NR>& r, const float* A, float* red, int tid) {
+  using T = RvRows<D, NR>;
   const int c = tid % T::QPR, rb = tid / T::QPR;
   const float4 a = reinterpret_cast<const float4*>(A)[c];
   float* dst = red + c * T::kStride + T::RPT * rb;
@@ -1327,33 +1329,36 @@ __device__ __forceinline__ float rv_product(const RvRows<D>& r, const float* A, 
   return o;
 }
 
-// One query head per block:
+// Two blocks per query head, one per half of the output channels (each
+// applies half of R_V's rows; both merge all of the head's partials):
 //   out = (sum_hist f_s acc_s R_V^T + sum_bf16 f_s acc_s) / sum_all f_s l_s,
 //   f_s = exp2(m_s - M) with M the maximum over every partial.
 // The R_V rows are requested first, so their loads overlap the partials'.
 template <int D>
 __global__ __launch_bounds__(kBlock) void merge_kernel(DecodeDev p, int n_merge, DemoteDev dk, DemoteDev dv) {
+  constexpr int NR = D / 2;
+  using RV = RvRows<D, NR>;
   __shared__ MergeShared<D> sh;
-  __shared__ float red[RvRows<D>::QPR * RvRows<D>::kStride];
-  const int bh = blockIdx.x;
-  if (bh >= n_merge) {
-    demote_step_block<D>(p, bh - n_merge, dk, dv);
+  __shared__ float red[RV::QPR * RV::kStride];
+  if ((int)blockIdx.x >= n_merge) {
+    demote_step_block<D>(p, blockIdx.x - n_merge, dk, dv);
     return;
   }
+  const int bh = blockIdx.x >> 1, half = blockIdx.x & 1;
   const int b = bh / p.Hq, h = bh % p.Hq, g = h / p.G, kh = h % p.G;
   const int tid = threadIdx.x;
   const size_t stride = (size_t)p.G * part_row(D);
   const float* hp = p.hpart + ((size_t)b * p.n_kv + g) * p.splits * stride + (size_t)kh * part_row(D);
   const float* bp = p.bpart + ((size_t)b * p.n_kv + g) * p.chunks * stride + (size_t)kh * part_row(D);
   const int n = p.splits, nt = p.splits + p.chunks;
-  RvRows<D> rv;
-  load_rv_rows<D>(rv, p.r_v + (size_t)g * D * D, tid);
+  RV rv;
+  load_rv_rows<D, NR>(rv, p.r_v + ((size_t)g * D + (size_t)half * NR) * D, tid);
   const float2 ML = merge_head<D>(
       [&](int s) { return s < n ? hp + (size_t)s * stride : bp + (size_t)(s - n) * stride; }, n, nt, sh, tid);
-  // out_hist[i] = sum_j A_hist[j] R_V[g][i][j]
-  const float o = rv_product<D>(rv, sh.rot, red, tid);
-  const int i = tid / RvRows<D>::TPO;
-  if (tid % RvRows<D>::TPO == 0) {
+  // out_hist[i] = sum_j A_hist[j] R_V[g][i][j] for the half's rows i
+  const float o = rv_product<D, NR>(rv, sh.rot, red, tid);
+  const int i = half * NR + tid / RV::TPO;
+  if (tid % RV::TPO == 0) {
     const float L = ML.y;
     float out;
     if (isnan(L)) out = NAN;
@@ -1372,12 +1377,12 @@ constexpr int kUnitRound = 16;
 
 template <int D, int G>
 __global__ __launch_bounds__(kBlock) void merge_unit_kernel(DecodeDev p, int n_merge, DemoteDev dk, DemoteDev dv) {
-  constexpr int QPR = D / 4, R = part_row(D), TPO = RvRows<D>::TPO;
+  constexpr int QPR = D / 4, R = part_row(D), TPO = RvRows<D, D>::TPO;
   static_assert(G * QPR <= kBlock, "one (head, channel quad) per thread");
   __shared__ __attribute__((aligned(16))) float arot[G][D];
   __shared__ __attribute__((aligned(16))) float aplain[G][D];
   __shared__ float Ls[G];
-  __shared__ float red[RvRows<D>::QPR * RvRows<D>::kStride];
+  __shared__ float red[RvRows<D, D>::QPR * RvRows<D, D>::kStride];
   if ((int)blockIdx.x >= n_merge) {
     demote_step_block<D>(p, blockIdx.x - n_merge, dk, dv);
     return;
@@ -1385,8 +1390,8 @@ __global__ __launch_bounds__(kBlock) void merge_unit_kernel(DecodeDev p, int n_m
   const int unit = blockIdx.x, b = unit / p.n_kv, g = unit % p.n_kv;
   const int tid = threadIdx.x;
   const int i = tid / TPO;   // output channel of this thread
-  RvRows<D> rv;
-  load_rv_rows<D>(rv, p.r_v + (size_t)g * D * D, tid);
+  RvRows<D, D> rv;
+  load_rv_rows<D, D>(rv, p.r_v + (size_t)g * D * D, tid);
   const size_t stride = (size_t)G * R;
   const int n = p.splits, nt = p.splits + p.chunks;
   const float* hb = p.hpart + (size_t)unit * n * stride;
@@ -1427,7 +1432,7 @@ __global__ __launch_bounds__(kBlock) void merge_unit_kernel(DecodeDev p, int n_m
   // out[h][i] = (sum_j A_hist[h][j] R_V[g][i][j] + A_bf16[h][i]) / L[h]
   for (int h = 0; h < G; ++h) {
     if (h > 0) __syncthreads();   // every thread has read red for head h - 1
-    const float o = rv_product<D>(rv, arot[h], red, tid);
+    const float o = rv_product<D, D>(rv, arot[h], red, tid);
     if (tid % TPO == 0) {
       const float L = Ls[h];
       float out;
@@ -1465,8 +1470,8 @@ template <int D>
 void launch_merge(const DecodeDev& dv, const DemoteDev& mk, const DemoteDev& mv, hipStream_t stream) {
   const unsigned n_dem = (unsigned)((mk.n_tok + mv.n_tok) * dv.n_kv);
   if (dv.B > 0 && launch_merge_unit<D>(dv, n_dem, mk, mv, stream)) return;
-  const int nbh = dv.B * dv.Hq;
-  if (nbh + n_dem > 0) merge_kernel<D><<<(unsigned)nbh + n_dem, kBlock, 0, stream>>>(dv, nbh, mk, mv);
+  const int n_merge = 2 * dv.B * dv.Hq;   // two blocks per query head
+  if (n_merge + n_dem > 0) merge_kernel<D><<<(unsigned)n_merge + n_dem, kBlock, 0, stream>>>(dv, n_merge, mk, mv);
 }
 
 template <int D, int G>
