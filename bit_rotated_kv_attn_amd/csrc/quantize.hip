@@ -22,8 +22,11 @@ constexpr int kQTok = 32;  // tokens per block
 
 typedef double v4d __attribute__((ext_vector_type(4)));
 
+// Eight waves per SIMD (at most 64 VGPRs; 54 without spills): the loads of x
+// and R and the fp64 products are latency-bound, and eight resident blocks
+// per compute unit hide more of it than the six that 80 VGPRs allow.
 template <int D>
-__global__ __launch_bounds__(kBlock) void quantize_pack_kernel(
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) void quantize_pack_kernel(
     int kind, const uint16_t* __restrict__ x, int64_t n_src, int64_t tok_stride,
     int64_t head_stride, const int32_t* __restrict__ src_idx, int64_t n_tok, int n_kv,
     const float* __restrict__ rot, float clip, const int32_t* __restrict__ dst_slot,
