@@ -20,6 +20,15 @@ namespace {
 
 constexpr int kQTok = 32;  // tokens per block
 
+// fp64 sum over the 16 lanes of a DPP row, every lane receiving it (all lanes
+// of the wave active)
+__device__ __forceinline__ double group16_sum_f64(double v) {
+  v += dpp_f64<kDppXor1>(v);
+  v += dpp_f64<kDppXor2>(v);
+  v += dpp_f64<kDppHalfMirror>(v);
+  return v + dpp_f64<kDppMirror>(v);
+}
+
 typedef double v4d __attribute__((ext_vector_type(4)));
 
 // Eight waves per SIMD (at most 64 VGPRs; 54 without spills): the loads of x
@@ -42,7 +51,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) 
   float (*ys)[D + 1] = reinterpret_cast<float (*)[D + 1]>(tile);
   __shared__ int64_t src_s[kQTok];
   __shared__ int64_t dst_s[kQTok];       // -1: skip this token
-  constexpr int kPer = D / kWave;        // channels per lane in the statistics (channel lane + 64k)
+  constexpr int kPer = D / kWave;        // 64-channel groups per head
   __shared__ float zf[kQTok][kPer], sf[kQTok][kPer];   // per token and group
 
   const int g = blockIdx.y;
@@ -139,44 +148,56 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) 
   __syncthreads();
 
   // per-token group statistics: zero = fp16(min), scale = fp16((max - min) / 3),
-  // or the Lloyd-Max mean and deviation (fp64); lane holds channels lane + 64k,
-  // and with 64-channel groups element k is group k's
-  const int lane = tid & (kWave - 1), wave = tid / kWave;
-  for (int t = wave; t < kQTok; t += kBlock / kWave) {
-    float v[kPer];
+  // or the Lloyd-Max mean and deviation (fp64).  A 16-lane DPP row handles one
+  // token (four tokens per wave at a time); lane c of the row holds channels
+  // c + 16k, so with 64-channel groups elements k of one group are adjacent.
+  {
+    constexpr int KP = D / 16;
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    const int gq = lane >> 4, c = lane & 15;
+    const int per = KP / ng;     // elements of one group in this lane
+    for (int rd = 0; rd < kQTok / 16; ++rd) {
+      const int t = 16 * rd + 4 * wave + gq;
+      float v[KP];
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) v[k] = ys[t][lane + kWave * k];
-    const int per = kPer / ng;   // elements of one group in this lane
-    for (int j = 0; j < ng; ++j) {
-      float mn = INFINITY, mx = -INFINITY;
-      for (int k = j * per; k < (j + 1) * per; ++k) {
-        mn = fminf(mn, v[k]);
-        mx = fmaxf(mx, v[k]);
-      }
-      mn = wave_min(mn);
-      mx = wave_max(mx);
-      __half z = __float2half_rn(mn);
-      __half s = __float2half_rn(__fdiv_rn(mx - mn, 3.0f));
-      if (lm) {
-        double s1 = 0.0;
-        for (int k = j * per; k < (j + 1) * per; ++k) s1 += (double)v[k];
-        const double mean = wave_sum_f64(s1) / (D / ng);
-        double s2 = 0.0;
-        for (int k = j * per; k < (j + 1) * per; ++k) {
-          const double dv = (double)v[k] - mean;
-          s2 = __dadd_rn(s2, __dmul_rn(dv, dv));
+      for (int k = 0; k < KP; ++k) v[k] = ys[t][c + 16 * k];
+      for (int j = 0; j < ng; ++j) {
+        float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < KP; ++k) {
+          if (k / per != j) continue;
+          mn = fminf(mn, v[k]);
+          mx = fmaxf(mx, v[k]);
         }
-        lm_scale_zero(mean, wave_sum_f64(s2), D / ng, s, z);
-      }
-      if (lane == 0) {
-        zf[t][j] = __half2float(z);
-        sf[t][j] = __half2float(s);
-        const int64_t slot = dst_s[t];
-        if (slot >= 0) {
-          const int64_t page = slot / kPage;
-          const int o = (int)(slot % kPage);
-          sz[((page * n_kv + g) * ng + j) * kPage + o] =
-              (uint32_t)__half_as_ushort(s) | ((uint32_t)__half_as_ushort(z) << 16);
+        mn = group16_min(mn);
+        mx = group16_max(mx);
+        __half z = __float2half_rn(mn);
+        __half s = __float2half_rn(__fdiv_rn(mx - mn, 3.0f));
+        if (lm) {
+          double s1 = 0.0;
+#pragma unroll
+          for (int k = 0; k < KP; ++k)
+            if (k / per == j) s1 += (double)v[k];
+          const double mean = group16_sum_f64(s1) / (D / ng);
+          double s2 = 0.0;
+#pragma unroll
+          for (int k = 0; k < KP; ++k) {
+            if (k / per != j) continue;
+            const double dv = (double)v[k] - mean;
+            s2 = __dadd_rn(s2, __dmul_rn(dv, dv));
+          }
+          lm_scale_zero(mean, group16_sum_f64(s2), D / ng, s, z);
+        }
+        if (c == 0) {
+          zf[t][j] = __half2float(z);
+          sf[t][j] = __half2float(s);
+          const int64_t slot = dst_s[t];
+          if (slot >= 0) {
+            const int64_t page = slot / kPage;
+            const int o = (int)(slot % kPage);
+            sz[((page * n_kv + g) * ng + j) * kPage + o] =
+                (uint32_t)__half_as_ushort(s) | ((uint32_t)__half_as_ushort(z) << 16);
+          }
         }
       }
     }
