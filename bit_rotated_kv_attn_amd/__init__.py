@@ -26,7 +26,8 @@ CODEBOOK_UNIFORM, CODEBOOK_LLOYD_MAX = 0, 0x100
 # 64-channel quantisation groups (oscar.h); OR'ed into a demotion's kind
 GROUPS_64 = 0x200
 # arithmetic the kernels of this build compute in (reported by bench.py)
-COMPUTE_DTYPE = "i8 MFMA (exact integer digits) + f32 softmax; f64 rotation in demotion"
+COMPUTE_DTYPE = ("QK i8 MFMA (exact integer digits), PV f16 MFMA (fp16 weight pairs) + f32 sums and softmax; "
+                 "f64 rotation in demotion")
 OSCAR_OK, OSCAR_EINVAL, OSCAR_EUNSUPPORTED, OSCAR_EWORKSPACE, OSCAR_EHIP = range(5)
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liboscar.so")
 ABI_VERSION = 2   # OSCAR_ABI_VERSION of the oscar.h these mirrors follow

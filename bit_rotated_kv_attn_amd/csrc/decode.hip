@@ -13,18 +13,19 @@
 // x_hat = zero + c*scale, a history logit is scale*(q_rot . c) + zero*sum(q_rot)
 // and a history output is sum_t p_t*scale_t*c_t + sum_t p_t*zero_t.
 //
-// History scan on the matrix cores, in exact integer arithmetic
+// History scan on the matrix cores.  QK is exact integer arithmetic
 // (v_mfma_i32_16x16x64_i8): the 2-bit codes become int8 operands by masking
 // (no conversion; with the Lloyd-Max codebook a byte permute maps each code to
-// its int8 level, and c reads L[c] above), the rotated query and the softmax weights become 30-bit
-// fixed-point integers split into four balanced 8-bit digits, one MFMA row per
-// (head, digit), so 4 heads fill the 16 rows.  Products and sums are exact;
-// the only roundings are the fixed-point conversions (a query element to
-// 2^-25 of the query's norm, a weight to 2^-18 of the reference weight) and the
-// fp32 combination of the digit results.  PV accumulates in int32 across a
-// wave's pages; the softmax reference maximum is only raised when a logit
-// exceeds it by 2^12 (then the integer accumulator is folded into fp32).
-//
+// its int8 level, and c reads L[c] above), and the rotated query becomes a
+// 30-bit fixed-point integer split into four balanced 8-bit digits, one MFMA
+// row per (head, digit), so 4 heads fill the 16 rows; a query element is
+// exact to 2^-25 of the query's norm.  PV runs on the fp16 matrix cores with
+// fp32 sums (v_mfma_f32_16x16x32_f16): each weight p*scale_V is an fp16 pair
+// (high part, and the remainder scaled by 2^11), so it is held to 2^-21 of
+// itself with no fixed-point floor, and the V codes enter as fp16 subnormal
+// integers masked in place (c * 4^f * 2^-24, multiplied exactly).  The
+// softmax reference maximum is only raised when a logit exceeds it by 2^12;
+// the raise then rescales the fp32 sums.
 // Launches (all on the caller's stream):
 //   1. prepare_kernel       q_rot = q R_K[g] per query head -> MFMA digit
 //                           operands
@@ -44,17 +45,19 @@ namespace oscar {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 
 constexpr uint32_t kMask0 = 0x03030303u;  // code field 0 of each byte (x1)
 constexpr uint32_t kMask1 = 0x0C0C0C0Cu;  // field 1 (x4)
 constexpr uint32_t kMask2 = 0x30303030u;  // field 2 (x16); field 3 is shifted into it
 // Raise the reference maximum only when a logit passes it by 2^kLazyThr.
-// Weights stay below 1.75 * 2^30 for any threshold (kw scales with it); 12
-// keeps a reference weight at 2^18 fixed-point units and leaves about one
-// page in forty to the fold path on the long-context workloads.
+// On the long-context workloads about one page in a hundred then takes the
+// rescale path; the fp32 PV sums make that path a multiply per sum.
 constexpr float kLazyThr = 12.0f;
-constexpr float kScaleSlack = 1.75f;      // refold when a V scale exceeds 1.75x the running max
-constexpr float kFix = 1073741824.0f;     // 2^30: fixed-point range of digits
+constexpr float kScaleSlack = 1.75f;      // rescale when a V scale exceeds 1.75x the running max
+constexpr float kWeightTop = 16384.0f;    // 2^14: largest weight p*scale_V*kap the thresholds allow
+constexpr float kFix = 1073741824.0f;     // 2^30: fixed-point range of the query digits
 constexpr int kBf16WaveTokens = 16;       // tokens of a BF16 chunk per wave (4 waves per chunk)
 
 struct DecodeDev {
@@ -124,10 +127,6 @@ __device__ __forceinline__ int code_mask(uint32_t w, int p) {
   return (int)(p == 0 ? (w & kMask0) : p == 1 ? (w & kMask1) : p == 2 ? (w & kMask2) : ((w >> 2) & kMask2));
 }
 
-__device__ __forceinline__ float code_scale_inv(int p) {  // 1 / (x1, x4, x16, x16)
-  return p == 0 ? 1.0f : p == 1 ? 0.25f : 0.0625f;
-}
-
 // Lloyd-Max levels (-10, -3, 3, 10) as the int8 bytes of one word, indexed by the code
 constexpr uint32_t kLmLevels = 0x0A03FDF6u;
 
@@ -138,32 +137,6 @@ template <bool LM>
 __device__ __forceinline__ int code_operand(uint32_t w, int p) {
   if constexpr (LM) return (int)__builtin_amdgcn_perm(kLmLevels, kLmLevels, (w >> (2 * p)) & kMask0);
   else return code_mask(w, p);
-}
-
-// factor that undoes operand p's in-place weight
-template <bool LM>
-__device__ __forceinline__ float code_scale(int p) {
-  if constexpr (LM) return 1.0f;
-  else return code_scale_inv(p);
-}
-
-// fp32 value of a 4-digit (base 256, balanced) integer held in one MFMA result
-// column.  A PV digit sum can approach 2^25 over a wave's pages, so the digits
-// are converted one by one (x + 256y could overflow int32).
-__device__ __forceinline__ float digits_to_f32(v4i d) {
-  return fmaf((float)d.w, 16777216.0f, fmaf((float)d.z, 65536.0f, fmaf((float)d.y, 256.0f, (float)d.x)));
-}
-
-// Zero an accumulator in its own registers.  A plain assignment of 0 in the
-// rarely taken rescale branch makes the compiler materialise zeros and copy
-// the accumulators on every page at the branch join.
-__device__ __forceinline__ void clear_in_place(v4i& a) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    int x = a[k];
-    asm volatile("v_mov_b32 %0, 0" : "+v"(x));
-    a[k] = x;
-  }
 }
 
 // c + f * a and f * a, per component
@@ -470,7 +443,7 @@ __device__ __forceinline__ void wait_page(int ahead) {
 // exactly the 16 bytes that the same lane reads back as an MFMA operand, so the
 // reads (16*l + 1024*c) are free of LDS bank conflicts:
 //   K copy c, lane (q = l/16, n = l%16): plane q, tokens 4n..4n+3, bytes 16c..16c+15
-//   V copy c, lane (q, n): byte column (D/64)*n + c, tokens 16q..16q+15
+//   V copy c, lane (q, n): byte column 16c + n, tokens 16q..16q+15
 template <int D, int NG>
 struct Stage {   // NG (scale, zero) groups per head, group-planar
   static constexpr int kK = 0, kV = 16 * D, kKsz = 32 * D, kVsz = 32 * D + 256 * NG, kBytes = 32 * D + 512 * NG;
@@ -482,15 +455,14 @@ struct StageOffsets {
   uint32_t k, v, sz;
 };
 
-// V: lane (n, q) of LDS chunk c gets byte column 2n + c (NG = 1: PV column n
-// of a chunk is channels 8n + 4c + field) or 16c + n (NG = 2: the chunk's
-// products cover channels 64c .. 64c + 63 only, one group), tokens 16q..16q+15.
+// V: lane (n, q) of LDS chunk c gets byte column 16c + n, tokens 16q..16q+15:
+// the PV products of chunk c then cover channels 64c .. 64c + 63 (one
+// 64-channel group), channel 64c + 4n + field in column n.
 template <int D, int NG>
 __device__ __forceinline__ StageOffsets stage_offsets(int lane) {
-  constexpr int NCH = D / 64, PLANE = D / 16;
+  constexpr int PLANE = D / 16;
   const int q = lane >> 4, n = lane & 15;
-  const int vcol = NG == 2 ? n : NCH * n;
-  return StageOffsets{(uint32_t)(q * kPage * PLANE + 4 * n * PLANE), (uint32_t)(vcol * kPage + 16 * q),
+  return StageOffsets{(uint32_t)(q * kPage * PLANE + 4 * n * PLANE), (uint32_t)(n * kPage + 16 * q),
                       (uint32_t)(4 * lane)};
 }
 
@@ -508,7 +480,7 @@ __device__ __forceinline__ void stage_page(const DecodeDev& p, size_t blk, uint3
   copy16_to_lds(kb, o.k, stage_lds + S::kK);
   if constexpr (D == 128) copy16_to_lds(kb, o.k + 16, stage_lds + S::kK + 1024);
   copy16_to_lds(vb, o.v, stage_lds + S::kV);
-  if constexpr (D == 128) copy16_to_lds(vb, o.v + (NG == 2 ? 16 * kPage : kPage), stage_lds + S::kV + 1024);
+  if constexpr (D == 128) copy16_to_lds(vb, o.v + 16 * kPage, stage_lds + S::kV + 1024);
 #pragma unroll
   for (int j = 0; j < NG; ++j) {
     copy4_to_lds(p.k_sz + (blk * NG + j) * kPage, o.sz, stage_lds + S::kKsz + 256 * j);
@@ -516,34 +488,51 @@ __device__ __forceinline__ void stage_page(const DecodeDev& p, size_t blk, uint3
   }
 }
 
-// Per-wave LDS: a ring of page stages and the weight-digit planes (unless
-// they reuse the consumed K codes).  Two stages: the page being processed and
+// Softmax weights as PV A operands: one plane per (row block of 8 heads,
+// group), 16 rows x 64 fp16 token slots.  Row 4g + 2e + part holds head
+// 4e + g of the row block (e = head block within it, g = lane group), part 0
+// the weight's high fp16 part and part 1 its low part.  The 16-byte chunk c
+// of row r sits at chunk c ^ ((r >> 1) & 3): the eight rows read by one
+// phase of a 128-bit load then fall in distinct banks.
+constexpr int kPlaneRow = 128, kPlaneBytes = 16 * kPlaneRow;
+__device__ __forceinline__ int plane_chunk(int r, int c) { return r * kPlaneRow + 16 * (c ^ ((r >> 1) & 3)); }
+
+// Per-wave LDS: a ring of page stages and the weight planes (unless they
+// reuse the consumed K codes).  Two stages: the page being processed and
 // one page in flight.  With every wave of the chip one page ahead, about 9 MB
 // of copies are outstanding, enough to keep HBM busy; deeper rings only
 // lengthen the memory queues, and a wave then stalls issuing its copies
 // instead of computing.
 template <int D, int NB, int NG = 1>
 struct Ring {
-  // weight-digit planes: one per (head block, group); they reuse the consumed K codes when they fit
-  static constexpr bool kPlanesInK = NB * NG * 1024 <= 16 * D;
+  static constexpr int PB = (NB + 1) / 2;   // PV row blocks
+  // The planes reuse the consumed K codes when they fit and every row is
+  // written on every page (two head blocks per row block); otherwise they
+  // have their own LDS, zeroed once, so rows of absent heads stay zero.
+  static constexpr bool kPlanesInK = NB % 2 == 0 && PB * NG * kPlaneBytes <= 16 * D;
 #ifdef OSCAR_SCAN_STAGES
   static constexpr int kStages = OSCAR_SCAN_STAGES;
 #else
   static constexpr int kStages = 2;
 #endif
-  static constexpr int kPlaneBytes = kPlanesInK ? 0 : NB * NG * 1024;
-  static constexpr int kWaveBytes = kStages * Stage<D, NG>::kBytes + kPlaneBytes;
+  static constexpr int kPlaneLds = kPlanesInK ? 0 : PB * NG * kPlaneBytes;
+  static constexpr int kWaveBytes = kStages * Stage<D, NG>::kBytes + kPlaneLds;
 };
 
 // Lane roles (lane = 16*grp + n):
-//  * QK:  D[(head, digit)][token] = sum_ch Qdigit[(head,digit)][ch] * code'[ch][token].
-//         A (q digits) comes from the workspace; B lane (n, grp) holds, for token
-//         block tb, token 4n+tb and the 16 channels of one code word of K plane grp.
-//         The result lane holds the 4 digit sums of head (4nb+grp) for token 4n+tb.
-//  * PV:  D[(head, digit)][channel] = sum_t Wdigit[(head,digit)][t] * code'[t][channel].
-//         A (weight digits) is read back from LDS planes; B lane (n, grp) holds
-//         tokens 16grp..16grp+15 of one channel of V byte column D/64*n + bs.
-//         The result lane holds the 4 digit sums of head (4nb+grp), channel D/16*n + u.
+//  * QK:  D[(head, digit)][token] = sum_ch Qdigit[(head,digit)][ch] * code'[ch][token]
+//         (v_mfma_i32_16x16x64_i8, exact).  A (q digits) comes from the
+//         workspace; B lane (n, grp) holds, for token block tb, token 4n+tb and
+//         the 16 channels of one code word of K plane grp.  The result lane
+//         holds the 4 digit sums of head (4nb+grp) for token 4n+tb.
+//  * PV:  D[(head, part)][channel] = sum_t W[(head, part)][t] * c[t][channel]
+//         (v_mfma_f32_16x16x32_f16, fp32 sums).  A (fp16 weight parts) is
+//         read from the LDS planes; B lane (n, grp) holds the fp16 operand of
+//         8 tokens (of 16grp..16grp+15) of channel 64c + 4n + f: the 2-bit
+//         code masked in place, i.e. the subnormal fp16 c * 4^f * 2^-24,
+//         which the matrix cores multiply exactly.  The result lane holds
+//         rows 4grp..4grp+3 (heads grp and 4 + grp, two parts each) of
+//         column n.
 // QK operands of a history wave: q digit A operands and the logit constants
 template <int D, int G>
 struct HistOperands {
@@ -599,6 +588,22 @@ __device__ __forceinline__ void load_pair_operands(const DecodeDev& p, int b, in
   }
 }
 
+// The PV B operand of field f for 8 tokens: bytes 0 and 2 of the code words
+// w0, w1 and bytes 1 and 3 (s = w >> 8) hold tokens (0, 2), (4, 6) and
+// (1, 3), (5, 7), one per 16-bit half.  Masked in place, each half is the
+// fp16 subnormal c * 4^f * 2^-24.  With kHiBit only the field's high bit
+// stays (2 * (c >> 1) * 4^f * 2^-24).
+template <bool kHiBit>
+__device__ __forceinline__ half8 pv_operand(uint32_t w0, uint32_t s0, uint32_t w1, uint32_t s1, int f) {
+  const uint32_t m = (kHiBit ? 0x00020002u : 0x00030003u) << (2 * f);
+  const u32x4 x = {w0 & m, s0 & m, w1 & m, s1 & m};
+  return __builtin_bit_cast(half8, x);
+}
+
+__device__ __forceinline__ uint32_t pack_rtz(float a, float b) {   // two fp16, toward zero: a low, b high
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
 // One wave's scan of history pages pg_begin .. pg_begin + count - 1.  pid_lane
 // holds the page id of page pg_begin + lane, and qo the QK operands; both were
 // loaded by the caller together with the history length, and this wave's
@@ -608,10 +613,10 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
                                           const HistOperands<D, G>& qo, uint8_t* ring, float* mw, bool& poison,
                                           int lane) {
   constexpr int NB = (G + 3) / 4;
-  constexpr int NCH = D / 64;   // code words per token per K plane; V byte columns per lane
-  constexpr int NU = 4 * NCH;   // PV result column blocks per head block
+  constexpr int NCH = D / 64;   // code words per token per K plane; 64-channel chunks of V
   using S = Stage<D, NG>;
   using RG = Ring<D, NB, NG>;
+  constexpr int PB = RG::PB;
   constexpr int NS = RG::kStages;
   const int n = lane & 15, grp = lane >> 4;
   const auto& qa = qo.qa;
@@ -628,13 +633,13 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
     for (int c = 0; c < NCH; ++c) qa0[nb][c] = (NG == 2 && grp < 2) ? qa[nb][c] : v4i{0, 0, 0, 0};
   const uint64_t page_ok = __ballot(pid_lane >= 0 && (int64_t)pid_lane < p.n_pages);
 
-  // pv: integer digit sums of the PV products since the last rescale; facc:
-  // the fp32 sums folded at each rescale
-  v4i pv[NB][NU];
-  float facc[NB][NU];
-  // mref: reference maximum (log2 units) of each head block; logits are kept
-  // relative to it.  thr: rescale when a relative logit exceeds it (-inf until
-  // the first page has set the references).
+  // acc: fp32 PV sums of row block rb, chunk c, field f, rows 4grp..4grp+3
+  // (Lloyd-Max: acc2 the sums over the codes' high bits).  mref: reference
+  // maximum (log2 units) of each head block; logits are kept relative to it.
+  // thr: rescale when a relative logit exceeds it (-inf until the first page
+  // has set the references).  kap: weight scale putting the largest weight
+  // the thresholds allow at 2^14 (0 until the first page).
+  v4f acc[PB][NCH][4], acc2[PB][NCH][4];
   float mref[NB], lsum[NB], zsum[NB][NG];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -642,16 +647,25 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
     lsum[nb] = 0.0f;
 #pragma unroll
     for (int j = 0; j < NG; ++j) zsum[nb][j] = 0.0f;
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      pv[nb][u] = v4i{0, 0, 0, 0};
-      facc[nb][u] = 0.0f;
-    }
   }
-  float thr = -INFINITY, smax = 0.0f, sthr = 0.0f, kw = 0.0f, kw_inv = 0.0f;
+#pragma unroll
+  for (int rb = 0; rb < PB; ++rb)
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        acc[rb][c][f] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        acc2[rb][c][f] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+  float thr = -INFINITY, smax = 0.0f, sthr = 0.0f, kap = 0.0f;
 
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_offset(ring));
   uint8_t* planes = RG::kPlanesInK ? nullptr : ring + NS * S::kBytes;
+  if constexpr (!RG::kPlanesInK) {   // rows of absent heads are never written
+#pragma unroll
+    for (int o = 0; o < PB * NG * kPlaneBytes; o += 16 * kWave)
+      *reinterpret_cast<uint4*>(planes + o + 16 * lane) = make_uint4(0, 0, 0, 0);
+  }
   // (page, head) block of each of the wave's pages, one per lane; an invalid
   // page id is staged from page 0 and skipped
   const size_t blk_lane = ((page_ok >> lane) & 1) ? (size_t)pid_lane * p.n_kv + g : (size_t)g;
@@ -713,8 +727,8 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
     }
     uint4 vpre[NCH];
 #pragma unroll
-    for (int bs = 0; bs < NCH; ++bs) vpre[bs] = *reinterpret_cast<const uint4*>(st + S::kV + 1024 * bs + 16 * lane);
-    // token 4n+tb, group j
+    for (int c = 0; c < NCH; ++c) vpre[c] = *reinterpret_cast<const uint4*>(st + S::kV + 1024 * c + 16 * lane);
+    // token 4n+tb, group j; the Lloyd-Max level 7c - 10 - (c >> 1) moves its -10 into the zero
     float sk[NG][4], zk[NG][4], sv[NG][4], zv[NG][4];
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
@@ -728,6 +742,7 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
         zk[j][tb] = f16_to_f32(kw4[tb] >> 16);
         sv[j][tb] = f16_to_f32(vw4[tb] & 0xffffu);
         zv[j][tb] = f16_to_f32(vw4[tb] >> 16);
+        if constexpr (LM) zv[j][tb] = fmaf(-10.0f, sv[j][tb], zv[j][tb]);
       }
     }
 
@@ -785,25 +800,22 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
 
     __builtin_amdgcn_sched_barrier(0);
     if (__any(need)) {
-      // raise the references and the V-scale bound; fold the integer
-      // accumulators into fp32 under the old ones first
-      const bool first = !(kw_inv > 0.0f);   // nothing accumulated yet
+      // raise the references and the V-scale bound; rescale the sums under the
+      // new ones (the fp32 PV sums by the same factor as the weight sums, and
+      // by the change of the weight scale)
+      const bool first = !(kap > 0.0f);   // nothing accumulated yet
       const float s_new = fmaxf(smax, group16_max(svmax));
+      float alpha[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const float t = group16_max(lmax[nb]);
         // raise of the reference; the first page sets it (all -inf: head has no rows)
         const float delta = first ? (t == -INFINITY ? 0.0f : t) : fmaxf(t, 0.0f);
+        alpha[nb] = exp2f(-delta);
         if (!first) {
-          const float alpha = exp2f(-delta);
+          lsum[nb] *= alpha[nb];
 #pragma unroll
-          for (int u = 0; u < NU; ++u) {
-            facc[nb][u] = (facc[nb][u] + digits_to_f32(pv[nb][u]) * (code_scale<LM>(u & 3) * kw_inv)) * alpha;
-            clear_in_place(pv[nb][u]);
-          }
-          lsum[nb] *= alpha;
-#pragma unroll
-          for (int j = 0; j < NG; ++j) zsum[nb][j] *= alpha;
+          for (int j = 0; j < NG; ++j) zsum[nb][j] *= alpha[nb];
         }
         mref[nb] += delta;
 #pragma unroll
@@ -814,21 +826,41 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
       // scale state in scalar registers
       smax = wave_uniform(s_new);
       sthr = wave_uniform(kScaleSlack * smax);
-      // weights p*scale_V*kw stay below 2^30 * kScaleSlack < 2^31
-      const float denom = exp2f(kLazyThr) * (smax > 0.0f ? smax : 1.0f);
-      kw = wave_uniform(kFix / denom);
-      kw_inv = wave_uniform(denom / kFix);
+      // weights p*scale_V*kap stay below 2^14 (p < 2^kLazyThr, scale_V < kScaleSlack*smax)
+      const float kap_new = wave_uniform(kWeightTop / (exp2f(kLazyThr) * kScaleSlack * (smax > 0.0f ? smax : 1.0f)));
+      if (!first) {
+        const float r = kap_new / kap;
+#pragma unroll
+        for (int rb = 0; rb < PB; ++rb)
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            if (2 * rb + e >= NB) continue;   // rows of an absent head block hold zeros
+            const float fct = alpha[2 * rb + e] * r;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c)
+#pragma unroll
+              for (int f = 0; f < 4; ++f)
+#pragma unroll
+                for (int part = 0; part < 2; ++part) {
+                  acc[rb][c][f][2 * e + part] *= fct;
+                  if constexpr (LM) acc2[rb][c][f][2 * e + part] *= fct;
+                }
+          }
+      }
+      kap = kap_new;
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- weights p*scale_V as 30-bit fixed point, balanced digits,
-    // transposed into the LDS digit planes of the PV A operands
+    // ---- weights w = p*scale_V*kap as an fp16 pair (high part, and the
+    // remainder scaled by 2^11), into the planes of the PV A operands.  Lane
+    // (n, grp) holds tokens 4n..4n+3, stored in slots 4n..4n+3 in the order
+    // of the B operands' halves: tokens 0, 2, 1, 3.
     uint8_t* pl = RG::kPlanesInK ? st + S::kK : planes;
     float svk[NG][4];
 #pragma unroll
     for (int j = 0; j < NG; ++j)
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) svk[j][tb] = sv[j][tb] * kw;
+      for (int tb = 0; tb < 4; ++tb) svk[j][tb] = sv[j][tb] * kap;
     __builtin_amdgcn_wave_barrier();   // every lane has read its K words
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -838,49 +870,58 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
         pr[tb] = __builtin_amdgcn_exp2f(lg[nb][tb]);   // exp2(-inf) = 0
         lsum[nb] += pr[tb];
       }
-      // one plane per (head block, group): group j's weights p*scale_V[j]
+      const int r = 4 * grp + 2 * (nb & 1);   // the head's high-part row
 #pragma unroll
       for (int j = 0; j < NG; ++j) {
-        uint32_t dg[4];
+        float w[4], u[4];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
           zsum[nb][j] = fmaf(pr[tb], zv[j][tb], zsum[nb][j]);
-          dg[tb] = balanced_digits((uint32_t)fmaf(pr[tb], svk[j][tb], 0.5f));
+          w[tb] = pr[tb] * svk[j][tb];
+          u[tb] = w[tb] * 2048.0f;
         }
-        // 4x4 byte transpose: t_j byte tb = digit j of token 4n+tb
-        const uint32_t x01l = __builtin_amdgcn_perm(dg[1], dg[0], 0x05010400u);
-        const uint32_t x01h = __builtin_amdgcn_perm(dg[1], dg[0], 0x07030602u);
-        const uint32_t x23l = __builtin_amdgcn_perm(dg[3], dg[2], 0x05010400u);
-        const uint32_t x23h = __builtin_amdgcn_perm(dg[3], dg[2], 0x07030602u);
-        // word j is row (head 4nb+grp, digit j), tokens 4n..4n+3: it goes to the
-        // chunk the PV reader lane (4grp+j, n/4) loads (see plane_chunk)
-        uint8_t* plane = pl + (nb * NG + j) * 1024 + 256 * (n >> 2) + 4 * (n & 3);
-        const int sw = 4 * (n >> 2);
-        *reinterpret_cast<uint32_t*>(plane + 16 * ((4 * grp + 0) ^ sw)) = __builtin_amdgcn_perm(x23l, x01l, 0x05040100u);
-        *reinterpret_cast<uint32_t*>(plane + 16 * ((4 * grp + 1) ^ sw)) = __builtin_amdgcn_perm(x23l, x01l, 0x07060302u);
-        *reinterpret_cast<uint32_t*>(plane + 16 * ((4 * grp + 2) ^ sw)) = __builtin_amdgcn_perm(x23h, x01h, 0x05040100u);
-        *reinterpret_cast<uint32_t*>(plane + 16 * ((4 * grp + 3) ^ sw)) = __builtin_amdgcn_perm(x23h, x01h, 0x07060302u);
+        const uint32_t h02 = pack_rtz(w[0], w[2]), h13 = pack_rtz(w[1], w[3]);
+        const uint32_t l02 = pack_rtz(fmaf(f16_to_f32(h02 & 0xffffu), -2048.0f, u[0]),
+                                      fmaf(f16_to_f32(h02 >> 16), -2048.0f, u[2]));
+        const uint32_t l13 = pack_rtz(fmaf(f16_to_f32(h13 & 0xffffu), -2048.0f, u[1]),
+                                      fmaf(f16_to_f32(h13 >> 16), -2048.0f, u[3]));
+        uint8_t* plane = pl + ((nb >> 1) * NG + j) * kPlaneBytes + 8 * (n & 1);
+        *reinterpret_cast<uint2*>(plane + plane_chunk(r, n >> 1)) = make_uint2(h02, h13);
+        *reinterpret_cast<uint2*>(plane + plane_chunk(r + 1, n >> 1)) = make_uint2(l02, l13);
       }
     }
     __builtin_amdgcn_wave_barrier();
 
-    // ---- PV
+    // ---- PV: lane (n, grp) reads row n, token slots 16grp + 8ks .. + 7 of
+    // each plane; with two groups, chunk c of V is group c
+    half8 wa[PB][NG][2];
 #pragma unroll
-    for (int bs = 0; bs < NCH; ++bs) {
-      const uint4 v4 = vpre[bs];
-      const uint32_t r[4] = {v4.x, v4.y, v4.z, v4.w};
+    for (int rb = 0; rb < PB; ++rb)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        // A lane (n, grp): row (head 4nb + n/4, digit n%4), tokens 16grp..16grp+15;
-        // plane nb holds 4 token blocks of 256 bytes, chunk n ^ 4grp of block grp
-        // with two groups, chunk bs of V is group bs (see stage_offsets)
-        const v4i wa =
-            *reinterpret_cast<const v4i*>(pl + (nb * NG + (NG == 2 ? bs : 0)) * 1024 + 256 * grp + 16 * (n ^ (4 * grp)));
+      for (int j = 0; j < NG; ++j)
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-          const v4i bop = v4i{code_operand<LM>(r[0], pp), code_operand<LM>(r[1], pp), code_operand<LM>(r[2], pp),
-                              code_operand<LM>(r[3], pp)};
-          pv[nb][4 * bs + pp] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa, bop, pv[nb][4 * bs + pp], 0, 0, 0);
+        for (int ks = 0; ks < 2; ++ks)
+          wa[rb][j][ks] = *reinterpret_cast<const half8*>(pl + (rb * NG + j) * kPlaneBytes + plane_chunk(n, 2 * grp + ks));
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const uint4 v4 = vpre[c];
+      const uint32_t s0 = v4.x >> 8, s1 = v4.y >> 8, s2 = v4.z >> 8, s3 = v4.w >> 8;
+      const int jp = NG == 2 ? c : 0;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint32_t a0 = ks ? v4.z : v4.x, b0 = ks ? s2 : s0, a1 = ks ? v4.w : v4.y, b1 = ks ? s3 : s1;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const half8 bop = pv_operand<false>(a0, b0, a1, b1, f);
+#pragma unroll
+          for (int rb = 0; rb < PB; ++rb)
+            acc[rb][c][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[rb][jp][ks], bop, acc[rb][c][f], 0, 0, 0);
+          if constexpr (LM) {
+            const half8 bhi = pv_operand<true>(a0, b0, a1, b1, f);
+#pragma unroll
+            for (int rb = 0; rb < PB; ++rb)
+              acc2[rb][c][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[rb][jp][ks], bhi, acc2[rb][c][f], 0, 0, 0);
+          }
         }
       }
     }
@@ -889,33 +930,39 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
   wait_vmem<0>();
   set_wave_priority(3);   // the block's merge waits for this wave
 
-  // ---- fold, reduce over the 16 lanes of each head; each head's (m, l, acc)
-  // slot overlays the start of the wave's ring
-  float acc[NB][NU], lz[NB], zs[NB][NG];
+  // ---- reduce the weight sums over the 16 lanes of each head; each head's
+  // (m, l, acc) slot overlays the start of the wave's ring.  Channel value:
+  // (high row + low row / 2^11) * 2^24 / (kap * 4^f), plus the zero-point sum.
+  float lz[NB], zs[NB][NG];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     lz[nb] = group16_sum(lsum[nb]);
 #pragma unroll
     for (int j = 0; j < NG; ++j) zs[nb][j] = group16_sum(zsum[nb][j]);
-#pragma unroll
-    for (int u = 0; u < NU; ++u)
-      acc[nb][u] = facc[nb][u] + digits_to_f32(pv[nb][u]) * (code_scale<LM>(u & 3) * kw_inv);
   }
+  const float kinv = kap > 0.0f ? 16777216.0f / kap : 0.0f;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int h = 4 * nb + grp;
     if (h < G) {
       float* mh = mw + h * part_row(D);
       if (n == 0) {
-        mh[0] = kw_inv > 0.0f ? mref[nb] : -INFINITY;   // no page processed: empty partial
+        mh[0] = kap > 0.0f ? mref[nb] : -INFINITY;   // no page processed: empty partial
         mh[1] = lz[nb];
       }
-      // result u = (chunk u/4, field u%4) of column n: channel NU*n + u, or with
-      // two groups 64*(u/4) + 4n + u%4 (chunk u/4 is group u/4)
+      const int rb = nb >> 1, e = nb & 1;
 #pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        if constexpr (NG == 1) mh[kPartAcc + NU * n + u] = acc[nb][u] + zs[nb][0];
-        else mh[kPartAcc + 64 * (u >> 2) + 4 * n + (u & 3)] = acc[nb][u] + zs[nb][u >> 2];
+      for (int c = 0; c < NCH; ++c) {
+        const float z = zs[nb][NG == 2 ? c : 0];
+        float o[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          float v = fmaf(acc[rb][c][f][2 * e + 1], 1.0f / 2048.0f, acc[rb][c][f][2 * e]);
+          if constexpr (LM)
+            v = fmaf(7.0f, v, -0.5f * fmaf(acc2[rb][c][f][2 * e + 1], 1.0f / 2048.0f, acc2[rb][c][f][2 * e]));
+          o[f] = fmaf(v, kinv * (f == 0 ? 1.0f : f == 1 ? 0.25f : f == 2 ? 0.0625f : 0.015625f), z);
+        }
+        *reinterpret_cast<float4*>(mh + kPartAcc + 64 * c + 4 * n) = make_float4(o[0], o[1], o[2], o[3]);
       }
     }
   }
