@@ -55,11 +55,55 @@ def parse():
                     help="channels per (scale, zero) group: 0 = the whole head, 64 = 64-channel groups")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="time only the selected workload (no 28-request and bulk-demotion sub-records)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (torch.neg) 3 times: the known-size "
                          "kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+class Timer:
+    """HIP-graph capture and event timing on the current torch stream (the
+    stream the library's launches go to)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def capture(self, fn, idxs):
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(g, stream=s):
+            for i in idxs:
+                fn(i)
+        torch.cuda.synchronize()
+        # one untimed replay: a graph's first launch also uploads it, a cost
+        # that would otherwise land in the timed region
+        g.replay()
+        torch.cuda.synchronize()
+        return g
+
+    def timed_fn(self, fn):
+        torch = self.torch
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3, time.perf_counter() - w0
+
+    def timed(self, graph_all, graph_rem, n_full):
+        def run():
+            for _ in range(n_full):
+                graph_all.replay()
+            if graph_rem is not None:
+                graph_rem.replay()
+        return self.timed_fn(run)
 
 
 def main():
@@ -70,17 +114,84 @@ def main():
               "(how it would shard is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    import torch
+
+    import bit_rotated_kv_attn_amd as hip
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    hip.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tm = Timer(torch)
+
+    head = decode_workload(args.workload, args, args.steps, args.warmup, not args.no_bf16, tm)
+    cfg, rec = head.pop("cfg"), head
+    B = cfg["batch"]
+    result = {
+        "metric": "decode-attn tokens/s + achieved HBM GB/s (% peak) at 100k ctx, INT2 vs BF16",
+        "value": B / (rec["ms_per_step"] * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": rec["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": hip.COMPUTE_DTYPE, "data": "synthetic",
+        "config": rec["config"],
+        "roofline": rec["roofline"],
+        "kv_tokens_per_s": rec["kv_tokens_per_s"],
+        "int2_decode_us": rec["int2_decode_us"],
+        "decode_GBps": rec["decode_GBps"],
+    }
+    for k in ("bf16_comparator", "speedup_int2_vs_bf16_decode"):
+        if k in rec:
+            result[k] = rec[k]
+
+    # ---- what this part's HBM sustains for a plain stream: a 1 GiB device copy
+    # (512 MiB read + 512 MiB written per torch.neg), beside the spec peak of the roofline
+    n = (512 << 20) // 4
+    src = torch.randn(n, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        torch.neg(src, out=dst)
+    reps_copy = 10
+    copy_sec, _ = tm.timed_fn(lambda: [torch.neg(src, out=dst) for _ in range(reps_copy)])
+    copy_gbs = 2 * n * 4 * reps_copy / copy_sec / 1e9
+    achieved = rec["roofline"]["achieved"]
+    result["hbm_copy_probe"] = {"GBps": copy_gbs, "bytes_per_copy": 2 * n * 4, "kernel": "torch.neg",
+                                "scan_frac_of_copy": achieved / copy_gbs}
+    log(f"copy probe: {copy_gbs:.0f} GB/s; the scan reaches {achieved / copy_gbs:.1%} of it")
+    del src, dst
+
+    # ---- the other workloads, each in its own sub-record of the same line
+    if not args.no_extra:
+        extra = {}
+        if args.workload != "qwen3-8b-b28-100k":
+            torch.cuda.empty_cache()
+            sub = decode_workload("qwen3-8b-b28-100k", args, min(args.steps, 40), min(args.warmup, 5),
+                                  not args.no_bf16, tm)
+            sub.pop("cfg")
+            sub["tokens_per_s"] = sub["config"]["batch"] / (sub["ms_per_step"] * 1e-3)
+            extra["qwen3-8b-b28-100k"] = sub
+        torch.cuda.empty_cache()
+        extra["bulk-demotion"] = bulk_demotion(args, tm)
+        result["workloads"] = extra
+
+    # ---- CPU oracle on a bounded sample (reported baseline, not a target)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, "lloyd_max" if args.codebook == "lloyd-max"
+                                              else "uniform", args.groups or None)
+    print(json.dumps(result), flush=True)
+
+
+def decode_workload(name, args, K, warmup, with_bf16, tm):
+    """Time the decode step, the scan and the three-launch decode on one decode
+    workload; returns the record fields (and the generated inputs as "cfg")."""
     import numpy as np
     import torch
 
     import bit_rotated_kv_attn_amd as hip
     import synth
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    hip.lib()
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    cfg_index = WORKLOADS[args.workload]
+    cfg_index = WORKLOADS[name]
     lm = args.codebook == "lloyd-max"
     cb_flag = hip.CODEBOOK_LLOYD_MAX if lm else hip.CODEBOOK_UNIFORM
     grouped = args.groups == 64
@@ -91,10 +202,9 @@ def main():
     log(f"generated {shape.name} in {time.time() - t0:.1f}s")
     B, Hq, d = cfg["q"].shape
     n_kv, P = cfg["n_kv"], cfg["n_pages"]
-    G = Hq // n_kv
     hl = int(cfg["hist_len"].max())
 
-    def t(a, dtype=None):
+    def t(a):
         a = np.ascontiguousarray(a)
         if a.dtype == np.uint16:
             a = a.view(np.int16)
@@ -115,13 +225,14 @@ def main():
     # algorithmic bytes: every history token of a physical page once (a page
     # shared by several requests' tables needs reading only once), the BF16
     # windows and the block-table entries
-    ng = d // 64 if args.groups == 64 else 1   # (scale, zero) pairs per token and head
+    ng = d // 64 if grouped else 1   # (scale, zero) pairs per token and head
     hist_bytes = unique_tokens(cfg["block_table"], cfg["hist_len"]) * n_kv * (2 * d // 4 + 2 * 4 * ng)
     win_bytes = int((cfg["sink_len"] + cfg["recent_len"]).sum()) * n_kv * 4 * d
     table_bytes = int(sum(-(-int(h) // 64) for h in cfg["hist_len"])) * 4
     scan_bytes = hist_bytes + win_bytes + table_bytes
-    per_replica = (P * n_kv * 64 * (2 * d // 4 + 8 * (d // 64 if args.groups == 64 else 1))
-                   + 2 * cfg["sink_k"].nbytes + 2 * cfg["recent_k"].nbytes)
+    # the whole decode also reads q, R_K and R_V, and writes the output
+    decode_bytes = scan_bytes + q.numel() * 2 + 2 * r_k.numel() * 4 + B * Hq * d * 4
+    per_replica = (P * n_kv * 64 * (2 * d // 4 + 8 * ng) + 2 * cfg["sink_k"].nbytes + 2 * cfg["recent_k"].nbytes)
     R = args.replicas or max(2, math.ceil((1 << 30) / per_replica))
     log(f"replicas: {R} x {per_replica / 1e6:.1f} MB = {R * per_replica / 2**30:.2f} GiB "
         f"(MALL {MALL_BYTES >> 20} MiB)")
@@ -132,7 +243,7 @@ def main():
     for r in range(R):
         kc = torch.zeros((P, n_kv, 64 * d // 4), dtype=torch.uint8, device=dev)
         vc = torch.zeros_like(kc)
-        ks = torch.zeros((P, n_kv, 64 * (d // 64 if grouped else 1), 2), dtype=torch.int16, device=dev)
+        ks = torch.zeros((P, n_kv, 64 * ng, 2), dtype=torch.int16, device=dev)
         vs = torch.zeros_like(ks)
         hip.oscar_quantize_pack(hip.KIND_K | q_flags, hist_k, r_k, float(cfg["tau_k"]), hist_slot, kc, ks)
         hip.oscar_quantize_pack(hip.KIND_V | q_flags, hist_v, r_v, float(cfg["tau_v"]), hist_slot, vc, vs)
@@ -168,55 +279,17 @@ def main():
     def step(r):
         hip.oscar_decode_step(args=dargs[r], demote_k=dem[r][0], demote_v=dem[r][1])
 
-    def capture(fn, idxs):
-        g = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.graph(g, stream=s):
-            for i in idxs:
-                fn(i)
-        torch.cuda.synchronize()
-        # one untimed replay: a graph's first launch also uploads it, a cost
-        # that would otherwise land in the timed region
-        g.replay()
-        torch.cuda.synchronize()
-        return g
-
-    def timed_fn(fn):
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        w0 = time.perf_counter()
-        e0.record()
-        fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e-3, time.perf_counter() - w0
-
-    def timed(graph_all, graph_rem, n_full):
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        w0 = time.perf_counter()
-        e0.record()
-        for _ in range(n_full):
-            graph_all.replay()
-        if graph_rem is not None:
-            graph_rem.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e-3, time.perf_counter() - w0
-
     # ---- warmup (eager), then graphs
-    log(f"warmup: {args.warmup} steps")
-    for i in range(args.warmup):
+    log(f"{name}: warmup {warmup} steps")
+    for i in range(warmup):
         step(i % R)
     torch.cuda.synchronize()
-    K = args.steps
-    g_all = capture(step, range(R))
-    g_rem = capture(step, range(K % R)) if K % R else None
-    log(f"timing {K} steps")
-    sec, wall = timed(g_all, g_rem, K // R)
+    g_all = tm.capture(step, range(R))
+    g_rem = tm.capture(step, range(K % R)) if K % R else None
+    log(f"{name}: timing {K} steps")
+    sec, wall = tm.timed(g_all, g_rem, K // R)
     ms_per_step = sec * 1e3 / K
-    log(f"step: {ms_per_step * 1e3:.2f} us (wall {wall * 1e3 / K:.2f} us)")
+    log(f"step: {ms_per_step * 1e3:.2f} us (host wall clock {wall * 1e6 / K:.2f} us per step)")
 
     if args.copy_probe:
         n = (256 << 20) // 4
@@ -230,43 +303,44 @@ def main():
         del src, dst
 
     # ---- dominant kernel: the scan, R launches back to back per graph replay
-    g_scan = capture(lambda r: hip.oscar_decode_scan(args=dargs[r]), range(R))
+    g_scan = tm.capture(lambda r: hip.oscar_decode_scan(args=dargs[r]), range(R))
     n_scan = max(1, K // R)
-    scan_sec, _ = timed(g_scan, None, n_scan)
+    scan_sec, _ = tm.timed(g_scan, None, n_scan)
     scan_us = scan_sec * 1e6 / (n_scan * R)
-    g_dec = capture(lambda r: hip.oscar_decode_attn(args=dargs[r]), range(R))
-    dec_sec, _ = timed(g_dec, None, n_scan)
+    g_dec = tm.capture(lambda r: hip.oscar_decode_attn(args=dargs[r]), range(R))
+    dec_sec, _ = tm.timed(g_dec, None, n_scan)
     dec_us = dec_sec * 1e6 / (n_scan * R)
     achieved = scan_bytes / (scan_us * 1e-6) / 1e9
+    dec_gbs = decode_bytes / (dec_us * 1e-6) / 1e9
     log(f"scan kernel: {scan_us:.2f} us, {achieved:.0f} GB/s algorithmic ({achieved / HBM_PEAK_GBS:.1%} of peak); "
-        f"decode (3 kernels): {dec_us:.2f} us")
+        f"decode (3 kernels): {dec_us:.2f} us, {dec_gbs:.0f} GB/s ({dec_gbs / HBM_PEAK_GBS:.1%})")
 
-    result = {
-        "metric": "decode-attn tokens/s + achieved HBM GB/s (% peak) at 100k ctx, INT2 vs BF16",
-        "value": B / (ms_per_step * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_per_step,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": hip.COMPUTE_DTYPE, "data": "synthetic",
+    rec = {
+        "cfg": cfg, "ms_per_step": ms_per_step, "step_us": ms_per_step * 1e3,
         "config": {"workload": shape.name, "batch": B, "context": shape.context, "n_q_heads": Hq,
                    "n_kv_heads": n_kv, "head_dim": d, "sink": int(cfg["sink_len"][0]),
                    "history": hl, "recent": int(cfg["recent_len"][0]), "page_tokens": 64,
-                   "cache_replicas": R, "shared_prefix_pages": shared, "codebook": args.codebook, "group_channels": args.groups,
+                   "cache_replicas": R, "shared_prefix_pages": shared, "codebook": args.codebook,
+                   "group_channels": args.groups,
                    "step": "oscar_decode_step: demote K,V of 1 token/request + decode attention"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(args.workload + ("-lloyd-max" if lm else "") +
-                                                 ("-groups64" if grouped else "")),
+                     "traffic": measured_traffic(name + ("-lloyd-max" if lm else "") + ("-groups64" if grouped else "")),
                      "kernel": "decode_main_kernel (oscar_decode_scan)", "kernel_us": scan_us,
                      "bytes_per_launch": scan_bytes},
         "kv_tokens_per_s": float(cfg["hist_len"].sum() + cfg["sink_len"].sum() + cfg["recent_len"].sum())
                            / (ms_per_step * 1e-3),
         "int2_decode_us": dec_us,
+        # the whole decode (q rotation, scan, merge): its bytes over the three launches' time
+        "decode_GBps": dec_gbs, "decode_frac_of_peak": dec_gbs / HBM_PEAK_GBS, "decode_bytes": decode_bytes,
     }
+    del g_all, g_rem, g_scan, g_dec, dargs, dem, reps, ws
 
     # ---- BF16 comparator (same layer, whole context in BF16 pages)
-    if not args.no_bf16:
+    if with_bf16:
+        t0 = time.time()
         bf = synth.bf16_context_pages(cfg)
+        log(f"bf16 pages of {name} in {time.time() - t0:.1f}s")
         bf_bytes = bf["k_pages"].nbytes + bf["v_pages"].nbytes
         Rb = max(2, math.ceil((1 << 30) / bf_bytes))
         kp0, vp0 = t(bf["k_pages"]), t(bf["v_pages"])
@@ -283,38 +357,76 @@ def main():
                                        sm_scale=float(cfg["sm_scale"]))
         for r in range(Rb):
             bf16_step(r)
-        g_bf = capture(bf16_step, range(Rb))
+        g_bf = tm.capture(bf16_step, range(Rb))
         nb = max(1, K // Rb)
-        bf_sec, _ = timed(g_bf, None, nb)
+        bf_sec, _ = tm.timed(g_bf, None, nb)
         bf_us = bf_sec * 1e6 / (nb * Rb)
         bf_need = unique_tokens(bf["block_table"], bf["ctx_len"]) * n_kv * 4 * d
-        result["bf16_comparator"] = {"decode_us": bf_us, "tokens_per_s": B / (bf_us * 1e-6),
-                                     "algorithmic_GBps": bf_need / (bf_us * 1e-6) / 1e9, "replicas": Rb,
-                                     "kernel": "oscar_decode_attn_bf16"}
-        result["speedup_int2_vs_bf16_decode"] = bf_us / dec_us
+        rec["bf16_comparator"] = {"decode_us": bf_us, "tokens_per_s": B / (bf_us * 1e-6),
+                                  "algorithmic_GBps": bf_need / (bf_us * 1e-6) / 1e9, "replicas": Rb,
+                                  "kernel": "oscar_decode_attn_bf16"}
+        rec["speedup_int2_vs_bf16_decode"] = bf_us / dec_us
         log(f"bf16 comparator: {bf_us:.2f} us/decode; INT2 decode speedup {bf_us / dec_us:.2f}x")
-        del bre, kp0, vp0
+        del bre, kp0, vp0, g_bf
+    return rec
 
-    # ---- what this part's HBM sustains for a plain stream: a 1 GiB device copy
-    # (512 MiB read + 512 MiB written per torch.neg), beside the spec peak of the roofline
-    n = (512 << 20) // 4
-    src = torch.randn(n, device=dev)
-    dst = torch.empty_like(src)
-    for _ in range(2):
-        torch.neg(src, out=dst)
-    reps_copy = 10
-    copy_sec, _ = timed_fn(lambda: [torch.neg(src, out=dst) for _ in range(reps_copy)])
-    copy_gbs = 2 * n * 4 * reps_copy / copy_sec / 1e9
-    result["hbm_copy_probe"] = {"GBps": copy_gbs, "bytes_per_copy": 2 * n * 4, "kernel": "torch.neg",
-                                "scan_frac_of_copy": achieved / copy_gbs}
-    log(f"copy probe: {copy_gbs:.0f} GB/s; the scan reaches {achieved / copy_gbs:.1%} of it")
-    del src, dst
 
-    # ---- CPU oracle on a bounded sample (reported baseline, not a target)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, "lloyd_max" if lm else "uniform",
-                                              args.groups or None)
-    print(json.dumps(result), flush=True)
+def bulk_demotion(args, tm):
+    """Bulk demotion of 131072 tokens x 8 KV heads x 128 for K and for V, in
+    one oscar_quantize_pack launch per tensor, timed over repeated launches
+    (K, V, K, V, ...) between HIP events on the launching stream.  Algorithmic
+    bytes per tensor: read the bf16 tokens, R and the slots; write the codes
+    and the (scale, zero) pairs.  Flops: the rotation x R, 2 d^2 per token
+    and head."""
+    import numpy as np
+    import torch
+
+    import bit_rotated_kv_attn_amd as hip
+    import synth
+
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    cfg = synth.make_bulk_demotion_config()
+    log(f"generated {cfg['name']} in {time.time() - t0:.1f}s")
+    n_tok, n_kv, d, P = cfg["x_k"].shape[0], cfg["n_kv"], cfg["head_dim"], cfg["n_pages"]
+
+    def t(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    x = {k: t(cfg["x_" + k]) for k in ("k", "v")}
+    rot = {k: t(cfg["r_" + k]) for k in ("k", "v")}
+    slot = t(cfg["dst_slot"])
+    pools = {k: (torch.zeros((P, n_kv, 64 * d // 4), dtype=torch.uint8, device=dev),
+                 torch.zeros((P, n_kv, 64, 2), dtype=torch.int16, device=dev)) for k in ("k", "v")}
+    kinds = {"k": hip.KIND_K, "v": hip.KIND_V}
+
+    def launch(i):
+        k = "kv"[i % 2]
+        hip.oscar_quantize_pack(kinds[k], x[k], rot[k], float(cfg["tau_" + k]), slot, *pools[k])
+
+    for i in range(4):
+        launch(i)
+    torch.cuda.synchronize()
+    n = 2 * max(4, min(args.steps, 20))
+    g = tm.capture(launch, range(n))
+    sec, _ = tm.timed(g, None, 1)
+    us = sec * 1e6 / n
+    bytes_per = n_tok * n_kv * (2 * d + d // 4 + 4) + rot["k"].numel() * 4 + slot.numel() * 4
+    flops_per = 2.0 * d * d * n_kv * n_tok
+    gbs = bytes_per / (us * 1e-6) / 1e9
+    tfs = flops_per / (us * 1e-6) / 1e12
+    peak = hip.DEMOTION_MATMUL_PEAK_TFLOPS
+    log(f"bulk demotion: {us:.1f} us per tensor, {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM peak), "
+        f"{tfs:.1f} TFLOP/s ({tfs / peak:.1%} of the {hip.DEMOTION_MATMUL_DTYPE} matrix peak)")
+    del g, x, pools
+    return {"config": {"workload": cfg["name"], "tokens": n_tok, "n_kv_heads": n_kv, "head_dim": d,
+                       "tensors": "K and V, one launch each", "kernel": "oscar_quantize_pack (quantize_pack_kernel)"},
+            "us_per_tensor": us, "tokens_per_s": n_tok / (2 * us * 1e-6),
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": bytes_per, "kernel_us": us},
+            "contraction": {"dtype": hip.DEMOTION_MATMUL_DTYPE, "achieved": tfs, "peak": peak, "unit": "TFLOP/s",
+                            "frac": tfs / peak, "flops_per_launch": flops_per}}
 
 
 SCAN_SOURCES = ("bit_rotated_kv_attn_amd/csrc/decode.hip", "bit_rotated_kv_attn_amd/csrc/common.hpp")

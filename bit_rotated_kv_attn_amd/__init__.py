@@ -28,6 +28,8 @@ GROUPS_64 = 0x200
 # arithmetic the kernels of this build compute in (reported by bench.py)
 COMPUTE_DTYPE = ("QK i8 MFMA (exact integer digits), PV f16 MFMA (fp16 weight pairs) + f32 sums and softmax; "
                  "f64 rotation in demotion")
+# the bulk demotion's rotation x R runs on the fp64 matrix cores (MI355X dense fp64 MFMA peak)
+DEMOTION_MATMUL_DTYPE, DEMOTION_MATMUL_PEAK_TFLOPS = "f64", 78.6
 OSCAR_OK, OSCAR_EINVAL, OSCAR_EUNSUPPORTED, OSCAR_EWORKSPACE, OSCAR_EHIP = range(5)
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liboscar.so")
 ABI_VERSION = 2   # OSCAR_ABI_VERSION of the oscar.h these mirrors follow
@@ -182,7 +184,9 @@ def decode_args(*, q, sink_k, sink_v, recent_k, recent_v, sink_len, recent_len, 
     shared_pages: leading history pages every request holds at the same ids (0: none);
     codebook: CODEBOOK_UNIFORM or CODEBOOK_LLOYD_MAX, as the pools were demoted;
     group_channels: 0 (whole-head groups) or 64, as the pools were demoted.
-    The tensors must stay alive while the call (or a captured graph) uses them."""
+    The returned DecodeArgs holds a reference to every tensor it points to
+    (``keep``), so tensors made inline stay allocated while the args live; a
+    captured graph that replays the call must keep the args alive too."""
     B, Hq, d = q.shape
     n_kv = sink_k.shape[1]
     if tuple(out.shape) != (B, Hq, d):
@@ -203,6 +207,8 @@ def decode_args(*, q, sink_k, sink_v, recent_k, recent_v, sink_len, recent_len, 
                    block_table=_ptr(block_table, 4, "block_table"), max_pages=block_table.shape[1],
                    r_k=_ptr(r_k, 4, "r_k"), r_v=_ptr(r_v, 4, "r_v"), out=_ptr(out, 4, "out"),
                    shared_pages=int(shared_pages), codebook=int(codebook), group_channels=int(group_channels))
+    a.keep = (q, sink_k, sink_v, recent_k, recent_v, sink_len, recent_len, hist_len, k_codes, v_codes, k_sz, v_sz,
+              block_table, r_k, r_v, out, workspace)
     return a, _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size()
 
 
@@ -237,8 +243,8 @@ def oscar_decode_merge(*, args=None, stream=None, **kw) -> None:
 def demote_args(*, x, rot, clip: float, dst_slot, codes, scale_zero, src_idx=None, n_src=None,
                 x_tok_stride=None, x_head_stride=None) -> DemoteArgs:
     """Marshal one tensor's demotion for :func:`oscar_decode_step` (arguments
-    as for :func:`oscar_quantize_pack`).  The tensors must stay alive while
-    the call (or a captured graph) uses them."""
+    as for :func:`oscar_quantize_pack`).  The returned DemoteArgs holds a
+    reference to every tensor it points to (``keep``)."""
     n_kv, d = rot.shape[0], rot.shape[-1]
     if x_tok_stride is None:
         if x.dim() != 3 or x.shape[1:] != (n_kv, d):
@@ -259,6 +265,7 @@ def demote_args(*, x, rot, clip: float, dst_slot, codes, scale_zero, src_idx=Non
                    codes=_ptr(codes, 1, "codes"), scale_zero=_ptr(scale_zero, 2, "scale_zero"),
                    n_pages=int(codes.shape[0]))
     a.sz_pairs = int(scale_zero.shape[2])   # (scale, zero) pairs per (page, head) of this pool
+    a.keep = (x, src_idx, rot, dst_slot, codes, scale_zero)
     return a
 
 
