@@ -30,9 +30,11 @@ COMPUTE_DTYPE = ("QK i8 MFMA (exact integer digits), PV f16 MFMA (fp16 weight pa
                  "f64 rotation in demotion")
 # the bulk demotion's rotation x R runs on the fp64 matrix cores (MI355X dense fp64 MFMA peak)
 DEMOTION_MATMUL_DTYPE, DEMOTION_MATMUL_PEAK_TFLOPS = "f64", 78.6
-OSCAR_OK, OSCAR_EINVAL, OSCAR_EUNSUPPORTED, OSCAR_EWORKSPACE, OSCAR_EHIP = range(5)
+OSCAR_OK, OSCAR_EINVAL, OSCAR_EUNSUPPORTED, OSCAR_EWORKSPACE, OSCAR_EHIP, OSCAR_ESCRATCH = range(6)
+# bytes of the static per-GPU scratch buffer of oscar_decode_step_static (oscar.h)
+STATIC_SCRATCH_BYTES = 32 << 20
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liboscar.so")
-ABI_VERSION = 2   # OSCAR_ABI_VERSION of the oscar.h these mirrors follow
+ABI_VERSION = 3   # OSCAR_ABI_VERSION of the oscar.h these mirrors follow
 
 _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 
@@ -89,6 +91,9 @@ def lib() -> ctypes.CDLL:
     L.oscar_decode_step.restype = ctypes.c_int
     L.oscar_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(DemoteArgs),
                                     ctypes.POINTER(DemoteArgs), _vp, _sz, _vp]
+    L.oscar_decode_step_static.restype = ctypes.c_int
+    L.oscar_decode_step_static.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(DemoteArgs),
+                                           ctypes.POINTER(DemoteArgs), _vp]
     L.oscar_decode_bf16_workspace_bytes.restype = _sz
     L.oscar_decode_bf16_workspace_bytes.argtypes = [_i32] * 5
     L.oscar_decode_attn_bf16.restype = ctypes.c_int
@@ -172,7 +177,7 @@ def oscar_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, max_his
 
 
 def decode_args(*, q, sink_k, sink_v, recent_k, recent_v, sink_len, recent_len, hist_len, max_hist_len: int,
-                k_codes, v_codes, k_sz, v_sz, block_table, r_k, r_v, out, workspace,
+                k_codes, v_codes, k_sz, v_sz, block_table, r_k, r_v, out, workspace=None,
                 sm_scale: float | None = None, shared_pages: int = 0, codebook: int = CODEBOOK_UNIFORM,
                 group_channels: int = 0):
     """Marshal tensors into (DecodeArgs, workspace pointer, workspace bytes).
@@ -180,7 +185,8 @@ def decode_args(*, q, sink_k, sink_v, recent_k, recent_v, sink_len, recent_len, 
     q bf16 [B][Hq][d]; sink_k/v bf16 [B][n_kv][sink_cap][d]; recent_k/v bf16
     [B][n_kv][recent_cap][d]; *_len int32 [B]; pools as for oscar_quantize_pack;
     block_table int32 [B][max_pages]; r_k/r_v fp32 [n_kv][d][d]; out fp32
-    [B][Hq][d]; workspace uint8 device tensor (size from oscar_decode_workspace_bytes);
+    [B][Hq][d]; workspace uint8 device tensor (size from oscar_decode_workspace_bytes;
+    None for oscar_decode_step_static, which brings its own);
     shared_pages: leading history pages every request holds at the same ids (0: none);
     codebook: CODEBOOK_UNIFORM or CODEBOOK_LLOYD_MAX, as the pools were demoted;
     group_channels: 0 (whole-head groups) or 64, as the pools were demoted.
@@ -209,7 +215,8 @@ def decode_args(*, q, sink_k, sink_v, recent_k, recent_v, sink_len, recent_len, 
                    shared_pages=int(shared_pages), codebook=int(codebook), group_channels=int(group_channels))
     a.keep = (q, sink_k, sink_v, recent_k, recent_v, sink_len, recent_len, hist_len, k_codes, v_codes, k_sz, v_sz,
               block_table, r_k, r_v, out, workspace)
-    return a, _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size()
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return a, _ptr(workspace, name="workspace"), nbytes
 
 
 def _decode(name: str, args, stream, kw):
@@ -283,6 +290,25 @@ def oscar_decode_step(*, args, demote_k=None, demote_v=None, stream=None) -> Non
                                  ctypes.byref(demote_v) if demote_v is not None else None, ws, nbytes,
                                  _stream(stream))
     _check(st, "oscar_decode_step")
+
+
+def oscar_decode_step_static(*, args, demote_k=None, demote_v=None, stream=None) -> None:
+    """oscar_decode_step with its workspace in the library's static per-GPU
+    scratch buffer (see oscar_decode_step_static in oscar.h): for callers that
+    cannot allocate device memory.  ``args`` is a :func:`decode_args` tuple;
+    its workspace, if any, is not used.  Raises ValueError (OSCAR_ESCRATCH)
+    when the sizes need more than STATIC_SCRATCH_BYTES.  Calls that can
+    overlap on one GPU race on the shared buffer."""
+    a = args[0]
+    pairs = PAGE * (a.head_dim // 64 if a.group_channels == 64 else 1)
+    for name, dm in (("demote_k", demote_k), ("demote_v", demote_v)):
+        if dm is not None and getattr(dm, "sz_pairs", pairs) != pairs:
+            raise ValueError(f"{name}: its scale/zero pool holds {dm.sz_pairs} pairs per (page, head); "
+                             f"group_channels={a.group_channels} writes {pairs}")
+    st = lib().oscar_decode_step_static(ctypes.byref(a),
+                                        ctypes.byref(demote_k) if demote_k is not None else None,
+                                        ctypes.byref(demote_v) if demote_v is not None else None, _stream(stream))
+    _check(st, "oscar_decode_step_static")
 
 
 def oscar_decode_bf16_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, max_ctx_len) -> int:

@@ -1,6 +1,8 @@
 // C ABI of liboscar: argument validation (host only, before any HIP call),
 // workspace sizing and dispatch to the kernel launchers.
+#include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "common.hpp"
 
@@ -39,6 +41,9 @@ const char* oscar_status_str(int status) {
     case OSCAR_EUNSUPPORTED: return "unsupported shape (head_dim must be 64 or 128; query heads per KV head 1, 2, 4, 8 or 16)";
     case OSCAR_EWORKSPACE: return "workspace missing, misaligned or smaller than the size query returned";
     case OSCAR_EHIP: return "HIP runtime error";
+    case OSCAR_ESCRATCH:
+      return "the decode needs more scratch than the static buffer of oscar_decode_step_static holds "
+             "(OSCAR_STATIC_SCRATCH_BYTES); call oscar_decode_step with a workspace";
     default: return "unknown status";
   }
 }
@@ -116,14 +121,53 @@ oscar_status check_demote(const oscar_demote_args* d, int32_t n_kv) {
   return OSCAR_OK;
 }
 
+// Static scratch of oscar_decode_step_static: one copy per GPU in the code
+// object's device memory.  In host code `scratch` is only a symbol handle;
+// the buffer's address on a device comes from hipGetSymbolAddress, looked up
+// once per device (with that device current) and kept in scratch_ptr.
+__device__ __attribute__((aligned(256))) uint8_t scratch[OSCAR_STATIC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 256;
+std::atomic<void*> scratch_ptr[kMaxDevices];
+std::mutex scratch_mu;
+
+oscar_status static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return OSCAR_EHIP;
+  void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    p = scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return OSCAR_EHIP;
+      scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return OSCAR_OK;
+}
+
 oscar_status run_phases(const oscar_decode_args* a, void* workspace, size_t workspace_bytes,
                         hipStream_t stream, int first, int last, const oscar_demote_args* dk = nullptr,
-                        const oscar_demote_args* dv = nullptr) {
+                        const oscar_demote_args* dv = nullptr, bool use_static = false) {
   DecodePlan plan;
-  oscar_status st = check_decode(a, workspace, workspace_bytes, &plan);
+  oscar_status st;
+  if (use_static) {
+    // every check first (the workspace one with a stand-in address), then the
+    // scratch address, the one HIP call before the launches
+    if (!a) return OSCAR_EINVAL;
+    if (check_decode_shape(a->batch, a->n_q_heads, a->n_kv_heads, a->head_dim, a->max_hist_len, a->sink_cap,
+                           a->recent_cap) == OSCAR_OK &&
+        make_decode_plan(a->batch, a->n_q_heads, a->n_kv_heads, a->head_dim, a->max_hist_len, a->sink_cap,
+                         a->recent_cap).total > OSCAR_STATIC_SCRATCH_BYTES)
+      return OSCAR_ESCRATCH;
+    st = check_decode(a, reinterpret_cast<void*>(uintptr_t(256)), OSCAR_STATIC_SCRATCH_BYTES, &plan);
+  } else {
+    st = check_decode(a, workspace, workspace_bytes, &plan);
+  }
   if (st != OSCAR_OK) return st;
   if ((st = check_demote(dk, a->n_kv_heads)) != OSCAR_OK || (st = check_demote(dv, a->n_kv_heads)) != OSCAR_OK)
     return st;
+  if (use_static && (st = static_scratch(&workspace)) != OSCAR_OK) return st;
   const bool demote = (dk && dk->n_tok > 0) || (dv && dv->n_tok > 0);
   if (a->batch == 0 && !demote) return OSCAR_OK;
   for (int ph = first; ph <= last; ++ph) {
@@ -145,6 +189,11 @@ oscar_status oscar_decode_step(const oscar_decode_args* a, const oscar_demote_ar
                                const oscar_demote_args* demote_v, void* workspace, size_t workspace_bytes,
                                hipStream_t stream) {
   return run_phases(a, workspace, workspace_bytes, stream, kPhaseRotate, kPhaseMerge, demote_k, demote_v);
+}
+
+oscar_status oscar_decode_step_static(const oscar_decode_args* a, const oscar_demote_args* demote_k,
+                                      const oscar_demote_args* demote_v, hipStream_t stream) {
+  return run_phases(a, nullptr, 0, stream, kPhaseRotate, kPhaseMerge, demote_k, demote_v, true);
 }
 
 oscar_status oscar_decode_rotate_query(const oscar_decode_args* a, void* workspace, size_t workspace_bytes,

@@ -19,7 +19,8 @@
  * Conventions shared by every entry point:
  *  - Pointers named in a signature are DEVICE pointers owned by the caller,
  *    unless documented as host.  The library allocates, frees and
- *    synchronises nothing and keeps no mutable global state.  Work is
+ *    synchronises nothing.  It keeps no mutable global state, except the
+ *    static per-device scratch buffer of oscar_decode_step_static.  Work is
  *    enqueued on `stream` (NULL = the default stream); results are valid
  *    after the caller synchronises that stream.
  *  - All argument checks run on the host BEFORE any HIP call.  A failed
@@ -52,7 +53,7 @@
 extern "C" {
 #endif
 
-#define OSCAR_ABI_VERSION 2
+#define OSCAR_ABI_VERSION 3
 #define OSCAR_PAGE_TOKENS 64
 
 #ifndef OSCAR_API
@@ -64,7 +65,9 @@ typedef enum oscar_status {
   OSCAR_EINVAL = 1,        /* a pointer, size or scalar argument is invalid */
   OSCAR_EUNSUPPORTED = 2,  /* a valid shape this build has no kernel for   */
   OSCAR_EWORKSPACE = 3,    /* workspace missing, misaligned or too small    */
-  OSCAR_EHIP = 4           /* the HIP runtime reported an error             */
+  OSCAR_EHIP = 4,          /* the HIP runtime reported an error             */
+  OSCAR_ESCRATCH = 5       /* the call needs more than the static scratch
+                              buffer of oscar_decode_step_static holds      */
 } oscar_status;
 
 typedef enum oscar_kind { OSCAR_KIND_K = 0, OSCAR_KIND_V = 1 } oscar_kind;
@@ -271,6 +274,27 @@ typedef struct oscar_demote_args {
 OSCAR_API oscar_status oscar_decode_step(const oscar_decode_args* args, const oscar_demote_args* demote_k,
                                          const oscar_demote_args* demote_v, void* workspace,
                                          size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * oscar_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, and serving loops
+ * or harnesses that forbid hipMalloc.  The workspace lives in a static
+ * device buffer of OSCAR_STATIC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends; its address on the current
+ * device is looked up (hipGetSymbolAddress) on the first call there.
+ * Arguments, results and the other status codes are those of
+ * oscar_decode_step.  A call whose oscar_decode_workspace_bytes exceeds
+ * OSCAR_STATIC_SCRATCH_BYTES returns OSCAR_ESCRATCH before any HIP call
+ * (use oscar_decode_step with a workspace then).  The call allocates and
+ * frees nothing.  Every call on one GPU uses the same buffer: calls that
+ * can overlap on one GPU (on different streams, or concurrent host threads
+ * on one stream) race and must be serialised by the caller.  Nothing in
+ * the buffer needs clearing between calls; each call writes what it reads.
+ */
+#define OSCAR_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+OSCAR_API oscar_status oscar_decode_step_static(const oscar_decode_args* args,
+                                                const oscar_demote_args* demote_k,
+                                                const oscar_demote_args* demote_v, hipStream_t stream);
 
 /*
  * BF16 comparator: plain decode attention with the whole context held in

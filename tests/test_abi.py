@@ -28,15 +28,15 @@ def test_library_exports_every_declared_function():
     L = hip.lib()
     for n in declared_functions():
         assert hasattr(L, n), n
-    assert hip.oscar_abi_version() == hip.ABI_VERSION == 2
+    assert hip.oscar_abi_version() == hip.ABI_VERSION == 3
     # the binding offers a function of the same name for each entry point
     for n in declared_functions():
         assert callable(getattr(hip, n)), n
 
 
 def test_status_strings():
-    for s in range(5):
-        assert hip.oscar_status_str(s)
+    for s in range(6):
+        assert hip.oscar_status_str(s) != "unknown status"
     assert hip.oscar_status_str(99) == "unknown status"
 
 
@@ -157,3 +157,19 @@ def test_decode_step_validation(kw, status):
                                None) == hip.OSCAR_EWORKSPACE   # workspace checked first
     assert L.oscar_decode_step(ctypes.byref(_decode_args(batch=0, q=None, out=None)), None, ctypes.byref(dk),
                                None, 0, None) == status
+
+
+def test_static_step_checks_sizes_before_any_hip_call():
+    """oscar_decode_step_static: sizes past its static scratch buffer return
+    OSCAR_ESCRATCH, and invalid arguments OSCAR_EINVAL, with no HIP call
+    (this host has no GPU)."""
+    big = hip.DecodeArgs(batch=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, sm_scale=0.088, sink_cap=64,
+                         recent_cap=256, max_hist_len=99680, max_pages=1558, n_pages=1)
+    need = hip.oscar_decode_workspace_bytes(4096, 32, 8, 128, 99680)
+    assert need > hip.STATIC_SCRATCH_BYTES
+    assert hip.lib().oscar_decode_step_static(ctypes.byref(big), None, None, None) == hip.OSCAR_ESCRATCH
+    small = hip.DecodeArgs(batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128, sm_scale=0.088, sink_cap=64,
+                           recent_cap=256, max_hist_len=99680, max_pages=1558, n_pages=1)   # null pointers
+    assert hip.oscar_decode_workspace_bytes(1, 32, 8, 128, 99680) <= hip.STATIC_SCRATCH_BYTES
+    assert hip.lib().oscar_decode_step_static(ctypes.byref(small), None, None, None) == hip.OSCAR_EINVAL
+    assert hip.lib().oscar_decode_step_static(None, None, None, None) == hip.OSCAR_EINVAL
