@@ -27,9 +27,9 @@ CODEBOOK_UNIFORM, CODEBOOK_LLOYD_MAX = 0, 0x100
 GROUPS_64 = 0x200
 # arithmetic the kernels of this build compute in (reported by bench.py)
 COMPUTE_DTYPE = ("QK i8 MFMA (exact integer digits), PV f16 MFMA (fp16 weight pairs) + f32 sums and softmax; "
-                 "f64 rotation in demotion")
-# the bulk demotion's rotation x R runs on the fp64 matrix cores (MI355X dense fp64 MFMA peak)
-DEMOTION_MATMUL_DTYPE, DEMOTION_MATMUL_PEAK_TFLOPS = "f64", 78.6
+                 "bf16x3 MFMA rotation with certified decisions and fp64 exact recomputes in demotion")
+# the bulk demotion's rotation x R runs on the bf16 matrix cores (MI355X dense bf16 MFMA peak)
+DEMOTION_MATMUL_DTYPE, DEMOTION_MATMUL_PEAK_TFLOPS = "bf16", 2500.0
 OSCAR_OK, OSCAR_EINVAL, OSCAR_EUNSUPPORTED, OSCAR_EWORKSPACE, OSCAR_EHIP, OSCAR_ESCRATCH = range(6)
 # bytes of the static per-GPU scratch buffer of oscar_decode_step_static (oscar.h)
 STATIC_SCRATCH_BYTES = 32 << 20
