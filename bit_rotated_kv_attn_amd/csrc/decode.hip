@@ -30,8 +30,9 @@
 //   1. prepare_kernel       q_rot = q R_K[g] per query head -> MFMA digit
 //                           operands
 //   2. decode_main_kernel   one grid: INT2 history splits (those inside a
-//                           declared shared prefix read once per request
-//                           pair), then the BF16 sink / recent chunks; each
+//                           declared shared prefix read once per pack of
+//                           two or four requests), then the BF16 sink /
+//                           recent chunks; each
 //                           block writes an (m, l, acc) partial per head
 //   3. merge_kernel         LSE merge of the history partials, * R_V^T, LSE merge
 //      (merge_unit_kernel)  with the BF16 partials, normalise (one block per
@@ -64,8 +65,10 @@ struct DecodeDev {
   int B, Hq, n_kv, G, NB, sink_cap, recent_cap, max_hist_len, max_pages;
   int splits, pps, chunks, sink_chunks, bf_blocks;   // bf_blocks: BF16 blocks per unit (one per chunk)
   // shared-prefix packing (G = 4 only): the first n_pref splits lie inside the
-  // prefix and are read once for each of the `pairs` request pairs (2i, 2i+1)
-  int n_pref, pairs;
+  // prefix and are read once for each of the `packs` packs of `pack` requests
+  // (requests pack*i .. pack*i + pack - 1; pack = 2 or 4); the requests past the
+  // last whole pack read them on their own
+  int n_pref, packs, pack;
   int lm;   // the pools hold Lloyd-Max codes (oscar.h OSCAR_CODEBOOK_LLOYD_MAX)
   int ng;   // (scale, zero) groups per head: 1, or 2 with 64-channel groups at d = 128
   float sm_log2;
@@ -566,14 +569,15 @@ __device__ __forceinline__ void load_hist_operands(const DecodeDev& p, int b, in
   }
 }
 
-// The QK operands of a request pair (b, b+1) at group size 4: head block nb
-// of the 8-head wave is request b+nb's only head block.
-template <int D>
-__device__ __forceinline__ void load_pair_operands(const DecodeDev& p, int b, int g, int lane, HistOperands<D, 8>& o) {
+// The QK operands of a pack of PACK requests b .. b+PACK-1 at group size 4:
+// head block nb of the 4*PACK-head wave is request b+nb's only head block.
+template <int D, int PACK>
+__device__ __forceinline__ void load_pack_operands(const DecodeDev& p, int b, int g, int lane,
+                                                   HistOperands<D, 4 * PACK>& o) {
   constexpr int NCH = D / 64;
   const int grp = lane >> 4;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
+  for (int nb = 0; nb < PACK; ++nb) {
     const int unit = (b + nb) * p.n_kv + g;
     o.ca[nb] = p.qa[(size_t)(b + nb) * p.Hq + g * 4 + grp];
 #pragma unroll
@@ -1079,13 +1083,21 @@ __device__ __forceinline__ void demote_step_block(const DecodeDev& p, int id, co
 #ifndef OSCAR_SCAN_WAVES_PER_SIMD
 #define OSCAR_SCAN_WAVES_PER_SIMD 2
 #endif
-template <int D, int G, bool LM, int NG>
-__global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) void decode_main_kernel(DecodeDev p) {
+// Waves per SIMD the scan is compiled for: the 16-head wave (G = 16, or four
+// requests of group size 4 in one wave) fits two per SIMD without spills with
+// the uniform codebook and whole-head groups, and one otherwise.
+template <int G, bool LM, int NG, int PACK>
+constexpr int scan_waves_per_simd() {
+  return (G > 8 || PACK > 2) && (LM || NG == 2) ? 1 : OSCAR_SCAN_WAVES_PER_SIMD;
+}
+
+template <int D, int G, bool LM, int NG, int PACK = 2>
+__global__ __launch_bounds__(kBlock, (scan_waves_per_simd<G, LM, NG, PACK>())) void decode_main_kernel(DecodeDev p) {
   constexpr int NB = (G + 3) / 4;
   using RG = Ring<D, NB, NG>;
-  // a group-4 kernel also runs 8-head waves (two requests) on shared-prefix splits
+  // a group-4 kernel also runs 4*PACK-head waves (PACK requests) on shared-prefix splits
   constexpr int kHistOwn = 4 * RG::kWaveBytes;
-  constexpr int kHistPair = G == 4 ? 4 * Ring<D, 2, NG>::kWaveBytes : 0;
+  constexpr int kHistPair = G == 4 ? 4 * Ring<D, PACK, NG>::kWaveBytes : 0;
   constexpr int kHistBytes = kHistOwn > kHistPair ? kHistOwn : kHistPair;
   constexpr int kBf16Bytes = 4 * bf16_lds_bytes<D, G>();
   constexpr int kSmem = kHistBytes > kBf16Bytes ? kHistBytes : kBf16Bytes;
@@ -1097,12 +1109,14 @@ __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) vo
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int units = p.B * p.n_kv;
   const int id = blockIdx.x;
-  // block ids: the shared-prefix splits read for request pairs (split, pair,
-  // KV head), the other history splits (split, request, KV head), an odd last
-  // request's prefix splits (split, KV head), then the BF16 chunks
-  const int n_packed = p.n_pref * p.pairs * p.n_kv;
+  // block ids: the shared-prefix splits read for request packs (split, pack,
+  // KV head), the other history splits (split, request, KV head), the prefix
+  // splits of the requests past the last whole pack (split, request, KV head),
+  // then the BF16 chunks
+  const int n_packed = p.n_pref * p.packs * p.n_kv;
   const int n_rest = (p.splits - p.n_pref) * units;
-  const int n_hist = n_packed + n_rest + p.n_pref * (p.B & 1) * p.n_kv;
+  const int left = p.B - p.packs * p.pack;
+  const int n_hist = n_packed + n_rest + p.n_pref * left * p.n_kv;
   bool poison = false;
 
   if (id >= n_hist) {
@@ -1158,38 +1172,46 @@ __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) vo
 
   if constexpr (G == 4) {
     if (id < n_packed) {
-      // ---- a split inside the shared prefix for requests b and b+1: one
-      // 8-head wave reads each page once for both
-      using RP = Ring<D, 2, NG>;
-      static_assert(8 * part_row(D) * 4 <= RP::kWaveBytes, "merge slot must fit in the wave's ring");
-      const int per_split = p.pairs * p.n_kv;
-      const int split = id / per_split, pair = (id % per_split) / p.n_kv, g = id % p.n_kv;
-      const int b = 2 * pair;
+      // ---- a split inside the shared prefix for requests b .. b+PACK-1: one
+      // 4*PACK-head wave reads each page once for all of them
+      constexpr int GP = 4 * PACK;
+      using RP = Ring<D, PACK, NG>;
+      static_assert(GP * part_row(D) * 4 <= RP::kWaveBytes, "merge slot must fit in the wave's ring");
+      const int per_split = p.packs * p.n_kv;
+      const int split = id / per_split, pk = (id % per_split) / p.n_kv, g = id % p.n_kv;
+      const int b = PACK * pk;
       const int per_wave = (p.pps + 3) / 4;
       const int ws0 = split * p.pps + wave * per_wave;
       const int pe = split * p.pps + p.pps;   // split end; the prefix holds it whole
       const bool mine = lane < per_wave && ws0 + lane < pe;
       const int32_t* row = p.block_table + (size_t)b * p.max_pages;
       const int pid_lane = mine ? row[ws0 + lane] : -1;
-      const int pid_other = mine ? row[p.max_pages + ws0 + lane] : -1;
-      HistOperands<D, 8> qo;
-      load_pair_operands<D>(p, b, g, lane, qo);
-      const int hl0 = p.hist_len[b], hl1 = p.hist_len[b + 1];
+      int pid_other[PACK - 1], hlr[PACK];
+#pragma unroll
+      for (int r = 1; r < PACK; ++r) pid_other[r - 1] = mine ? row[(size_t)r * p.max_pages + ws0 + lane] : -1;
+      HistOperands<D, GP> qo;
+      load_pack_operands<D, PACK>(p, b, g, lane, qo);
+#pragma unroll
+      for (int r = 0; r < PACK; ++r) hlr[r] = p.hist_len[b + r];
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      const int full = pe * kPage;   // both histories must cover the split
-      if (hl0 < full || hl1 < full || hl0 > p.max_hist_len || hl1 > p.max_hist_len || __any(pid_lane != pid_other))
-        poison = true;
+      const int full = pe * kPage;   // every history of the pack must cover the split
+      bool bad = false;
+#pragma unroll
+      for (int r = 0; r < PACK; ++r) bad |= hlr[r] < full || hlr[r] > p.max_hist_len;
+#pragma unroll
+      for (int r = 1; r < PACK; ++r) bad |= pid_other[r - 1] != pid_lane;
+      if (__any(bad)) poison = true;
       const int count =
           __builtin_amdgcn_readfirstlane(poison ? 0 : max(0, min(ws0 + per_wave, pe) - ws0));
       uint8_t* ring = smem + wave * RP::kWaveBytes;
-      hist_wave<D, 8, LM, NG>(p, g, ws0, count, full, pid_lane, qo, ring, reinterpret_cast<float*>(ring), poison,
-                              lane);
+      hist_wave<D, GP, LM, NG>(p, g, ws0, count, full, pid_lane, qo, ring, reinterpret_cast<float*>(ring), poison,
+                               lane);
       if (lane == 0) flags[wave] = poison ? 1 : 0;
       __syncthreads();
       const size_t rows = (size_t)4 * part_row(D);
-      combine_block<8, D, 4>(reinterpret_cast<const float*>(smem), RP::kWaveBytes / 4, flags,
-                             p.hpart + (((size_t)b * p.n_kv + g) * p.splits + split) * rows, tid,
-                             (size_t)p.n_kv * p.splits * rows);
+      combine_block<GP, D, 4>(reinterpret_cast<const float*>(smem), RP::kWaveBytes / 4, flags,
+                              p.hpart + (((size_t)b * p.n_kv + g) * p.splits + split) * rows, tid,
+                              (size_t)p.n_kv * p.splits * rows);
       return;
     }
   }
@@ -1201,11 +1223,11 @@ __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : OSCAR_SCAN_WAVES_PER_SIMD)) vo
     split = p.n_pref + j / units;
     b = unit / p.n_kv;
     g = unit % p.n_kv;
-  } else {   // the odd last request's prefix splits
+  } else {   // the prefix splits of the requests past the last whole pack
     const int j = id - n_packed - n_rest;
-    split = j / p.n_kv;
+    split = j / (left * p.n_kv);
+    b = p.packs * p.pack + (j / p.n_kv) % left;
     g = j % p.n_kv;
-    b = p.B - 1;
   }
   const int per_wave = (p.pps + 3) / 4;   // at most 64
   const int ws0 = split * p.pps + wave * per_wave;   // the wave's first page, before the history length clips it
@@ -1584,8 +1606,8 @@ __global__ __launch_bounds__(kBlock) void merge_plain_kernel(Bf16Dev p) {
 template <int D, int G>
 void launch_main(const DecodeDev& dv, hipStream_t stream) {
   const long units = (long)dv.B * dv.n_kv;
-  const long blocks = (long)dv.n_pref * dv.pairs * dv.n_kv + (long)(dv.splits - dv.n_pref) * units +
-                      (long)dv.n_pref * (dv.B & 1) * dv.n_kv + units * dv.bf_blocks;
+  const long blocks = (long)dv.n_pref * dv.packs * dv.n_kv + (long)(dv.splits - dv.n_pref) * units +
+                      (long)dv.n_pref * (dv.B - dv.packs * dv.pack) * dv.n_kv + units * dv.bf_blocks;
   if (blocks == 0) return;
   const dim3 grid((unsigned)blocks);
   if constexpr (D == 128) {
@@ -1593,6 +1615,15 @@ void launch_main(const DecodeDev& dv, hipStream_t stream) {
       if (dv.lm) decode_main_kernel<D, G, true, 2><<<grid, kBlock, 0, stream>>>(dv);
       else decode_main_kernel<D, G, false, 2><<<grid, kBlock, 0, stream>>>(dv);
       return;
+    }
+    if constexpr (G == 4) {
+      // four-request packs (uniform codebook, whole-head groups): the whole launch runs at the
+      // 16-head waves' two waves per SIMD (their own launch, leaving three per SIMD to the other
+      // blocks, measured 199 against 167 us per step on the 28-request layer)
+      if (!dv.lm && dv.n_pref > 0 && dv.pack == 4) {
+        decode_main_kernel<D, 4, false, 1, 4><<<grid, kBlock, 0, stream>>>(dv);
+        return;
+      }
     }
   }
   if (dv.lm) decode_main_kernel<D, G, true, 1><<<grid, kBlock, 0, stream>>>(dv);
@@ -1638,9 +1669,14 @@ DecodeDev make_dev(const oscar_decode_args& a, const DecodePlan& plan, char* ws)
   dv.bf_blocks = plan.chunks;
   dv.lm = a.codebook == OSCAR_CODEBOOK_LLOYD_MAX ? 1 : 0;
   dv.ng = (a.group_channels == 64 && a.head_dim == 128) ? 2 : 1;
-  // pack the splits that lie wholly inside a shared prefix (group size 4, two or more requests)
-  dv.pairs = a.batch / 2;
-  dv.n_pref = (dv.G == 4 && dv.pairs > 0 && plan.splits > 0) ? std::min(plan.splits, a.shared_pages / plan.pages_per_split)
+  // pack the splits that lie wholly inside a shared prefix (group size 4, two or
+  // more requests): four requests per wave with the uniform codebook and
+  // whole-head groups at d = 128 (the 16-head wave fits two per SIMD there),
+  // else two
+  const bool quad = a.batch >= 4 && dv.lm == 0 && dv.ng == 1 && a.head_dim == 128;
+  dv.pack = quad ? 4 : 2;
+  dv.packs = a.batch / dv.pack;
+  dv.n_pref = (dv.G == 4 && dv.packs > 0 && plan.splits > 0) ? std::min(plan.splits, a.shared_pages / plan.pages_per_split)
                                                             : 0;
   dv.sm_log2 = a.sm_scale * kLog2e;
   dv.n_pages = a.n_pages;

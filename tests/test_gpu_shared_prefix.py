@@ -1,9 +1,11 @@
 """Shared-prefix packing of the history scan (group size 4): the splits that
-lie inside a declared shared prefix are read once for each request pair.
-Parity with the oracle on ragged private parts, an odd last request and two
-split partitions; the pair checks (rows that differ inside the prefix, a
-history shorter than the prefix) that turn exactly that pair's rows into NaN;
-and group sizes that ignore the declaration."""
+lie inside a declared shared prefix are read once for each pack of requests,
+four per wave (uniform codebook, whole-head groups, d = 128, batches of four
+or more) or two per wave (otherwise).  Parity with the oracle on ragged
+private parts, requests past the last whole pack and two split partitions;
+the pack checks (rows that differ inside the prefix, a history shorter than
+the prefix) that turn exactly that pack's rows into NaN; and group sizes that
+ignore the declaration."""
 import numpy as np
 import pytest
 
@@ -85,3 +87,47 @@ def test_other_group_sizes_ignore_the_prefix(G):
     base = gpu_decode(cfg, pools)
     compare_out(base, oracle.decode_attn_ref(cfg, *pools), what=f"G={G}")
     assert np.array_equal(gpu_decode(cfg, pools, shared_pages=13), base)
+
+
+@pytest.mark.parametrize("B", [4, 6, 8, 11])
+def test_prefix_quads_match_oracle(B):
+    """Four requests per wave: whole packs, and one to three requests past the
+    last whole pack read on their own."""
+    cfg, pools = prefix_cache(20 + B, B, 4, 128, hist_pages=21, shared=13)
+    ref = oracle.decode_attn_ref(cfg, *pools)
+    compare_out(gpu_decode(cfg, pools, shared_pages=13), ref, what=f"prefix quads B={B}")
+
+
+@pytest.mark.parametrize("codebook,groups", [("lloyd_max", 0), ("uniform", 64)])
+def test_prefix_pairs_for_other_formats(codebook, groups):
+    """The Lloyd-Max codebook and 64-channel groups pack two requests per wave
+    even in batches of four or more."""
+    from gpu_util import oracle_pools as pools_of
+    ctx = 64 + 256 + 64 * 21
+    shape = synth.DecodeShape("prefix-fmt-b5", 5, 8, 2, 128, ctx, shared_hist_pages=13)
+    cfg = synth.make_decode_config(0, shape=shape, seed_index=60 + groups)
+    cfg["codebook"] = codebook
+    cfg["group_channels"] = groups
+    pools = pools_of(cfg)
+    ref = oracle.decode_attn_ref(cfg, *pools)
+    compare_out(gpu_decode(cfg, pools, shared_pages=13), ref, what=f"prefix {codebook} groups {groups}")
+
+
+def test_mismatched_rows_poison_the_quad():
+    cfg, pools = prefix_cache(30, 6, 4, 128, hist_pages=21, shared=13)
+    ref = oracle.decode_attn_ref(cfg, *pools)
+    table = cfg["block_table"].copy()
+    table[2, 7] = table[2, 16]                   # request 2 leaves the prefix at page 7
+    got = gpu_decode(cfg, pools, block_table=table, shared_pages=13)
+    assert np.all(np.isnan(got[:4]))
+    compare_out(got[4:], ref[4:], what="requests outside the quad")
+
+
+def test_short_history_poisons_the_quad():
+    cfg, pools = prefix_cache(31, 5, 4, 128, hist_pages=21, shared=13)
+    ref = oracle.decode_attn_ref(cfg, *pools)
+    hl = cfg["hist_len"].copy()
+    hl[3] = 64 * 13 - 9                          # ends inside the declared prefix
+    got = gpu_decode(cfg, pools, hist_len=hl, shared_pages=13)
+    assert np.all(np.isnan(got[:4]))
+    compare_out(got[4:], ref[4:], what="request outside the quad")
