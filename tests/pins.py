@@ -175,6 +175,30 @@ def check_column_permutation_invariance(seed: int = 5):
     assert np.array_equal(c1[:, perm], c2)
 
 
+def check_grouped_quantize_pack(seed: int = 14):
+    """32-channel groups: each group of a token is the whole-row quantiser
+    applied to its 32 channels, and its (scale, zero) lands at group j,
+    offset o of the group-planar pool: pair j*64 + o (hand layout)."""
+    rng = np.random.default_rng(seed)
+    d, nkv, n_pages, grp = 128, 2, 2, 32
+    rot = np.stack([random_orthogonal(d, rng) for _ in range(nkv)])
+    x = synth.f32_to_bf16_bits(rng.standard_normal((5, nkv, d)).astype(np.float32) * np.linspace(0.3, 3, d))
+    kc = np.zeros((n_pages, nkv, PAGE * d // 4), np.uint8)
+    ks = np.zeros((n_pages, nkv, PAGE * d // grp, 2), np.uint16)
+    slots = np.array([70, 3, 127, 64, 9], np.int32)
+    oracle.quantize_pack_ref("v", x, rot, 2.0, slots, kc, ks, group=grp)
+    for r, s in enumerate(slots):
+        p, o = divmod(int(s), PAGE)
+        for g in range(nkv):
+            y = oracle.rotate_round_f32(x[r, g][None], rot[g])[0]
+            for j in range(d // grp):
+                c, sc, ze, _ = oracle.quantize_group(np.ascontiguousarray(y[None, grp * j:grp * (j + 1)]), 2.0)
+                assert ks[p, g, j * PAGE + o, 0] == sc[0] and ks[p, g, j * PAGE + o, 1] == ze[0]
+                row = oracle.pack_codes_row(c[0])
+                for i in range(grp // 4):   # V byte of channels 4(8j+i).. at (8j+i)*64 + o
+                    assert kc[p, g, (grp // 4 * j + i) * PAGE + o] == row[i]
+
+
 def check_quantize_pack_slots(seed: int = 6):
     """Scatter into (page, offset) = divmod(slot, 64); skip slots and source
     rows outside the pools; bytes land where the layout literals say."""

@@ -40,7 +40,7 @@ def _some_pin_fails(checks):
 
 QUANT_PINS = [pins.check_quant_closed_forms, pins.check_quant_bruteforce, pins.check_pack_literals,
               pins.check_layout_literals, pins.check_column_permutation_invariance,
-              pins.check_quantize_pack_slots]
+              pins.check_quantize_pack_slots, pins.check_grouped_quantize_pack]
 DECODE_PINS = [pins.check_decode_vs_sdpa, pins.check_inverse_rotation_direction,
                pins.check_rotated_space_identity, pins.check_decode_special_cases,
                pins.check_decode_invariances, pins.check_partition_merge, pins.check_bf16_paged_vs_sdpa,
@@ -53,6 +53,9 @@ MUTANTS = [
     (oq, "quantize_group", "np.rint(t)", "np.floor(t)", QUANT_PINS),
     (oq, "quantize_group", "yc = np.minimum(np.maximum(y, -tau), tau)", "yc = y", QUANT_PINS),
     (oq, "quantize_group", "zero16 = mn.astype(np.float16)", "zero16 = (mn * 0).astype(np.float16)", QUANT_PINS),
+    (oq, "quantize_rows_grouped", ".reshape(n * ng, group)", ".reshape(group, n * ng).T", QUANT_PINS),
+    (oq, "quantize_pack_ref", "sz_pool[page, g, j * PAGE + off, 0]", "sz_pool[page, g, off * ng + j, 0]",
+     QUANT_PINS),
     (oq, "pack_codes_row", "(c[..., 1::4] << 2)", "(c[..., 1::4] << 4)", QUANT_PINS),
     (oq, "k_byte_offsets", "(i // w) * (PAGE * w) + o * w + (i % w)", "o * (d // 4) + i", QUANT_PINS),
     (oq, "v_byte_offsets", "i * PAGE + o", "o * (d // 4) + i", QUANT_PINS),
