@@ -51,8 +51,8 @@ def parse():
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas (0: enough for >= 1 GiB)")
     ap.add_argument("--codebook", default="uniform", choices=("uniform", "lloyd-max"),
                     help="INT2 codebook the history is demoted with and read by (oscar.h)")
-    ap.add_argument("--groups", type=int, default=0, choices=(0, 64),
-                    help="channels per (scale, zero) group: 0 = the whole head, 64 = 64-channel groups")
+    ap.add_argument("--groups", type=int, default=0, choices=(0, 64, 32),
+                    help="channels per (scale, zero) group: 0 = the whole head, 64 or 32 = sub-head groups")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
@@ -194,8 +194,8 @@ def decode_workload(name, args, K, warmup, with_bf16, tm):
     cfg_index = WORKLOADS[name]
     lm = args.codebook == "lloyd-max"
     cb_flag = hip.CODEBOOK_LLOYD_MAX if lm else hip.CODEBOOK_UNIFORM
-    grouped = args.groups == 64
-    q_flags = cb_flag | (hip.GROUPS_64 if grouped else 0)
+    grouped = args.groups > 0
+    q_flags = cb_flag | {0: 0, 64: hip.GROUPS_64, 32: hip.GROUPS_32}[args.groups]
     shape = synth.DECODE_SHAPES[cfg_index]
     t0 = time.time()
     cfg = ensure_free_slot(synth.make_decode_config(cfg_index))
@@ -225,7 +225,7 @@ def decode_workload(name, args, K, warmup, with_bf16, tm):
     # algorithmic bytes: every history token of a physical page once (a page
     # shared by several requests' tables needs reading only once), the BF16
     # windows and the block-table entries
-    ng = d // 64 if grouped else 1   # (scale, zero) pairs per token and head
+    ng = hip.groups_per_head(d, args.groups)   # (scale, zero) pairs per token and head
     hist_bytes = unique_tokens(cfg["block_table"], cfg["hist_len"]) * n_kv * (2 * d // 4 + 2 * 4 * ng)
     win_bytes = int((cfg["sink_len"] + cfg["recent_len"]).sum()) * n_kv * 4 * d
     table_bytes = int(sum(-(-int(h) // 64) for h in cfg["hist_len"])) * 4
@@ -325,7 +325,7 @@ def decode_workload(name, args, K, warmup, with_bf16, tm):
                    "step": "oscar_decode_step: demote K,V of 1 token/request + decode attention"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(name + ("-lloyd-max" if lm else "") + ("-groups64" if grouped else "")),
+                     "traffic": measured_traffic(name + ("-lloyd-max" if lm else "") + (f"-groups{args.groups}" if grouped else "")),
                      "kernel": "decode_main_kernel (oscar_decode_scan)", "kernel_us": scan_us,
                      "bytes_per_launch": scan_bytes},
         "kv_tokens_per_s": float(cfg["hist_len"].sum() + cfg["sink_len"].sum() + cfg["recent_len"].sum())

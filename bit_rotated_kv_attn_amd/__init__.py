@@ -23,8 +23,8 @@ PAGE = 64
 KIND_K, KIND_V = 0, 1
 # INT2 codebooks (oscar.h); the Lloyd-Max flag is OR'ed into a demotion's kind
 CODEBOOK_UNIFORM, CODEBOOK_LLOYD_MAX = 0, 0x100
-# 64-channel quantisation groups (oscar.h); OR'ed into a demotion's kind
-GROUPS_64 = 0x200
+# 64- and 32-channel quantisation groups (oscar.h); at most one is OR'ed into a demotion's kind
+GROUPS_64, GROUPS_32 = 0x200, 0x400
 # arithmetic the kernels of this build compute in (reported by bench.py)
 COMPUTE_DTYPE = ("QK i8 MFMA (exact integer digits), PV f16 MFMA (fp16 weight pairs) + f32 sums and softmax; "
                  "bf16x3 MFMA rotation with certified decisions and fp64 exact recomputes in demotion")
@@ -34,7 +34,7 @@ OSCAR_OK, OSCAR_EINVAL, OSCAR_EUNSUPPORTED, OSCAR_EWORKSPACE, OSCAR_EHIP, OSCAR_
 # bytes of the static per-GPU scratch buffer of oscar_decode_step_static (oscar.h)
 STATIC_SCRATCH_BYTES = 32 << 20
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liboscar.so")
-ABI_VERSION = 3   # OSCAR_ABI_VERSION of the oscar.h these mirrors follow
+ABI_VERSION = 4   # OSCAR_ABI_VERSION of the oscar.h these mirrors follow
 
 _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 
@@ -139,16 +139,27 @@ def _ptr(t, itemsize=None, name="tensor"):
     return t.data_ptr()
 
 
+def groups_per_head(head_dim: int, group_channels: int) -> int:
+    """(scale, zero) groups per (token, head): 1 for whole-head groups
+    (group_channels 0, or at least head_dim), else head_dim / group_channels."""
+    return 1 if group_channels <= 0 or group_channels >= head_dim else head_dim // group_channels
+
+
+def kind_group_channels(kind: int) -> int:
+    """The group size a demotion kind's flags select (0: the whole head)."""
+    return 64 if int(kind) & GROUPS_64 else 32 if int(kind) & GROUPS_32 else 0
+
+
 def oscar_quantize_pack(kind: int, x, rot, clip: float, dst_slot, codes, scale_zero, *, src_idx=None,
                         n_src=None, x_tok_stride=None, x_head_stride=None, stream=None) -> None:
     """Demote tokens of one tensor into INT2 pages (see oscar_quantize_pack in oscar.h).
 
-    kind: KIND_K or KIND_V, optionally | CODEBOOK_LLOYD_MAX and / or | GROUPS_64.
+    kind: KIND_K or KIND_V, optionally | CODEBOOK_LLOYD_MAX and / or | GROUPS_64 or GROUPS_32.
 
     x: bf16 bits; by default a contiguous [n_src][n_kv][d] tensor.  For other
     layouts pass n_src, x_tok_stride and x_head_stride (elements).
     rot fp32 [n_kv][d][d]; dst_slot int32 [n_tok]; codes uint8 [n_pages][n_kv][64*d/4];
-    scale_zero 16-bit [n_pages][n_kv][64][2]; src_idx int32 [n_tok] or None."""
+    scale_zero 16-bit [n_pages][n_kv][64*ng][2] (ng groups per head); src_idx int32 [n_tok] or None."""
     n_kv, d = rot.shape[0], rot.shape[-1]
     if x_tok_stride is None:
         if x.dim() != 3 or x.shape[1:] != (n_kv, d):
@@ -157,7 +168,7 @@ def oscar_quantize_pack(kind: int, x, rot, clip: float, dst_slot, codes, scale_z
     n_tok = dst_slot.numel()
     if src_idx is not None and src_idx.numel() != n_tok:
         raise ValueError("src_idx and dst_slot lengths differ")
-    ng = d // 64 if int(kind) & GROUPS_64 else 1
+    ng = groups_per_head(d, kind_group_channels(kind))
     if codes.shape[1:] != (n_kv, PAGE * d // 4) or scale_zero.shape[1:] != (n_kv, PAGE * ng, 2):
         raise ValueError("pool shapes do not match [n_pages][n_kv][...]")
     if dst_slot.dtype.itemsize != 4 or (src_idx is not None and src_idx.dtype.itemsize != 4):
@@ -189,7 +200,7 @@ def decode_args(*, q, sink_k, sink_v, recent_k, recent_v, sink_len, recent_len, 
     None for oscar_decode_step_static, which brings its own);
     shared_pages: leading history pages every request holds at the same ids (0: none);
     codebook: CODEBOOK_UNIFORM or CODEBOOK_LLOYD_MAX, as the pools were demoted;
-    group_channels: 0 (whole-head groups) or 64, as the pools were demoted.
+    group_channels: 0 (whole-head groups), 64 or 32, as the pools were demoted.
     The returned DecodeArgs holds a reference to every tensor it points to
     (``keep``), so tensors made inline stay allocated while the args live; a
     captured graph that replays the call must keep the args alive too."""
@@ -197,7 +208,7 @@ def decode_args(*, q, sink_k, sink_v, recent_k, recent_v, sink_len, recent_len, 
     n_kv = sink_k.shape[1]
     if tuple(out.shape) != (B, Hq, d):
         raise ValueError("out must be [B][Hq][d] fp32")
-    pairs = PAGE * (d // 64 if group_channels == 64 else 1)   # (scale, zero) pairs per (page, head)
+    pairs = PAGE * groups_per_head(d, group_channels)   # (scale, zero) pairs per (page, head)
     for name, sz in (("k_sz", k_sz), ("v_sz", v_sz)):
         if sz.dim() != 4 or sz.shape[2:] != (pairs, 2):
             raise ValueError(f"{name} must be [n_pages][n_kv][{pairs}][2] for group_channels={group_channels}")
@@ -261,8 +272,8 @@ def demote_args(*, x, rot, clip: float, dst_slot, codes, scale_zero, src_idx=Non
     if src_idx is not None and src_idx.numel() != n_tok:
         raise ValueError("src_idx and dst_slot lengths differ")
     # the step decides the groups (its args' group_channels); oscar_decode_step checks this pool against them
-    if codes.shape[1:] != (n_kv, PAGE * d // 4) or scale_zero.shape[1:] not in ((n_kv, PAGE, 2),
-                                                                               (n_kv, PAGE * max(1, d // 64), 2)):
+    if codes.shape[1:] != (n_kv, PAGE * d // 4) or scale_zero.shape[1:] not in (
+            (n_kv, PAGE * groups_per_head(d, gc), 2) for gc in (0, 64, 32)):
         raise ValueError("pool shapes do not match [n_pages][n_kv][...]")
     if dst_slot.dtype.itemsize != 4 or (src_idx is not None and src_idx.dtype.itemsize != 4):
         raise ValueError("dst_slot / src_idx must be int32")
@@ -281,7 +292,7 @@ def oscar_decode_step(*, args, demote_k=None, demote_v=None, stream=None) -> Non
     (:func:`demote_args` results, or None) run in the decode's last launch.
     ``args`` is a :func:`decode_args` tuple."""
     a, ws, nbytes = args
-    pairs = PAGE * (a.head_dim // 64 if a.group_channels == 64 else 1)
+    pairs = PAGE * groups_per_head(a.head_dim, a.group_channels)
     for name, dm in (("demote_k", demote_k), ("demote_v", demote_v)):
         if dm is not None and getattr(dm, "sz_pairs", pairs) != pairs:
             raise ValueError(f"{name}: its scale/zero pool holds {dm.sz_pairs} pairs per (page, head); "
@@ -300,7 +311,7 @@ def oscar_decode_step_static(*, args, demote_k=None, demote_v=None, stream=None)
     when the sizes need more than STATIC_SCRATCH_BYTES.  Calls that can
     overlap on one GPU race on the shared buffer."""
     a = args[0]
-    pairs = PAGE * (a.head_dim // 64 if a.group_channels == 64 else 1)
+    pairs = PAGE * groups_per_head(a.head_dim, a.group_channels)
     for name, dm in (("demote_k", demote_k), ("demote_v", demote_v)):
         if dm is not None and getattr(dm, "sz_pairs", pairs) != pairs:
             raise ValueError(f"{name}: its scale/zero pool holds {dm.sz_pairs} pairs per (page, head); "

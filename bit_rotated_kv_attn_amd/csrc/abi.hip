@@ -53,8 +53,9 @@ oscar_status oscar_quantize_pack(int32_t kind, const uint16_t* x, int64_t n_src,
                                  int32_t n_kv, int32_t head_dim, const float* rot, float clip,
                                  const int32_t* dst_slot, uint8_t* codes, uint16_t* scale_zero,
                                  int64_t n_pages, hipStream_t stream) {
-  const int32_t layout = kind & ~(OSCAR_CODEBOOK_LLOYD_MAX | OSCAR_GROUPS_64);
+  const int32_t layout = kind & ~(OSCAR_CODEBOOK_LLOYD_MAX | kGroupFlags);
   if (layout != OSCAR_KIND_K && layout != OSCAR_KIND_V) return OSCAR_EINVAL;
+  if ((kind & kGroupFlags) == kGroupFlags) return OSCAR_EINVAL;
   if (n_tok < 0 || n_src < 0 || n_pages < 0 || n_kv < 1 || n_kv > 65535) return OSCAR_EINVAL;
   if (!supported_dim(head_dim)) return OSCAR_EUNSUPPORTED;
   if (!std::isfinite(clip) || !(clip > 0.0f) || clip > 65504.0f) return OSCAR_EINVAL;
@@ -92,7 +93,7 @@ oscar_status check_decode(const oscar_decode_args* a, void* workspace, size_t wo
   if (a->shared_pages < 0 || (int64_t)a->shared_pages * OSCAR_PAGE_TOKENS > a->max_hist_len)
     return OSCAR_EINVAL;
   if (a->codebook != OSCAR_CODEBOOK_UNIFORM && a->codebook != OSCAR_CODEBOOK_LLOYD_MAX) return OSCAR_EINVAL;
-  if (a->group_channels != 0 && a->group_channels != 64) return OSCAR_EINVAL;
+  if (a->group_channels != 0 && a->group_channels != 64 && a->group_channels != 32) return OSCAR_EINVAL;
   *plan = make_decode_plan(a->batch, a->n_q_heads, a->n_kv_heads, a->head_dim, a->max_hist_len,
                            a->sink_cap, a->recent_cap);
   if (a->batch == 0) return OSCAR_OK;

@@ -148,6 +148,16 @@ constexpr int kMaxPagesPerSplit = 4 * 64;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// (scale, zero) groups per head of a demotion kind's group flag (oscar.h)
+constexpr int kGroupFlags = OSCAR_GROUPS_64 | OSCAR_GROUPS_32;
+__host__ __device__ constexpr int kind_groups(int kind, int d) {
+  return (kind & OSCAR_GROUPS_32) ? d / 32 : (kind & OSCAR_GROUPS_64) ? d / 64 : 1;
+}
+// the in-page code layout of a kind: K planes or V byte columns
+__host__ __device__ constexpr bool kind_is_k(int kind) {
+  return (kind & ~(OSCAR_CODEBOOK_LLOYD_MAX | kGroupFlags)) == OSCAR_KIND_K;
+}
+
 // One head's partial softmax state in the workspace: (m, l, two pad floats,
 // acc[d]).  The pad puts acc on a 16-byte boundary for vector loads.
 constexpr int kPartAcc = 4;
@@ -176,7 +186,7 @@ inline DecodePlan make_decode_plan(int B, int Hq, int n_kv, int d, int max_hist_
   size_t off = 0;
   p.off_qdig = off;  off = align256(off + (size_t)B * n_kv * NB * (d / 64) * 64 * 16);
   p.off_qa = off;    off = align256(off + (size_t)B * Hq * sizeof(float));
-  p.off_qb = off;    off = align256(off + (size_t)B * Hq * 2 * sizeof(float));   // per (scale, zero) group
+  p.off_qb = off;    off = align256(off + (size_t)B * Hq * 4 * sizeof(float));   // per quarter of the head
   p.off_hpart = off; off = align256(off + (size_t)B * n_kv * p.splits * part);
   p.off_bpart = off; off = align256(off + (size_t)B * n_kv * p.chunks * part);
   p.total = off;

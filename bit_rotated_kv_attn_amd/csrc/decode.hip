@@ -70,7 +70,7 @@ struct DecodeDev {
   // last whole pack read them on their own
   int n_pref, packs, pack;
   int lm;   // the pools hold Lloyd-Max codes (oscar.h OSCAR_CODEBOOK_LLOYD_MAX)
-  int ng;   // (scale, zero) groups per head: 1, or 2 with 64-channel groups at d = 128
+  int ng;   // (scale, zero) groups per head: 1, 2 (64-channel groups at d = 128, 32 at d = 64) or 4
   float sm_log2;
   int64_t n_pages;
   const uint16_t *q, *sink_k, *sink_v, *recent_k, *recent_v;
@@ -541,8 +541,21 @@ template <int D, int G>
 struct HistOperands {
   static constexpr int NB = (G + 3) / 4, NCH = D / 64;
   v4i qa[NB][NCH];
-  float ca[NB], cb[NB][2];   // cb per (scale, zero) group (the second is 0 with one group)
+  float ca[NB], cb[NB][4];   // cb per (scale, zero) group (the first p.ng are used)
 };
+
+// The zero-point constants of one head: sm_log2 times the sum of q_rot over
+// each group's channels, from the four quarter sums.
+__device__ __forceinline__ void group_sums(const float* qb4, int ng, float sm_log2, float (&cb)[4]) {
+  const float q0 = qb4[0], q1 = qb4[1], q2 = qb4[2], q3 = qb4[3];
+  if (ng == 4) {
+    cb[0] = sm_log2 * q0; cb[1] = sm_log2 * q1; cb[2] = sm_log2 * q2; cb[3] = sm_log2 * q3;
+  } else if (ng == 2) {
+    cb[0] = sm_log2 * (q0 + q1); cb[1] = sm_log2 * (q2 + q3); cb[2] = 0.0f; cb[3] = 0.0f;
+  } else {
+    cb[0] = sm_log2 * ((q0 + q1) + (q2 + q3)); cb[1] = 0.0f; cb[2] = 0.0f; cb[3] = 0.0f;
+  }
+}
 
 template <int D, int G>
 __device__ __forceinline__ void load_hist_operands(const DecodeDev& p, int b, int g, int lane, HistOperands<D, G>& o) {
@@ -553,12 +566,7 @@ __device__ __forceinline__ void load_hist_operands(const DecodeDev& p, int b, in
   for (int nb = 0; nb < NB; ++nb) {
     const int hout = 4 * nb + grp;        // head whose results this lane holds
     o.ca[nb] = hout < G ? p.qa[h_base + hout] : 0.0f;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) o.cb[nb][j] = hout < G ? p.qb[2 * (h_base + hout) + j] : 0.0f;
-    if (p.ng == 1) {   // one group: the sum over both halves of the head
-      o.cb[nb][0] += o.cb[nb][1];
-      o.cb[nb][1] = 0.0f;
-    }
+    group_sums(p.qb + 4 * (size_t)(h_base + (hout < G ? hout : 0)), p.ng, p.sm_log2, o.cb[nb]);
     const bool row_ok = 4 * nb + (n >> 2) < G;   // head of the A row this lane supplies
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -580,12 +588,7 @@ __device__ __forceinline__ void load_pack_operands(const DecodeDev& p, int b, in
   for (int nb = 0; nb < PACK; ++nb) {
     const int unit = (b + nb) * p.n_kv + g;
     o.ca[nb] = p.qa[(size_t)(b + nb) * p.Hq + g * 4 + grp];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) o.cb[nb][j] = p.qb[2 * ((size_t)(b + nb) * p.Hq + g * 4 + grp) + j];
-    if (p.ng == 1) {
-      o.cb[nb][0] += o.cb[nb][1];
-      o.cb[nb][1] = 0.0f;
-    }
+    group_sums(p.qb + 4 * ((size_t)(b + nb) * p.Hq + g * 4 + grp), p.ng, p.sm_log2, o.cb[nb]);
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
       o.qa[nb][c] = reinterpret_cast<const v4i*>(p.qdig)[((size_t)unit * NCH + c) * kWave + lane];
@@ -600,6 +603,16 @@ __device__ __forceinline__ void load_pack_operands(const DecodeDev& p, int b, in
 template <bool kHiBit>
 __device__ __forceinline__ half8 pv_operand(uint32_t w0, uint32_t s0, uint32_t w1, uint32_t s1, int f) {
   const uint32_t m = (kHiBit ? 0x00020002u : 0x00030003u) << (2 * f);
+  const u32x4 x = {w0 & m, s0 & m, w1 & m, s1 & m};
+  return __builtin_bit_cast(half8, x);
+}
+
+// pv_operand restricted to the lanes whose mask lm is all ones (a column
+// half of the product: the 32-channel groups of one 64-channel chunk)
+template <bool kHiBit>
+__device__ __forceinline__ half8 pv_operand_cols(uint32_t w0, uint32_t s0, uint32_t w1, uint32_t s1, int f,
+                                                 uint32_t lm) {
+  const uint32_t m = ((kHiBit ? 0x00020002u : 0x00030003u) << (2 * f)) & lm;
   const u32x4 x = {w0 & m, s0 & m, w1 & m, s1 & m};
   return __builtin_bit_cast(half8, x);
 }
@@ -622,14 +635,19 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
   using RG = Ring<D, NB, NG>;
   constexpr int PB = RG::PB;
   constexpr int NS = RG::kStages;
+  constexpr int GC = D / NG;    // channels per (scale, zero) group
+  static_assert(NG == 1 || NG == 2 || (NG == 4 && D == 128), "groups of the head, 64 or 32 channels");
   const int n = lane & 15, grp = lane >> 4;
   const auto& qa = qo.qa;
   const auto& ca = qo.ca;
   const auto& cb = qo.cb;
-  // With two (scale, zero) groups the QK dot is also needed over channels
-  // 0..63 alone: K operand block grp holds channels 32grp..32grp+31 of both
-  // chunks, so group 0's q operand keeps blocks 0 and 1 and zeroes 2 and 3.
-  // Group 1's dot is the full one minus group 0's (exact in int32).
+  // With (scale, zero) groups the QK dot is needed per group.  Operand block
+  // grp (lanes 16grp .. 16grp + 15) of every chunk holds K plane grp, i.e.
+  // channels grp*D/4 .. grp*D/4 + D/4 - 1, so a group is one block (32-channel
+  // groups at d = 128) or two.  Two groups: group 0's q operand keeps blocks 0
+  // and 1 and zeroes 2 and 3.  Four groups: the K operand of group j < 3
+  // keeps block j only.  The last group's dot is the full one minus the
+  // others (exact in int32).
   v4i qa0[NB][NCH];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
@@ -759,7 +777,7 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
       const bool hok = 4 * nb + grp < G;
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        v4i dq, dq0;
+        v4i dq, dq0, dqg[3];
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
           const uint32_t w = kword[tb * NCH + c];
@@ -768,6 +786,13 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
           dq = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[nb][c], bop, c == 0 ? v4i{0, 0, 0, 0} : dq, 0, 0, 0);
           if constexpr (NG == 2)
             dq0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa0[nb][c], bop, c == 0 ? v4i{0, 0, 0, 0} : dq0, 0, 0, 0);
+          if constexpr (NG == 4) {
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+              const v4i bj = grp == j ? bop : v4i{0, 0, 0, 0};
+              dqg[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[nb][c], bj, c == 0 ? v4i{0, 0, 0, 0} : dqg[j], 0, 0, 0);
+            }
+          }
         }
         // digits: d0 + 2^8 d1 and d2 + 2^8 d3 are exact in int32
         auto dot_of = [](v4i v) {
@@ -779,9 +804,24 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
           const float off = hok ? fmaf(zk[0][tb], cb[nb][0], -mref[nb]) : -INFINITY;
           lg[nb][tb] = fmaf(sk[0][tb] * ca[nb], dot_of(dq), off);
         } else {
-          const v4i dq1 = dq - dq0;
-          const float off = hok ? fmaf(zk[0][tb], cb[nb][0], fmaf(zk[1][tb], cb[nb][1], -mref[nb])) : -INFINITY;
-          lg[nb][tb] = fmaf(sk[0][tb] * ca[nb], dot_of(dq0), fmaf(sk[1][tb] * ca[nb], dot_of(dq1), off));
+          // per-group digit sums, then the logit from the last group down
+          v4i dg[NG];
+          if constexpr (NG == 2) {
+            dg[0] = dq0;
+            dg[1] = dq - dq0;
+          } else {
+            dg[0] = dqg[0];
+            dg[1] = dqg[1];
+            dg[2] = dqg[2];
+            dg[3] = dq - dqg[0] - dqg[1] - dqg[2];
+          }
+          float off = -mref[nb];
+#pragma unroll
+          for (int j = NG - 1; j >= 0; --j) off = fmaf(zk[j][tb], cb[nb][j], off);
+          float l = hok ? off : -INFINITY;
+#pragma unroll
+          for (int j = NG - 1; j >= 0; --j) l = fmaf(sk[j][tb] * ca[nb], dot_of(dg[j]), l);
+          lg[nb][tb] = l;
         }
       }
     }
@@ -897,7 +937,10 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
     __builtin_amdgcn_wave_barrier();
 
     // ---- PV: lane (n, grp) reads row n, token slots 16grp + 8ks .. + 7 of
-    // each plane; with two groups, chunk c of V is group c
+    // each plane.  Column n of chunk c is channels 64c + 4n .. 64c + 4n + 3,
+    // of group (64c + 4n) / GC: with 64-channel groups chunk c is group c;
+    // with 32-channel groups columns 0..7 are group 2c and 8..15 group 2c + 1,
+    // and each takes its own product with the other half's columns masked.
     half8 wa[PB][NG][2];
 #pragma unroll
     for (int rb = 0; rb < PB; ++rb)
@@ -906,25 +949,45 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
           wa[rb][j][ks] = *reinterpret_cast<const half8*>(pl + (rb * NG + j) * kPlaneBytes + plane_chunk(n, 2 * grp + ks));
+    const uint32_t cols_lo = n < 8 ? 0xffffffffu : 0u;   // column half of this lane
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const uint4 v4 = vpre[c];
       const uint32_t s0 = v4.x >> 8, s1 = v4.y >> 8, s2 = v4.z >> 8, s3 = v4.w >> 8;
-      const int jp = NG == 2 ? c : 0;
+      const int jp = GC >= 64 ? 64 * c / GC : 2 * c;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const uint32_t a0 = ks ? v4.z : v4.x, b0 = ks ? s2 : s0, a1 = ks ? v4.w : v4.y, b1 = ks ? s3 : s1;
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-          const half8 bop = pv_operand<false>(a0, b0, a1, b1, f);
-#pragma unroll
-          for (int rb = 0; rb < PB; ++rb)
-            acc[rb][c][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[rb][jp][ks], bop, acc[rb][c][f], 0, 0, 0);
-          if constexpr (LM) {
-            const half8 bhi = pv_operand<true>(a0, b0, a1, b1, f);
+          if constexpr (GC >= 64) {
+            const half8 bop = pv_operand<false>(a0, b0, a1, b1, f);
 #pragma unroll
             for (int rb = 0; rb < PB; ++rb)
-              acc2[rb][c][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[rb][jp][ks], bhi, acc2[rb][c][f], 0, 0, 0);
+              acc[rb][c][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[rb][jp][ks], bop, acc[rb][c][f], 0, 0, 0);
+            if constexpr (LM) {
+              const half8 bhi = pv_operand<true>(a0, b0, a1, b1, f);
+#pragma unroll
+              for (int rb = 0; rb < PB; ++rb)
+                acc2[rb][c][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[rb][jp][ks], bhi, acc2[rb][c][f], 0, 0, 0);
+            }
+          } else {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const uint32_t cm = h ? ~cols_lo : cols_lo;
+              const half8 bop = pv_operand_cols<false>(a0, b0, a1, b1, f, cm);
+#pragma unroll
+              for (int rb = 0; rb < PB; ++rb)
+                acc[rb][c][f] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[rb][jp + h][ks], bop, acc[rb][c][f], 0, 0, 0);
+              if constexpr (LM) {
+                const half8 bhi = pv_operand_cols<true>(a0, b0, a1, b1, f, cm);
+#pragma unroll
+                for (int rb = 0; rb < PB; ++rb)
+                  acc2[rb][c][f] =
+                      __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[rb][jp + h][ks], bhi, acc2[rb][c][f], 0, 0, 0);
+              }
+            }
           }
         }
       }
@@ -957,7 +1020,10 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
       const int rb = nb >> 1, e = nb & 1;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        const float z = zs[nb][NG == 2 ? c : 0];
+        float z = zs[nb][0];   // the zero-point sum of column n's group
+#pragma unroll
+        for (int j = 1; j < NG; ++j)
+          if ((64 * c + 4 * n) / GC == j) z = zs[nb][j];
         float o[4];
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
@@ -977,8 +1043,10 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
 // ---------------------------------------------------------------------------
 // Two blocks per query head, one per half of the output channels (half = 0
 // or 1): each reads half of R_K, and the digit scale needs no exchange
-// between them (it comes from |q|_2).  qb[2 bh + half] is the sum of q_rot
-// over the half's channels (a 64-channel group when head_dim is 128).
+// between them (it comes from |q|_2).  qb[4 bh + 2 half + e] is the sum of
+// q_rot over channels 32e .. 32e + 31 of the half (none for e = 1 when
+// head_dim is 64): the sums of every 32-channel group, whose pairs give the
+// 64-channel groups and the head.
 template <int D>
 __device__ __forceinline__ void rotate_query_block(const DecodeDev& p, int bh, int half) {
   constexpr int NCH = D / 64, PLANE = D / 16;
@@ -1047,11 +1115,15 @@ __device__ __forceinline__ void rotate_query_block(const DecodeDev& p, int bh, i
       base[lane * 16 + 4 * pp + bb] = (uint8_t)(U >> (8 * dj));
     }
   }
-  // sum of q_rot over the half's channels (tid < DH <= 64: wave 0), after the digit stores
-  const float ws = wave_sum(acc);
+  // sums of q_rot over the half's 32-channel units (tid < DH <= 64: wave 0,
+  // unit e in lanes 32e .. 32e + 31 of the 16-lane row sums), after the digit
+  // stores
+  const float rs = group16_sum(acc);
+  const float s0 = lane_value(rs, 0) + lane_value(rs, 16), s1 = lane_value(rs, 32) + lane_value(rs, 48);
   if (tid == 0) {
     if (half == 0) p.qa[bh] = p.sm_log2 / (16.0f * kq);
-    p.qb[2 * bh + half] = p.sm_log2 * ws;
+    p.qb[4 * bh + 2 * half] = s0;
+    p.qb[4 * bh + 2 * half + 1] = s1;
   }
 }
 
@@ -1070,8 +1142,8 @@ __device__ __forceinline__ void demote_step_block(const DecodeDev& p, int id, co
                                                   const DemoteDev& dv) {
   const int64_t nk = dk.n_tok * p.n_kv;
   const DemoteDev& dm = id < nk ? dk : dv;
-  const int kind = (id < nk ? OSCAR_KIND_K : OSCAR_KIND_V) | (p.lm ? OSCAR_CODEBOOK_LLOYD_MAX : 0) |
-                   (p.ng == 2 ? OSCAR_GROUPS_64 : 0);
+  const int gflag = p.ng == 1 ? 0 : D / p.ng == 64 ? OSCAR_GROUPS_64 : OSCAR_GROUPS_32;
+  const int kind = (id < nk ? OSCAR_KIND_K : OSCAR_KIND_V) | (p.lm ? OSCAR_CODEBOOK_LLOYD_MAX : 0) | gflag;
   if (id >= nk) id -= (int)nk;
   demote_token_block<D>(kind, dm.x, dm.n_src, dm.tok_stride, dm.head_stride, dm.src_idx, id / p.n_kv, id % p.n_kv,
                         p.n_kv, dm.rot, dm.clip, dm.dst_slot, dm.codes, dm.sz, dm.n_pages);
@@ -1085,10 +1157,12 @@ __device__ __forceinline__ void demote_step_block(const DecodeDev& p, int id, co
 #endif
 // Waves per SIMD the scan is compiled for: the 16-head wave (G = 16, or four
 // requests of group size 4 in one wave) fits two per SIMD without spills with
-// the uniform codebook and whole-head groups, and one otherwise.
+// the uniform codebook and whole-head groups, and one otherwise.  Four groups
+// per head take one: their weight planes (8 KB per head block pair) leave
+// room in LDS for one block per compute unit.
 template <int G, bool LM, int NG, int PACK>
 constexpr int scan_waves_per_simd() {
-  return (G > 8 || PACK > 2) && (LM || NG == 2) ? 1 : OSCAR_SCAN_WAVES_PER_SIMD;
+  return NG == 4 || ((G > 8 || PACK > 2) && (LM || NG == 2)) ? 1 : OSCAR_SCAN_WAVES_PER_SIMD;
 }
 
 template <int D, int G, bool LM, int NG, int PACK = 2>
@@ -1610,10 +1684,15 @@ void launch_main(const DecodeDev& dv, hipStream_t stream) {
                       (long)dv.n_pref * (dv.B - dv.packs * dv.pack) * dv.n_kv + units * dv.bf_blocks;
   if (blocks == 0) return;
   const dim3 grid((unsigned)blocks);
+  if (dv.ng == 2) {   // 64-channel groups at d = 128, 32-channel ones at d = 64
+    if (dv.lm) decode_main_kernel<D, G, true, 2><<<grid, kBlock, 0, stream>>>(dv);
+    else decode_main_kernel<D, G, false, 2><<<grid, kBlock, 0, stream>>>(dv);
+    return;
+  }
   if constexpr (D == 128) {
-    if (dv.ng == 2) {   // 64-channel (scale, zero) groups
-      if (dv.lm) decode_main_kernel<D, G, true, 2><<<grid, kBlock, 0, stream>>>(dv);
-      else decode_main_kernel<D, G, false, 2><<<grid, kBlock, 0, stream>>>(dv);
+    if (dv.ng == 4) {   // 32-channel groups
+      if (dv.lm) decode_main_kernel<D, G, true, 4><<<grid, kBlock, 0, stream>>>(dv);
+      else decode_main_kernel<D, G, false, 4><<<grid, kBlock, 0, stream>>>(dv);
       return;
     }
     if constexpr (G == 4) {
@@ -1668,7 +1747,7 @@ DecodeDev make_dev(const oscar_decode_args& a, const DecodePlan& plan, char* ws)
   dv.chunks = plan.chunks; dv.sink_chunks = plan.sink_chunks;
   dv.bf_blocks = plan.chunks;
   dv.lm = a.codebook == OSCAR_CODEBOOK_LLOYD_MAX ? 1 : 0;
-  dv.ng = (a.group_channels == 64 && a.head_dim == 128) ? 2 : 1;
+  dv.ng = a.group_channels > 0 && a.group_channels < a.head_dim ? a.head_dim / a.group_channels : 1;
   // pack the splits that lie wholly inside a shared prefix (group size 4, two or
   // more requests): four requests per wave with the uniform codebook and
   // whole-head groups at d = 128 (the 16-head wave fits two per SIMD there),

@@ -4,9 +4,9 @@
 // an fp64 dot product rounded once to fp32; zero = fp16(min), scale =
 // fp16((max - min) / 3); code = rint((y - zero) / scale) clamped to [0, 3]
 // (or the Lloyd-Max statistics and thresholds of oscar.h when kind carries
-// OSCAR_CODEBOOK_LLOYD_MAX), over the whole head or over each 64-channel group
-// (OSCAR_GROUPS_64; the scale/zero block of a (page, head) is then
-// group-planar).
+// OSCAR_CODEBOOK_LLOYD_MAX), over the whole head or over each 64- or
+// 32-channel group (OSCAR_GROUPS_64, OSCAR_GROUPS_32; the scale/zero block of a
+// (page, head) is then group-planar).
 // Source: the demotion step of the serving pipeline in the myzaker.com article
 // on OSCAR; R and the clip threshold from the gist.science OSCAR technical
 // summary, section 2.2A.
@@ -34,13 +34,14 @@ __device__ __forceinline__ void demote_token_block(int kind, const uint16_t* __r
   __shared__ float xs[D];
   __shared__ double parts[P][D];
   __shared__ float ys[D];
-  __shared__ float red[2][kBlock / kWave];
-  __shared__ double dred[2][kBlock / kWave];
-  __shared__ float gzs[2][D / kWave];   // (zero, scale) of each group
+  constexpr int kUnits = D / 32;         // 32-channel units (half a wave each)
+  __shared__ float red[2][kUnits];
+  __shared__ double dred[2][kUnits];
+  __shared__ float gzs[2][kUnits];      // (zero, scale) of each group
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const bool lm = (kind & OSCAR_CODEBOOK_LLOYD_MAX) != 0;
-  const bool grouped = (kind & OSCAR_GROUPS_64) != 0;   // 64-channel groups
-  const bool k_layout = (kind & ~(OSCAR_CODEBOOK_LLOYD_MAX | OSCAR_GROUPS_64)) == OSCAR_KIND_K;
+  const int ng = kind_groups(kind, D), gu = kUnits / ng;   // groups; units per group
+  const bool k_layout = kind_is_k(kind);
   const int64_t src = src_idx ? (int64_t)src_idx[t] : t;
   const int64_t slot = dst_slot[t];
   if (src < 0 || src >= n_src || slot < 0 || slot >= n_pages * kPage) return;   // block-uniform
@@ -77,41 +78,62 @@ __device__ __forceinline__ void demote_token_block(int kind, const uint16_t* __r
     mn = yc;
     mx = yc;
   }
-  // per-wave (64-channel) extremes; a group is GW consecutive waves
+  // extremes and sums of each 32-channel unit: the 16-lane row results of
+  // rows (0, 1) and (2, 3) of a wave; a group is gu consecutive units.  The
+  // sums of a group add its unit pairs first, as a whole-wave sum would.
+  // Every lane read happens with the whole wave active (outside the
+  // branches that store the results): a lane outside the branch would not
+  // have finished the row reduction the read expects.
+  auto group_sum = [&](const double* u, int j) {
+    if (gu == 1) return u[j];
+    double tot = 0.0;
+    for (int k = j * gu; k < (j + 1) * gu; k += 2) tot += u[k] + u[k + 1];
+    return tot;
+  };
   constexpr int kWaves = D / kWave;
-  const int ng = grouped ? kWaves : 1, gw = kWaves / ng;
-  mn = wave_min(mn);
-  mx = wave_max(mx);
-  if (lane == 0) {
-    red[0][wave] = mn;
-    red[1][wave] = mx;
+  mn = group16_min(mn);
+  mx = group16_max(mx);
+  const float mn0 = fminf(lane_value(mn, 0), lane_value(mn, 16)), mn1 = fminf(lane_value(mn, 32), lane_value(mn, 48));
+  const float mx0 = fmaxf(lane_value(mx, 0), lane_value(mx, 16)), mx1 = fmaxf(lane_value(mx, 32), lane_value(mx, 48));
+  if (wave < kWaves && lane == 0) {
+    red[0][2 * wave] = mn0;
+    red[0][2 * wave + 1] = mn1;
+    red[1][2 * wave] = mx0;
+    red[1][2 * wave + 1] = mx1;
   }
   if (lm) {   // block-uniform: the group means, then the sums of squared deviations, in fp64
-    const double v = wave_sum_f64(tid < D ? (double)ys[tid] : 0.0);
-    if (lane == 0) dred[0][wave] = v;
+    auto row_sum = [](double v) {
+      v += dpp_f64<kDppXor1>(v);
+      v += dpp_f64<kDppXor2>(v);
+      v += dpp_f64<kDppHalfMirror>(v);
+      return v + dpp_f64<kDppMirror>(v);
+    };
+    const double v = row_sum(tid < D ? (double)ys[tid] : 0.0);
+    const double u0 = lane_value_f64(v, 0) + lane_value_f64(v, 16), u1 = lane_value_f64(v, 32) + lane_value_f64(v, 48);
+    if (wave < kWaves && lane == 0) {
+      dred[0][2 * wave] = u0;
+      dred[0][2 * wave + 1] = u1;
+    }
     __syncthreads();
-    double tot = 0.0;
-    const int g0 = (wave < kWaves ? wave / gw : 0) * gw;   // first wave of this thread's group
-    for (int w = g0; w < g0 + gw; ++w) tot += dred[0][w];
-    const double dv = tid < D ? (double)ys[tid] - tot / (D / ng) : 0.0;
-    const double sq = wave_sum_f64(__dmul_rn(dv, dv));
-    if (lane == 0) dred[1][wave] = sq;
+    const int j = tid < D ? (tid / 32) / gu : 0;   // this thread's group
+    const double dv = tid < D ? (double)ys[tid] - group_sum(dred[0], j) / (D / ng) : 0.0;
+    const double w = row_sum(__dmul_rn(dv, dv));
+    const double w0 = lane_value_f64(w, 0) + lane_value_f64(w, 16), w1 = lane_value_f64(w, 32) + lane_value_f64(w, 48);
+    if (wave < kWaves && lane == 0) {
+      dred[1][2 * wave] = w0;
+      dred[1][2 * wave + 1] = w1;
+    }
   }
   __syncthreads();
   if (tid < ng) {   // thread j: (scale, zero) of group j
     float gmn = INFINITY, gmx = -INFINITY;
-    double sum = 0.0, sq = 0.0;
-    for (int w = tid * gw; w < (tid + 1) * gw; ++w) {
-      gmn = fminf(gmn, red[0][w]);
-      gmx = fmaxf(gmx, red[1][w]);
-      if (lm) {
-        sum += dred[0][w];
-        sq += dred[1][w];
-      }
+    for (int k = tid * gu; k < (tid + 1) * gu; ++k) {
+      gmn = fminf(gmn, red[0][k]);
+      gmx = fmaxf(gmx, red[1][k]);
     }
     __half zh = __float2half_rn(gmn);
     __half sh = __float2half_rn(__fdiv_rn(gmx - gmn, 3.0f));
-    if (lm) lm_scale_zero(sum / (D / ng), sq, D / ng, sh, zh);
+    if (lm) lm_scale_zero(group_sum(dred[0], tid) / (D / ng), group_sum(dred[1], tid), D / ng, sh, zh);
     gzs[0][tid] = __half2float(zh);
     gzs[1][tid] = __half2float(sh);
     const int64_t page = slot / kPage;

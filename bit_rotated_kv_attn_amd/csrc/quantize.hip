@@ -53,15 +53,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) 
   float (*ys)[D + 1] = reinterpret_cast<float (*)[D + 1]>(tile);
   __shared__ int64_t src_s[kQTok];
   __shared__ int64_t dst_s[kQTok];       // -1: skip this token
-  constexpr int kPer = D / kWave;        // 64-channel groups per head
-  __shared__ float zf[kQTok][kPer], sf[kQTok][kPer];   // per token and group
+  constexpr int kMaxGroups = D / 32;     // 32-channel groups per head
+  __shared__ float zf[kQTok][kMaxGroups], sf[kQTok][kMaxGroups];   // per token and group
 
   const int g = blockIdx.y;
   const int64_t t0 = (int64_t)blockIdx.x * kQTok;
   const int tid = threadIdx.x;
   const bool lm = (kind & OSCAR_CODEBOOK_LLOYD_MAX) != 0;
-  const int ng = (kind & OSCAR_GROUPS_64) ? kPer : 1;   // 64-channel groups: group k holds channels 64k..
-  const bool k_layout = (kind & ~(OSCAR_CODEBOOK_LLOYD_MAX | OSCAR_GROUPS_64)) == OSCAR_KIND_K;
+  const int ng = kind_groups(kind, D);   // group k holds channels k*D/ng ..
+  const bool k_layout = kind_is_k(kind);
 
   if (tid < kQTok) {
     const int64_t t = t0 + tid;
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) 
   // per-token group statistics: zero = fp16(min), scale = fp16((max - min) / 3),
   // or the Lloyd-Max mean and deviation (fp64).  A 16-lane DPP row handles one
   // token (four tokens per wave at a time); lane c of the row holds channels
-  // c + 16k, so with 64-channel groups elements k of one group are adjacent.
+  // c + 16k, so with 64- or 32-channel groups elements k of one group are adjacent.
   {
     constexpr int KP = D / 16;
     const int lane = tid & (kWave - 1), wave = tid / kWave;
@@ -498,14 +498,16 @@ __device__ __forceinline__ void mfma_token(const v4f_t (&y)[8], const uint4 (&xq
       const int jn = tok_next(cmn, q), jx = tok_next(cmx, q);
       if (jn < 128) {
         const float v = clamp_sym(exact_channel4(xq, rt, jn, q), tau);
-        if (NG == 1 || jn < 64) mn[0] = fminf(mn[0], v);
-        else mn[NG - 1] = fminf(mn[NG - 1], v);
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi)
+          if (jn / (128 / NG) == gi) mn[gi] = fminf(mn[gi], v);
         if (((jn >> 2) & 3) == q) cmn &= ~channel_bit(jn);
       }
       if (jx < 128) {
         const float v = clamp_sym(exact_channel4(xq, rt, jx, q), tau);
-        if (NG == 1 || jx < 64) mx[0] = fmaxf(mx[0], v);
-        else mx[NG - 1] = fmaxf(mx[NG - 1], v);
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi)
+          if (jx / (128 / NG) == gi) mx[gi] = fmaxf(mx[gi], v);
         if (((jx >> 2) & 3) == q) cmx &= ~channel_bit(jx);
       }
     }
@@ -548,8 +550,9 @@ __device__ __forceinline__ void mfma_token(const v4f_t (&y)[8], const uint4 (&xq
     }
     bytes[cb] = (uint32_t)p;
   }
-  bool code_unsure = worst[0] >= thr[0];
-  if (NG == 2) code_unsure = code_unsure || worst[NG - 1] >= thr[NG - 1];
+  bool code_unsure = false;
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) code_unsure = code_unsure || worst[gi] >= thr[gi];
   const int64_t page = slot / kPage;
   const int o = (int)(slot % kPage);
   if (!kExact) {
@@ -573,8 +576,14 @@ __device__ __forceinline__ void mfma_token(const v4f_t (&y)[8], const uint4 (&xq
       if (j < 128) {
         const float v = exact_channel4(xq, rt, j, q);
         if (((j >> 2) & 3) == q) {
-          const int gi = (NG == 2 && j >= 64) ? NG - 1 : 0;
-          const uint32_t c = (uint32_t)ref_code(clamp_sym(v, tau), z[gi], s[gi]);
+          float zj = z[0], sj = s[0];
+#pragma unroll
+          for (int gi = 1; gi < NG; ++gi)
+            if (j / (128 / NG) == gi) {
+              zj = z[gi];
+              sj = s[gi];
+            }
+          const uint32_t c = (uint32_t)ref_code(clamp_sym(v, tau), zj, sj);
           const int cbj = j >> 4, sh2 = 2 * (j & 3);
 #pragma unroll
           for (int cb = 0; cb < 8; ++cb)
@@ -584,9 +593,14 @@ __device__ __forceinline__ void mfma_token(const v4f_t (&y)[8], const uint4 (&xq
       }
     }
   }
-  if (slot >= 0 && q < NG) {
-    const __half s16 = (NG == 2 && q == 1) ? sh[NG - 1] : sh[0];
-    const __half z16 = (NG == 2 && q == 1) ? zh[NG - 1] : zh[0];
+  if (slot >= 0 && q < NG) {   // lane q writes group q
+    __half s16 = sh[0], z16 = zh[0];
+#pragma unroll
+    for (int gi = 1; gi < NG; ++gi)
+      if (q == gi) {
+        s16 = sh[gi];
+        z16 = zh[gi];
+      }
     sz[((page * n_kv + g) * NG + q) * kPage + o] =
         (uint32_t)__half_as_ushort(s16) | ((uint32_t)__half_as_ushort(z16) << 16);
   }
@@ -705,7 +719,7 @@ __global__ __launch_bounds__(kMThreads, 1) void quantize_mfma_kernel(
   const int g = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   const int n = lane & 15, q = lane >> 4;
-  const bool k_layout = (kind & ~OSCAR_GROUPS_64) == OSCAR_KIND_K;
+  const bool k_layout = kind_is_k(kind);
   const int64_t n_tiles = (n_tok + 31) / 32;
   const int64_t tile0 = (int64_t)blockIdx.x * tiles_per_block;
   if (tile0 >= n_tiles) return;   // block-uniform
@@ -804,7 +818,7 @@ __global__ __launch_bounds__(kMThreads, 1) void quantize_exact_kernel(
   const int g = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   const int n = lane & 15, q = lane >> 4;
-  const bool k_layout = (kind & ~OSCAR_GROUPS_64) == OSCAR_KIND_K;
+  const bool k_layout = kind_is_k(kind);
   const int64_t n_tiles = (n_tok + 31) / 32;
   const int64_t tile0 = (int64_t)blockIdx.x * tiles_per_block;
   // block-uniform; with no pages nothing was written (and the clamped scan below reads slot 0)
@@ -942,7 +956,14 @@ hipError_t launch_quantize_pack(int kind, const uint16_t* x, int64_t n_src, int6
     const int64_t per_head = std::max<int64_t>(1, std::min<int64_t>(n_tiles, 256 / n_kv));
     const int64_t tiles = (n_tiles + per_head - 1) / per_head;
     const dim3 fgrid((unsigned)((n_tiles + tiles - 1) / tiles), (unsigned)n_kv);
-    if (kind & OSCAR_GROUPS_64) {
+    if (kind_groups(kind, d) == 4) {
+      quantize_mfma_kernel<4><<<fgrid, kMThreads, 0, stream>>>(kind, x, n_src, tok_stride, head_stride, src_idx,
+                                                              n_tok, n_kv, rot, clip, dst_slot, codes, sz,
+                                                              n_pages, (int)tiles);
+      quantize_exact_kernel<4><<<fgrid, kMThreads, 0, stream>>>(kind, x, n_src, tok_stride, head_stride, src_idx,
+                                                               n_tok, n_kv, rot, clip, dst_slot, codes, sz,
+                                                               n_pages, (int)tiles);
+    } else if (kind_groups(kind, d) == 2) {
       quantize_mfma_kernel<2><<<fgrid, kMThreads, 0, stream>>>(kind, x, n_src, tok_stride, head_stride, src_idx,
                                                               n_tok, n_kv, rot, clip, dst_slot, codes, sz,
                                                               n_pages, (int)tiles);

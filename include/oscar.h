@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define OSCAR_ABI_VERSION 3
+#define OSCAR_ABI_VERSION 4
 #define OSCAR_PAGE_TOKENS 64
 
 #ifndef OSCAR_API
@@ -92,12 +92,15 @@ typedef enum oscar_kind { OSCAR_KIND_K = 0, OSCAR_KIND_V = 1 } oscar_kind;
 /* Quantisation groups: by default one group is all head_dim channels of a
  * (token, head).  With 64-channel groups every block of 64 consecutive
  * channels has its own (scale, zero) (head_dim 128: two groups; head_dim 64:
- * one, the same as the default), which is where the bit-reversal permutation
- * of R balances the groups (gist.science summary, section 2.2A).  The
- * scale/zero pool is then [n_pages][n_kv][64*head_dim/64][2], group-planar:
- * group j of token o at j*64 + o.  OR'ed into a demotion's kind; the decode
- * args carry the group size. */
+ * one, the same as the default); with 32-channel groups every block of 32
+ * (head_dim 128: four groups; head_dim 64: two).  Sub-head groups are where
+ * the bit-reversal permutation of R balances the groups (gist.science
+ * summary, section 2.2A; aicoding.csdn.net explainer, section 3).  With ng
+ * groups per head the scale/zero pool is [n_pages][n_kv][64*ng][2],
+ * group-planar: group j of token o at j*64 + o.  At most one of the two flags
+ * is OR'ed into a demotion's kind; the decode args carry the group size. */
 #define OSCAR_GROUPS_64 0x200
+#define OSCAR_GROUPS_32 0x400
 
 /* ABI version of the loaded library (OSCAR_ABI_VERSION). */
 OSCAR_API int oscar_abi_version(void);
@@ -119,8 +122,10 @@ OSCAR_API const char* oscar_status_str(int status);
  *   row and (scale, zero) into slot dst_slot = page*64 + offset.
  *
  *  kind          OSCAR_KIND_K or OSCAR_KIND_V (selects the in-page layout),
- *                optionally OR'ed with OSCAR_CODEBOOK_LLOYD_MAX and / or
- *                OSCAR_GROUPS_64 (then scale_zero holds 64*head_dim/64 pairs per head)
+ *                optionally OR'ed with OSCAR_CODEBOOK_LLOYD_MAX and / or one of
+ *                OSCAR_GROUPS_64, OSCAR_GROUPS_32 (then scale_zero holds 64*ng
+ *                pairs per head, ng = head_dim/64 or head_dim/32); both group
+ *                flags together: OSCAR_EINVAL
  *  x             bf16; element (token s, head g, channel c) is at
  *                x[s*x_tok_stride + g*x_head_stride + c]; the caller
  *                guarantees that address is valid for every s in [0, n_src)
@@ -132,7 +137,7 @@ OSCAR_API const char* oscar_status_str(int status);
  *  clip          per-layer threshold, finite, 0 < clip <= 65504 (host scalar)
  *  dst_slot      int32 [n_tok]; slots outside [0, n_pages*64) are skipped
  *  codes         uint8 pool [n_pages][n_kv][64*head_dim/4]
- *  scale_zero    uint16 pool [n_pages][n_kv][64][2]
+ *  scale_zero    uint16 pool [n_pages][n_kv][64*ng][2] (ng = 1 without a group flag)
  *  Two demoted tokens must not share a slot (the result would be unspecified).
  */
 OSCAR_API oscar_status oscar_quantize_pack(int32_t kind, const uint16_t* x, int64_t n_src,
@@ -200,8 +205,9 @@ typedef struct oscar_decode_args {
   int32_t codebook;         /* OSCAR_CODEBOOK_UNIFORM or OSCAR_CODEBOOK_LLOYD_MAX: the
                                codebook the pools were demoted with (a decode step also
                                demotes with it)                                        */
-  int32_t group_channels;   /* 0 (a group is the whole head) or 64 (OSCAR_GROUPS_64
-                               pools); a decode step demotes with the same groups      */
+  int32_t group_channels;   /* 0 (a group is the whole head), 64 (OSCAR_GROUPS_64 pools)
+                               or 32 (OSCAR_GROUPS_32 pools); a decode step demotes with
+                               the same groups                                         */
 } oscar_decode_args;
 
 /* Workspace bytes oscar_decode_attn needs for these sizes (0 on invalid sizes).

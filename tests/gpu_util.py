@@ -88,10 +88,13 @@ def gpu_decode(cfg: dict, pools, *, block_table=None, hist_len=None, sink_len=No
 
 
 def gpu_quantize(kind: str, x: np.ndarray, rot: np.ndarray, clip, dst_slot: np.ndarray, n_pages: int,
-                 src_idx=None, pools=None, codebook: str = "uniform", groups64: bool = False):
+                 src_idx=None, pools=None, codebook: str = "uniform", group_channels: int = 0):
+    """Demote on the GPU with the given codebook and group size (0: the whole
+    head; 64 or 32 channels) into fresh pools (or ``pools``)."""
     n_kv, d = rot.shape[0], rot.shape[-1]
-    codes, sz = pools if pools is not None else empty_pools(n_pages, n_kv, d, ng=d // 64 if groups64 else 1)
-    flags = CODEBOOK_FLAG[codebook] | (hip.GROUPS_64 if groups64 else 0)
+    ng = hip.groups_per_head(d, group_channels)
+    codes, sz = pools if pools is not None else empty_pools(n_pages, n_kv, d, ng=ng)
+    flags = CODEBOOK_FLAG[codebook] | {0: 0, 64: hip.GROUPS_64, 32: hip.GROUPS_32}[group_channels]
     hip.oscar_quantize_pack((hip.KIND_K if kind == "k" else hip.KIND_V) | flags, dev(x), dev(rot),
                             float(clip),
                             dev(dst_slot.astype(np.int32)), codes, sz,

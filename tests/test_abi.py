@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
     L = hip.lib()
     for n in declared_functions():
         assert hasattr(L, n), n
-    assert hip.oscar_abi_version() == hip.ABI_VERSION == 3
+    assert hip.oscar_abi_version() == hip.ABI_VERSION == 4
     # the binding offers a function of the same name for each entry point
     for n in declared_functions():
         assert callable(getattr(hip, n)), n
@@ -52,7 +52,8 @@ def _qp(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(kind=2), hip.OSCAR_EINVAL),
-    (dict(kind=0x400), hip.OSCAR_EINVAL),                            # an unknown flag
+    (dict(kind=0x800), hip.OSCAR_EINVAL),                            # an unknown flag
+    (dict(kind=0x600), hip.OSCAR_EINVAL),                            # both group sizes
     (dict(kind=0x102), hip.OSCAR_EINVAL),
     (dict(d=96), hip.OSCAR_EUNSUPPORTED),
     (dict(clip=0.0), hip.OSCAR_EINVAL),
@@ -97,7 +98,8 @@ def _decode_args(**kw):
     (dict(shared_pages=-1), hip.OSCAR_EINVAL),
     (dict(shared_pages=2), hip.OSCAR_EINVAL),                        # 2 pages > max_hist_len 100
     (dict(codebook=1), hip.OSCAR_EINVAL),
-    (dict(group_channels=32), hip.OSCAR_EINVAL),
+    (dict(group_channels=16), hip.OSCAR_EINVAL),
+    (dict(group_channels=48), hip.OSCAR_EINVAL),
     (dict(batch=0, q=None, out=None), hip.OSCAR_OK),
 ])
 def test_decode_validation(kw, status):

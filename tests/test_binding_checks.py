@@ -20,13 +20,13 @@ def _decode_kw(group_channels, sz_pairs):
                 workspace=f(256, dt=torch.uint8), group_channels=group_channels)
 
 
-@pytest.mark.parametrize("group_channels,sz_pairs", [(64, 64), (0, 128)])
+@pytest.mark.parametrize("group_channels,sz_pairs", [(64, 64), (0, 128), (32, 128), (64, 256)])
 def test_decode_args_rejects_pools_of_the_other_grouping(group_channels, sz_pairs):
     with pytest.raises(ValueError, match="k_sz must be"):
         hip.decode_args(**_decode_kw(group_channels, sz_pairs))
 
 
-@pytest.mark.parametrize("group_channels,sz_pairs", [(64, 128), (0, 64)])
+@pytest.mark.parametrize("group_channels,sz_pairs", [(64, 128), (0, 64), (32, 256)])
 def test_decode_args_accepts_matching_pools(group_channels, sz_pairs):
     # the shape checks pass; the pointer check then refuses host tensors
     with pytest.raises(ValueError, match="device tensor"):
@@ -42,6 +42,8 @@ def test_quantize_pack_checks_the_pool_against_the_kind():
         hip.oscar_quantize_pack(hip.KIND_K | hip.GROUPS_64, x, rot, 1.0, slot, codes, torch.zeros((4, 2, 64, 2)))
     with pytest.raises(ValueError, match="pool shapes"):
         hip.oscar_quantize_pack(hip.KIND_K, x, rot, 1.0, slot, codes, torch.zeros((4, 2, 128, 2)))
+    with pytest.raises(ValueError, match="pool shapes"):
+        hip.oscar_quantize_pack(hip.KIND_K | hip.GROUPS_32, x, rot, 1.0, slot, codes, torch.zeros((4, 2, 128, 2)))
 
 
 def test_decode_step_checks_the_demotion_pools_against_the_groups():
@@ -50,3 +52,13 @@ def test_decode_step_checks_the_demotion_pools_against_the_groups():
     dk.sz_pairs = 64                      # a whole-head pool, but the step writes two pairs per token
     with pytest.raises(ValueError, match="demote_k"):
         hip.oscar_decode_step(args=(a, None, 0), demote_k=dk)
+    a32 = hip.DecodeArgs(head_dim=128, group_channels=32)
+    dk.sz_pairs = 128                     # a 64-channel pool, but the step writes four pairs per token
+    with pytest.raises(ValueError, match="demote_k"):
+        hip.oscar_decode_step(args=(a32, None, 0), demote_k=dk)
+
+
+def test_groups_per_head():
+    assert [hip.groups_per_head(128, g) for g in (0, 64, 32, 128)] == [1, 2, 4, 1]
+    assert [hip.groups_per_head(64, g) for g in (0, 64, 32)] == [1, 1, 2]
+    assert [hip.kind_group_channels(k) for k in (hip.KIND_V, hip.KIND_K | hip.GROUPS_64, hip.GROUPS_32)] == [0, 64, 32]

@@ -40,11 +40,11 @@ def _limit_cache(codebook, groups=1):
     vs = np.zeros((hp, n_kv, PAGE, 2), np.uint16)
     vs[..., 0] = np.float16(0.75).view(np.uint16)
     vs[..., 1] = np.float16(-1.0).view(np.uint16)
-    if groups == 2:   # 64-channel groups: the same K pairs for both, V group 1 at a smaller scale
-        ks = np.concatenate([ks, ks], axis=2)
+    if groups > 1:   # the same K pairs for every group, V groups past the first at a smaller scale
+        ks = np.concatenate([ks] * groups, axis=2)
         vs2 = vs.copy()
         vs2[..., 0] = np.float16(0.5).view(np.uint16)
-        vs = np.concatenate([vs, vs2], axis=2)
+        vs = np.concatenate([vs] + [vs2] * (groups - 1), axis=2)
     table = np.tile(rng.permutation(hp).astype(np.int32), (B, 1))
     eye = np.stack([np.eye(d, dtype=np.float32)] * n_kv)
     cfg = dict(q=q, sink_k=np.zeros((B, n_kv, 64, d), np.uint16), sink_v=np.zeros((B, n_kv, 64, d), np.uint16),
@@ -53,12 +53,12 @@ def _limit_cache(codebook, groups=1):
                hist_len=np.full(B, hl, np.int32), block_table=table, r_k=eye, r_v=eye, sm_scale=sm)
     if codebook != "uniform":
         cfg["codebook"] = codebook
-    if groups == 2:
-        cfg["group_channels"] = 64
+    if groups > 1:
+        cfg["group_channels"] = d // groups
     return cfg, (kc, vc, ks, vs)
 
 
-@pytest.mark.parametrize("groups", [1, 2])
+@pytest.mark.parametrize("groups", [1, 2, 4])
 @pytest.mark.parametrize("codebook", ["uniform", "lloyd_max"])
 def test_longest_wave_range_at_the_integer_bound(codebook, groups):
     cfg, pools = _limit_cache(codebook, groups)

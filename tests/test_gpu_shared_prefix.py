@@ -98,10 +98,10 @@ def test_prefix_quads_match_oracle(B):
     compare_out(gpu_decode(cfg, pools, shared_pages=13), ref, what=f"prefix quads B={B}")
 
 
-@pytest.mark.parametrize("codebook,groups", [("lloyd_max", 0), ("uniform", 64)])
+@pytest.mark.parametrize("codebook,groups", [("lloyd_max", 0), ("uniform", 64), ("uniform", 32)])
 def test_prefix_pairs_for_other_formats(codebook, groups):
-    """The Lloyd-Max codebook and 64-channel groups pack two requests per wave
-    even in batches of four or more."""
+    """The Lloyd-Max codebook and 64- or 32-channel groups pack two requests
+    per wave even in batches of four or more."""
     from gpu_util import oracle_pools as pools_of
     ctx = 64 + 256 + 64 * 21
     shape = synth.DecodeShape("prefix-fmt-b5", 5, 8, 2, 128, ctx, shared_hist_pages=13)

@@ -37,7 +37,7 @@ def _pools_with_room(cfg):
     return kc, vc, ks, vs
 
 
-@pytest.mark.parametrize("groups", [0, 64])
+@pytest.mark.parametrize("groups", [0, 64, 32])
 @pytest.mark.parametrize("codebook", ["uniform", "lloyd_max"])
 @pytest.mark.parametrize("shape", SHAPES, ids=[s.name for s in SHAPES])
 def test_decode_step_matches_separate_oracle_steps(shape, codebook, groups):
