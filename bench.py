@@ -397,9 +397,11 @@ def bulk_demotion(args, tm):
     x = {k: t(cfg["x_" + k]) for k in ("k", "v")}
     rot = {k: t(cfg["r_" + k]) for k in ("k", "v")}
     slot = t(cfg["dst_slot"])
+    ng = hip.groups_per_head(d, args.groups)   # (scale, zero) pairs per token and head
     pools = {k: (torch.zeros((P, n_kv, 64 * d // 4), dtype=torch.uint8, device=dev),
-                 torch.zeros((P, n_kv, 64, 2), dtype=torch.int16, device=dev)) for k in ("k", "v")}
-    kinds = {"k": hip.KIND_K, "v": hip.KIND_V}
+                 torch.zeros((P, n_kv, 64 * ng, 2), dtype=torch.int16, device=dev)) for k in ("k", "v")}
+    gflag = {0: 0, 64: hip.GROUPS_64, 32: hip.GROUPS_32}[args.groups]
+    kinds = {"k": hip.KIND_K | gflag, "v": hip.KIND_V | gflag}
 
     def launch(i):
         k = "kv"[i % 2]
@@ -412,7 +414,7 @@ def bulk_demotion(args, tm):
     g = tm.capture(launch, range(n))
     sec, _ = tm.timed(g, None, 1)
     us = sec * 1e6 / n
-    bytes_per = n_tok * n_kv * (2 * d + d // 4 + 4) + rot["k"].numel() * 4 + slot.numel() * 4
+    bytes_per = n_tok * n_kv * (2 * d + d // 4 + 4 * ng) + rot["k"].numel() * 4 + slot.numel() * 4
     flops_per = 2.0 * d * d * n_kv * n_tok
     gbs = bytes_per / (us * 1e-6) / 1e9
     tfs = flops_per / (us * 1e-6) / 1e12
@@ -421,7 +423,8 @@ def bulk_demotion(args, tm):
         f"{tfs:.1f} TFLOP/s ({tfs / peak:.1%} of the {hip.DEMOTION_MATMUL_DTYPE} matrix peak)")
     del g, x, pools
     return {"config": {"workload": cfg["name"], "tokens": n_tok, "n_kv_heads": n_kv, "head_dim": d,
-                       "tensors": "K and V, one launch each", "kernel": "oscar_quantize_pack (quantize_pack_kernel)"},
+                       "group_channels": args.groups, "tensors": "K and V, one oscar_quantize_pack call each",
+                       "kernel": "quantize_mfma_kernel (certified fast pass) + quantize_exact_kernel (marked tokens)"},
             "us_per_tensor": us, "tokens_per_s": n_tok / (2 * us * 1e-6),
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": bytes_per, "kernel_us": us},

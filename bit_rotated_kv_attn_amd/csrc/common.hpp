@@ -140,7 +140,8 @@ struct DecodePlan {
 // two 4-wave scan blocks per CU).  The split policy sizes the history splits
 // so that history and BF16 blocks together fill them in one round: every wave
 // then pays the latency of its first page once, and no second round of
-// blocks runs on a partly idle chip.
+// blocks runs on a partly idle chip.  Scan variants that fit one block per
+// CU (scan_resident_blocks) plan with half as many.
 constexpr int kResidentBlocks = OSCAR_RESIDENT_BLOCKS;
 // at most 64 pages per wave (one page id per lane), which also keeps the int32
 // PV accumulators far from overflow
@@ -163,8 +164,10 @@ __host__ __device__ constexpr bool kind_is_k(int kind) {
 constexpr int kPartAcc = 4;
 __host__ __device__ constexpr int part_row(int d) { return d + kPartAcc; }
 
+// resident: scan blocks resident at once (the workspace query plans with the
+// largest count, whose splits and workspace bound every other plan's)
 inline DecodePlan make_decode_plan(int B, int Hq, int n_kv, int d, int max_hist_len, int sink_cap,
-                                   int recent_cap) {
+                                   int recent_cap, long resident = kResidentBlocks) {
   DecodePlan p{};
   const int G = Hq / n_kv;
   const int NB = (G + 3) / 4;
@@ -173,7 +176,7 @@ inline DecodePlan make_decode_plan(int B, int Hq, int n_kv, int d, int max_hist_
   p.chunks = p.sink_chunks + (recent_cap + kPage - 1) / kPage;
   if (p.hist_pages > 0) {
     const long units = (long)(B > 0 ? B : 1) * n_kv;
-    long target = kResidentBlocks - units * p.chunks;   // blocks left for history (one BF16 block per chunk)
+    long target = resident - units * p.chunks;   // blocks left for history (one BF16 block per chunk)
     if (target < units) target = units;
     long s0 = (target + units - 1) / units;
     const long s_min = (p.hist_pages + kMaxPagesPerSplit - 1) / kMaxPagesPerSplit;
@@ -233,5 +236,9 @@ hipError_t launch_decode_phase(int phase, const oscar_decode_args& a, const Deco
 
 hipError_t launch_decode_bf16(const oscar_bf16_decode_args& a, const Bf16Plan& plan, char* ws,
                               hipStream_t stream);
+
+// scan blocks of the variant these (validated) args launch that are resident at
+// once: kResidentBlocks scaled by its blocks per compute unit (two or one)
+long scan_resident_blocks(const oscar_decode_args& a);
 
 }  // namespace oscar

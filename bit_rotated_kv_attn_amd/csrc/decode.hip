@@ -1165,16 +1165,34 @@ constexpr int scan_waves_per_simd() {
   return NG == 4 || ((G > 8 || PACK > 2) && (LM || NG == 2)) ? 1 : OSCAR_SCAN_WAVES_PER_SIMD;
 }
 
+// LDS of a scan block: four history waves' rings (a group-4 kernel also runs
+// 4*PACK-head waves, PACK requests, on shared-prefix splits) or four BF16
+// chunk waves' tiles, whichever is larger
+template <int D, int G, int NG, int PACK>
+constexpr int scan_smem_bytes() {
+  constexpr int own = 4 * Ring<D, (G + 3) / 4, NG>::kWaveBytes;
+  constexpr int pack = G == 4 ? 4 * Ring<D, PACK, NG>::kWaveBytes : 0;
+  constexpr int hist = own > pack ? own : pack;
+  constexpr int bf16 = 4 * bf16_lds_bytes<D, G>();
+  return hist > bf16 ? hist : bf16;
+}
+
+// Scan blocks one compute unit holds at once: the waves per SIMD the kernel is
+// compiled for (a block has one wave per SIMD), or fewer if its LDS (plus the
+// four block flags) does not fit that many times into the 160 KB of a CU.
+constexpr int kLdsPerCu = 160 * 1024;
+template <int D, int G, bool LM, int NG, int PACK>
+constexpr int scan_blocks_per_cu() {
+  constexpr int by_lds = kLdsPerCu / (scan_smem_bytes<D, G, NG, PACK>() + 16);
+  constexpr int by_waves = scan_waves_per_simd<G, LM, NG, PACK>();
+  return by_lds < by_waves ? by_lds : by_waves;
+}
+
 template <int D, int G, bool LM, int NG, int PACK = 2>
 __global__ __launch_bounds__(kBlock, (scan_waves_per_simd<G, LM, NG, PACK>())) void decode_main_kernel(DecodeDev p) {
   constexpr int NB = (G + 3) / 4;
   using RG = Ring<D, NB, NG>;
-  // a group-4 kernel also runs 4*PACK-head waves (PACK requests) on shared-prefix splits
-  constexpr int kHistOwn = 4 * RG::kWaveBytes;
-  constexpr int kHistPair = G == 4 ? 4 * Ring<D, PACK, NG>::kWaveBytes : 0;
-  constexpr int kHistBytes = kHistOwn > kHistPair ? kHistOwn : kHistPair;
-  constexpr int kBf16Bytes = 4 * bf16_lds_bytes<D, G>();
-  constexpr int kSmem = kHistBytes > kBf16Bytes ? kHistBytes : kBf16Bytes;
+  constexpr int kSmem = scan_smem_bytes<D, G, NG, PACK>();
   static_assert(4 * G * part_row(D) * 4 <= kSmem, "BF16 merge slots must fit");
   static_assert(G * part_row(D) * 4 <= RG::kWaveBytes, "merge slot must fit in the wave's ring");
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
@@ -1737,6 +1755,40 @@ void launch_bf16_g(const Bf16Dev& dv, hipStream_t stream) {
   }
 }
 
+// (scale, zero) groups per head of the pools a decode reads
+int decode_groups(const oscar_decode_args& a) {
+  return a.group_channels > 0 && a.group_channels < a.head_dim ? a.head_dim / a.group_channels : 1;
+}
+
+// blocks per CU of the scan variant launch_main picks for these formats (the
+// four-request packs of group size 4 included, whichever is smaller)
+template <int D, int G>
+int scan_blocks_per_cu_of(bool lm, int ng) {
+  int b;
+  if (ng == 2) {
+    b = lm ? scan_blocks_per_cu<D, G, true, 2, 2>() : scan_blocks_per_cu<D, G, false, 2, 2>();
+  } else if (ng == 4) {
+    if constexpr (D == 128) b = lm ? scan_blocks_per_cu<D, G, true, 4, 2>() : scan_blocks_per_cu<D, G, false, 4, 2>();
+    else b = 1;   // not reached: four groups need head_dim 128
+  } else {
+    b = lm ? scan_blocks_per_cu<D, G, true, 1, 2>() : scan_blocks_per_cu<D, G, false, 1, 2>();
+    if constexpr (D == 128 && G == 4)
+      if (!lm) b = std::min(b, scan_blocks_per_cu<D, 4, false, 1, 4>());
+  }
+  return b;
+}
+
+template <int D>
+int scan_blocks_per_cu_g(int G, bool lm, int ng) {
+  switch (G) {
+    case 1: return scan_blocks_per_cu_of<D, 1>(lm, ng);
+    case 2: return scan_blocks_per_cu_of<D, 2>(lm, ng);
+    case 4: return scan_blocks_per_cu_of<D, 4>(lm, ng);
+    case 8: return scan_blocks_per_cu_of<D, 8>(lm, ng);
+    default: return scan_blocks_per_cu_of<D, 16>(lm, ng);
+  }
+}
+
 DecodeDev make_dev(const oscar_decode_args& a, const DecodePlan& plan, char* ws) {
   DecodeDev dv{};
   dv.B = a.batch; dv.Hq = a.n_q_heads; dv.n_kv = a.n_kv_heads; dv.G = a.n_q_heads / a.n_kv_heads;
@@ -1747,7 +1799,7 @@ DecodeDev make_dev(const oscar_decode_args& a, const DecodePlan& plan, char* ws)
   dv.chunks = plan.chunks; dv.sink_chunks = plan.sink_chunks;
   dv.bf_blocks = plan.chunks;
   dv.lm = a.codebook == OSCAR_CODEBOOK_LLOYD_MAX ? 1 : 0;
-  dv.ng = a.group_channels > 0 && a.group_channels < a.head_dim ? a.head_dim / a.group_channels : 1;
+  dv.ng = decode_groups(a);
   // pack the splits that lie wholly inside a shared prefix (group size 4, two or
   // more requests): four requests per wave with the uniform codebook and
   // whole-head groups at d = 128 (the 16-head wave fits two per SIMD there),
@@ -1796,6 +1848,13 @@ hipError_t launch_decode_phase(int phase, const oscar_decode_args& a, const Deco
     else launch_main_g<64>(dv, stream);
   }
   return hipGetLastError();
+}
+
+long scan_resident_blocks(const oscar_decode_args& a) {
+  const int G = a.n_q_heads / a.n_kv_heads, ng = decode_groups(a);
+  const bool lm = a.codebook == OSCAR_CODEBOOK_LLOYD_MAX;
+  const int b = a.head_dim == 128 ? scan_blocks_per_cu_g<128>(G, lm, ng) : scan_blocks_per_cu_g<64>(G, lm, ng);
+  return (long)kResidentBlocks * std::max(b, 1) / 2;
 }
 
 hipError_t launch_decode_bf16(const oscar_bf16_decode_args& a, const Bf16Plan& plan, char* ws,
