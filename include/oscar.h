@@ -95,7 +95,8 @@ typedef enum oscar_kind { OSCAR_KIND_K = 0, OSCAR_KIND_V = 1 } oscar_kind;
  * one, the same as the default); with 32-channel groups every block of 32
  * (head_dim 128: four groups; head_dim 64: two).  Sub-head groups are where
  * the bit-reversal permutation of R balances the groups (gist.science
- * summary, section 2.2A; aicoding.csdn.net explainer, section 3).  With ng
+ * summary, section 2.2A; the myzaker.com article on OSCAR, its paragraph on
+ * aligning the rotation with attention).  With ng
  * groups per head the scale/zero pool is [n_pages][n_kv][64*ng][2],
  * group-planar: group j of token o at j*64 + o.  At most one of the two flags
  * is OR'ed into a demotion's kind; the decode args carry the group size. */
