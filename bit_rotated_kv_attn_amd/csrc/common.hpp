@@ -143,6 +143,13 @@ struct DecodePlan {
 // blocks runs on a partly idle chip.  Scan variants that fit one block per
 // CU (scan_resident_blocks) plan with half as many.
 constexpr int kResidentBlocks = OSCAR_RESIDENT_BLOCKS;
+#ifndef OSCAR_SCAN_WAVES_PER_SIMD
+#define OSCAR_SCAN_WAVES_PER_SIMD 2
+#endif
+// the most scan blocks any variant keeps resident (kResidentBlocks counts two
+// per CU; a variant holds at most OSCAR_SCAN_WAVES_PER_SIMD): the workspace
+// query plans with it, so its splits and workspace bound every launch's
+constexpr long kMaxResidentBlocks = (long)kResidentBlocks * OSCAR_SCAN_WAVES_PER_SIMD / 2;
 // at most 64 pages per wave (one page id per lane), which also keeps the int32
 // PV accumulators far from overflow
 constexpr int kMaxPagesPerSplit = 4 * 64;
@@ -167,7 +174,7 @@ __host__ __device__ constexpr int part_row(int d) { return d + kPartAcc; }
 // resident: scan blocks resident at once (the workspace query plans with the
 // largest count, whose splits and workspace bound every other plan's)
 inline DecodePlan make_decode_plan(int B, int Hq, int n_kv, int d, int max_hist_len, int sink_cap,
-                                   int recent_cap, long resident = kResidentBlocks) {
+                                   int recent_cap, long resident = kMaxResidentBlocks) {
   DecodePlan p{};
   const int G = Hq / n_kv;
   const int NB = (G + 3) / 4;

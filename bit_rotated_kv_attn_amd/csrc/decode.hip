@@ -1152,9 +1152,6 @@ __device__ __forceinline__ void demote_step_block(const DecodeDev& p, int id, co
 // ---------------------------------------------------------------------------
 // 2. scan: history splits, then one BF16 block per 64-token sink / recent chunk
 // ---------------------------------------------------------------------------
-#ifndef OSCAR_SCAN_WAVES_PER_SIMD
-#define OSCAR_SCAN_WAVES_PER_SIMD 2
-#endif
 // Waves per SIMD the scan is compiled for: the 16-head wave (G = 16, or four
 // requests of group size 4 in one wave) fits two per SIMD without spills with
 // the uniform codebook and whole-head groups, and one otherwise.  Four groups
