@@ -501,7 +501,7 @@ constexpr int kPlaneRow = 128, kPlaneBytes = 16 * kPlaneRow;
 __device__ __forceinline__ int plane_chunk(int r, int c) { return r * kPlaneRow + 16 * (c ^ ((r >> 1) & 3)); }
 
 // Per-wave LDS: a ring of page stages and the weight planes (unless they
-// reuse the consumed K codes).  Two stages: the page being processed and
+// reuse the consumed page slot).  Two stages: the page being processed and
 // one page in flight.  With every wave of the chip one page ahead, about 9 MB
 // of copies are outstanding, enough to keep HBM busy; deeper rings only
 // lengthen the memory queues, and a wave then stalls issuing its copies
@@ -509,16 +509,26 @@ __device__ __forceinline__ int plane_chunk(int r, int c) { return r * kPlaneRow 
 template <int D, int NB, int NG = 1>
 struct Ring {
   static constexpr int PB = (NB + 1) / 2;   // PV row blocks
-  // The planes reuse the consumed K codes when they fit and every row is
-  // written on every page (two head blocks per row block); otherwise they
-  // have their own LDS, zeroed once, so rows of absent heads stay zero.
-  static constexpr bool kPlanesInK = NB % 2 == 0 && PB * NG * kPlaneBytes <= 16 * D;
+  // The planes reuse the slot of the page being processed.  With one or two
+  // groups: all of them in its consumed K codes, when they fit there and every
+  // row is written on every page (two head blocks per row block).  With four
+  // groups: the first kSlotPlanes anywhere in the slot, since every word of it
+  // (codes, scales and zeros) is in registers before the first plane store;
+  // rows of an absent second head block then keep stale bytes, which only
+  // reach PV result rows that are never read (MFMA rows are independent, and
+  // the rescale and the fold skip absent head blocks).  The rest have their
+  // own LDS, zeroed once, so rows of absent heads stay zero.
+  static constexpr int kAllPlanes = PB * NG;
+  static constexpr int kSlotFit = Stage<D, NG>::kBytes / kPlaneBytes;
+  static constexpr int kSlotPlanes = NG == 4 ? (kAllPlanes < kSlotFit ? kAllPlanes : kSlotFit)
+                                     : NB % 2 == 0 && kAllPlanes * kPlaneBytes <= 16 * D ? kAllPlanes : 0;
+  static constexpr bool kPlanesInK = kSlotPlanes == kAllPlanes;   // no LDS of their own
 #ifdef OSCAR_SCAN_STAGES
   static constexpr int kStages = OSCAR_SCAN_STAGES;
 #else
   static constexpr int kStages = 2;
 #endif
-  static constexpr int kPlaneLds = kPlanesInK ? 0 : PB * NG * kPlaneBytes;
+  static constexpr int kPlaneLds = (kAllPlanes - kSlotPlanes) * kPlaneBytes;
   static constexpr int kWaveBytes = kStages * Stage<D, NG>::kBytes + kPlaneLds;
 };
 
@@ -685,7 +695,7 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
   uint8_t* planes = RG::kPlanesInK ? nullptr : ring + NS * S::kBytes;
   if constexpr (!RG::kPlanesInK) {   // rows of absent heads are never written
 #pragma unroll
-    for (int o = 0; o < PB * NG * kPlaneBytes; o += 16 * kWave)
+    for (int o = 0; o < RG::kPlaneLds; o += 16 * kWave)
       *reinterpret_cast<uint4*>(planes + o + 16 * lane) = make_uint4(0, 0, 0, 0);
   }
   // (page, head) block of each of the wave's pages, one per lane; an invalid
@@ -772,58 +782,71 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
     // Relative logit (log2 units): scale*ca*dot + (zero*cb - mref).
     float lg[NB][4], lmax[NB];
     bool need = false;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
+    auto qk_block = [&](int nb, int tb) {
       const bool hok = 4 * nb + grp < G;
+      v4i dq, dq0, dqg[3];
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        v4i dq, dq0, dqg[3];
+      for (int c = 0; c < NCH; ++c) {
+        const uint32_t w = kword[tb * NCH + c];
+        const v4i bop = v4i{code_operand<LM>(w, 0), code_operand<LM>(w, 1), code_operand<LM>(w, 2),
+                            code_operand<LM>(w, 3)};
+        dq = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[nb][c], bop, c == 0 ? v4i{0, 0, 0, 0} : dq, 0, 0, 0);
+        if constexpr (NG == 2)
+          dq0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa0[nb][c], bop, c == 0 ? v4i{0, 0, 0, 0} : dq0, 0, 0, 0);
+        if constexpr (NG == 4) {
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-          const uint32_t w = kword[tb * NCH + c];
-          const v4i bop = v4i{code_operand<LM>(w, 0), code_operand<LM>(w, 1), code_operand<LM>(w, 2),
-                              code_operand<LM>(w, 3)};
-          dq = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[nb][c], bop, c == 0 ? v4i{0, 0, 0, 0} : dq, 0, 0, 0);
-          if constexpr (NG == 2)
-            dq0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa0[nb][c], bop, c == 0 ? v4i{0, 0, 0, 0} : dq0, 0, 0, 0);
-          if constexpr (NG == 4) {
-#pragma unroll
-            for (int j = 0; j < 3; ++j) {
-              const v4i bj = grp == j ? bop : v4i{0, 0, 0, 0};
-              dqg[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[nb][c], bj, c == 0 ? v4i{0, 0, 0, 0} : dqg[j], 0, 0, 0);
-            }
+          for (int j = 0; j < 3; ++j) {
+            const v4i bj = grp == j ? bop : v4i{0, 0, 0, 0};
+            dqg[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[nb][c], bj, c == 0 ? v4i{0, 0, 0, 0} : dqg[j], 0, 0, 0);
           }
-        }
-        // digits: d0 + 2^8 d1 and d2 + 2^8 d3 are exact in int32
-        auto dot_of = [](v4i v) {
-          const int lo = v.x + v.y * 256, hi = v.z + v.w * 256;
-          return fmaf((float)hi, 65536.0f, (float)lo);
-        };
-        if constexpr (NG == 1) {
-          // an invalid head gets fma(0, dot, -inf) = -inf (dot is finite)
-          const float off = hok ? fmaf(zk[0][tb], cb[nb][0], -mref[nb]) : -INFINITY;
-          lg[nb][tb] = fmaf(sk[0][tb] * ca[nb], dot_of(dq), off);
-        } else {
-          // per-group digit sums, then the logit from the last group down
-          v4i dg[NG];
-          if constexpr (NG == 2) {
-            dg[0] = dq0;
-            dg[1] = dq - dq0;
-          } else {
-            dg[0] = dqg[0];
-            dg[1] = dqg[1];
-            dg[2] = dqg[2];
-            dg[3] = dq - dqg[0] - dqg[1] - dqg[2];
-          }
-          float off = -mref[nb];
-#pragma unroll
-          for (int j = NG - 1; j >= 0; --j) off = fmaf(zk[j][tb], cb[nb][j], off);
-          float l = hok ? off : -INFINITY;
-#pragma unroll
-          for (int j = NG - 1; j >= 0; --j) l = fmaf(sk[j][tb] * ca[nb], dot_of(dg[j]), l);
-          lg[nb][tb] = l;
         }
       }
+      // digits: d0 + 2^8 d1 and d2 + 2^8 d3 are exact in int32
+      auto dot_of = [](v4i v) {
+        const int lo = v.x + v.y * 256, hi = v.z + v.w * 256;
+        return fmaf((float)hi, 65536.0f, (float)lo);
+      };
+      if constexpr (NG == 1) {
+        // an invalid head gets fma(0, dot, -inf) = -inf (dot is finite)
+        const float off = hok ? fmaf(zk[0][tb], cb[nb][0], -mref[nb]) : -INFINITY;
+        lg[nb][tb] = fmaf(sk[0][tb] * ca[nb], dot_of(dq), off);
+      } else {
+        // per-group digit sums, then the logit from the last group down
+        v4i dg[NG];
+        if constexpr (NG == 2) {
+          dg[0] = dq0;
+          dg[1] = dq - dq0;
+        } else {
+          dg[0] = dqg[0];
+          dg[1] = dqg[1];
+          dg[2] = dqg[2];
+          dg[3] = dq - dqg[0] - dqg[1] - dqg[2];
+        }
+        float off = -mref[nb];
+#pragma unroll
+        for (int j = NG - 1; j >= 0; --j) off = fmaf(zk[j][tb], cb[nb][j], off);
+        float l = hok ? off : -INFINITY;
+#pragma unroll
+        for (int j = NG - 1; j >= 0; --j) l = fmaf(sk[j][tb] * ca[nb], dot_of(dg[j]), l);
+        lg[nb][tb] = l;
+      }
+    };
+    if constexpr (NG == 4) {
+      // one token block at a time: its K operands and four chains per head block
+      // stay in registers, and the next block's MFMAs start after these results
+      // are consumed (with every token block in flight at once, the chains' results
+      // and masked operands overflow the VGPRs into the accumulation registers)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) qk_block(nb, tb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) qk_block(nb, tb);
     }
     if (nv < kPage) {   // tokens past the history end (the last page only)
 #pragma unroll
@@ -878,7 +901,7 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
         for (int rb = 0; rb < PB; ++rb)
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            if (2 * rb + e >= NB) continue;   // rows of an absent head block hold zeros
+            if (2 * rb + e >= NB) continue;   // rows of an absent head block are never read
             const float fct = alpha[2 * rb + e] * r;
 #pragma unroll
             for (int c = 0; c < NCH; ++c)
@@ -899,13 +922,16 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
     // remainder scaled by 2^11), into the planes of the PV A operands.  Lane
     // (n, grp) holds tokens 4n..4n+3, stored in slots 4n..4n+3 in the order
     // of the B operands' halves: tokens 0, 2, 1, 3.
-    uint8_t* pl = RG::kPlanesInK ? st + S::kK : planes;
+    // plane k of (row block, group) index rb*NG + j
+    auto plane_at = [&](int k) -> uint8_t* {
+      return k < RG::kSlotPlanes ? st + k * kPlaneBytes : planes + (k - RG::kSlotPlanes) * kPlaneBytes;
+    };
     float svk[NG][4];
 #pragma unroll
     for (int j = 0; j < NG; ++j)
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) svk[j][tb] = sv[j][tb] * kap;
-    __builtin_amdgcn_wave_barrier();   // every lane has read its K words
+    __builtin_amdgcn_wave_barrier();   // every lane has read the slot's words the planes may overlay
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       float pr[4];
@@ -929,7 +955,7 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
                                       fmaf(f16_to_f32(h02 >> 16), -2048.0f, u[2]));
         const uint32_t l13 = pack_rtz(fmaf(f16_to_f32(h13 & 0xffffu), -2048.0f, u[1]),
                                       fmaf(f16_to_f32(h13 >> 16), -2048.0f, u[3]));
-        uint8_t* plane = pl + ((nb >> 1) * NG + j) * kPlaneBytes + 8 * (n & 1);
+        uint8_t* plane = plane_at((nb >> 1) * NG + j) + 8 * (n & 1);
         *reinterpret_cast<uint2*>(plane + plane_chunk(r, n >> 1)) = make_uint2(h02, h13);
         *reinterpret_cast<uint2*>(plane + plane_chunk(r + 1, n >> 1)) = make_uint2(l02, l13);
       }
@@ -948,7 +974,7 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
       for (int j = 0; j < NG; ++j)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-          wa[rb][j][ks] = *reinterpret_cast<const half8*>(pl + (rb * NG + j) * kPlaneBytes + plane_chunk(n, 2 * grp + ks));
+          wa[rb][j][ks] = *reinterpret_cast<const half8*>(plane_at(rb * NG + j) + plane_chunk(n, 2 * grp + ks));
     const uint32_t cols_lo = n < 8 ? 0xffffffffu : 0u;   // column half of this lane
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -1155,11 +1181,13 @@ __device__ __forceinline__ void demote_step_block(const DecodeDev& p, int id, co
 // Waves per SIMD the scan is compiled for: the 16-head wave (G = 16, or four
 // requests of group size 4 in one wave) fits two per SIMD without spills with
 // the uniform codebook and whole-head groups, and one otherwise.  Four groups
-// per head take one: their weight planes (8 KB per head block pair) leave
-// room in LDS for one block per compute unit.
+// per head fit two with up to 8 heads per wave (the VGPR budget of two waves
+// also keeps their MFMA results out of the accumulation registers) and one
+// with 16.
 template <int G, bool LM, int NG, int PACK>
 constexpr int scan_waves_per_simd() {
-  return NG == 4 || ((G > 8 || PACK > 2) && (LM || NG == 2)) ? 1 : OSCAR_SCAN_WAVES_PER_SIMD;
+  if constexpr (NG == 4) return G > 8 ? 1 : 2;
+  return (G > 8 || PACK > 2) && (LM || NG == 2) ? 1 : OSCAR_SCAN_WAVES_PER_SIMD;
 }
 
 // LDS of a scan block: four history waves' rings (a group-4 kernel also runs
