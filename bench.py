@@ -53,6 +53,8 @@ def parse():
                     help="INT2 codebook the history is demoted with and read by (oscar.h)")
     ap.add_argument("--groups", type=int, default=0, choices=(0, 64, 32),
                     help="channels per (scale, zero) group: 0 = the whole head, 64 or 32 = sub-head groups")
+    ap.add_argument("--prefix-cascade", action="store_true",
+                    help="read the shared prefix in cascade blocks where oscar.h allows it (prefix_cascade = 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
@@ -263,7 +265,8 @@ def decode_workload(name, args, K, warmup, with_bf16, tm):
                              hist_len=hist_len, max_hist_len=hl, k_codes=rp["k_codes"], v_codes=rp["v_codes"],
                              k_sz=rp["k_sz"], v_sz=rp["v_sz"], block_table=table, r_k=r_k, r_v=r_v,
                              out=rp["out"], workspace=ws, sm_scale=float(cfg["sm_scale"]),
-                             shared_pages=shared, codebook=cb_flag, group_channels=args.groups) for rp in reps]
+                             shared_pages=shared, codebook=cb_flag, group_channels=args.groups,
+                             prefix_cascade=args.prefix_cascade) for rp in reps]
 
     # the step demotes ring slot 0 of every request's recent window (K and V) in
     # the decode's last launch
@@ -321,11 +324,12 @@ def decode_workload(name, args, K, warmup, with_bf16, tm):
                    "n_kv_heads": n_kv, "head_dim": d, "sink": int(cfg["sink_len"][0]),
                    "history": hl, "recent": int(cfg["recent_len"][0]), "page_tokens": 64,
                    "cache_replicas": R, "shared_prefix_pages": shared, "codebook": args.codebook,
-                   "group_channels": args.groups,
+                   "group_channels": args.groups, "prefix_cascade": bool(args.prefix_cascade),
                    "step": "oscar_decode_step: demote K,V of 1 token/request + decode attention"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(name + ("-lloyd-max" if lm else "") + (f"-groups{args.groups}" if grouped else "")),
+                     "traffic": measured_traffic(name + ("-lloyd-max" if lm else "") + (f"-groups{args.groups}" if grouped else "")
+                                                 + ("-cascade" if args.prefix_cascade else "")),
                      "kernel": "decode_main_kernel (oscar_decode_scan)", "kernel_us": scan_us,
                      "bytes_per_launch": scan_bytes},
         "kv_tokens_per_s": float(cfg["hist_len"].sum() + cfg["sink_len"].sum() + cfg["recent_len"].sum())

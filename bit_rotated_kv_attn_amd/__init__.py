@@ -34,7 +34,7 @@ OSCAR_OK, OSCAR_EINVAL, OSCAR_EUNSUPPORTED, OSCAR_EWORKSPACE, OSCAR_EHIP, OSCAR_
 # bytes of the static per-GPU scratch buffer of oscar_decode_step_static (oscar.h)
 STATIC_SCRATCH_BYTES = 32 << 20
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liboscar.so")
-ABI_VERSION = 4   # OSCAR_ABI_VERSION of the oscar.h these mirrors follow
+ABI_VERSION = 5   # OSCAR_ABI_VERSION of the oscar.h these mirrors follow
 
 _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 
@@ -47,7 +47,8 @@ class DecodeArgs(ctypes.Structure):
                 ("recent_len", _vp), ("hist_len", _vp), ("max_hist_len", _i32), ("k_codes", _vp),
                 ("v_codes", _vp), ("k_sz", _vp), ("v_sz", _vp), ("n_pages", _i64),
                 ("block_table", _vp), ("max_pages", _i32), ("r_k", _vp), ("r_v", _vp), ("out", _vp),
-                ("shared_pages", _i32), ("codebook", _i32), ("group_channels", _i32)]
+                ("shared_pages", _i32), ("codebook", _i32), ("group_channels", _i32),
+                ("prefix_cascade", _i32)]
 
 
 class DemoteArgs(ctypes.Structure):
@@ -190,7 +191,7 @@ def oscar_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, max_his
 def decode_args(*, q, sink_k, sink_v, recent_k, recent_v, sink_len, recent_len, hist_len, max_hist_len: int,
                 k_codes, v_codes, k_sz, v_sz, block_table, r_k, r_v, out, workspace=None,
                 sm_scale: float | None = None, shared_pages: int = 0, codebook: int = CODEBOOK_UNIFORM,
-                group_channels: int = 0):
+                group_channels: int = 0, prefix_cascade: bool = False):
     """Marshal tensors into (DecodeArgs, workspace pointer, workspace bytes).
 
     q bf16 [B][Hq][d]; sink_k/v bf16 [B][n_kv][sink_cap][d]; recent_k/v bf16
@@ -200,7 +201,9 @@ def decode_args(*, q, sink_k, sink_v, recent_k, recent_v, sink_len, recent_len, 
     None for oscar_decode_step_static, which brings its own);
     shared_pages: leading history pages every request holds at the same ids (0: none);
     codebook: CODEBOOK_UNIFORM or CODEBOOK_LLOYD_MAX, as the pools were demoted;
-    group_channels: 0 (whole-head groups), 64 or 32, as the pools were demoted.
+    group_channels: 0 (whole-head groups), 64 or 32, as the pools were demoted;
+    prefix_cascade: read the splits inside the shared prefix in cascade blocks
+    where oscar.h allows it (one page read per group of 16 requests).
     The returned DecodeArgs holds a reference to every tensor it points to
     (``keep``), so tensors made inline stay allocated while the args live; a
     captured graph that replays the call must keep the args alive too."""
@@ -223,7 +226,8 @@ def decode_args(*, q, sink_k, sink_v, recent_k, recent_v, sink_len, recent_len, 
                    k_sz=_ptr(k_sz, 2, "k_sz"), v_sz=_ptr(v_sz, 2, "v_sz"), n_pages=k_codes.shape[0],
                    block_table=_ptr(block_table, 4, "block_table"), max_pages=block_table.shape[1],
                    r_k=_ptr(r_k, 4, "r_k"), r_v=_ptr(r_v, 4, "r_v"), out=_ptr(out, 4, "out"),
-                   shared_pages=int(shared_pages), codebook=int(codebook), group_channels=int(group_channels))
+                   shared_pages=int(shared_pages), codebook=int(codebook), group_channels=int(group_channels),
+                   prefix_cascade=int(bool(prefix_cascade)))
     a.keep = (q, sink_k, sink_v, recent_k, recent_v, sink_len, recent_len, hist_len, k_codes, v_codes, k_sz, v_sz,
               block_table, r_k, r_v, out, workspace)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

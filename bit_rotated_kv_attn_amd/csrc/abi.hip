@@ -75,8 +75,7 @@ size_t oscar_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_
   if (check_decode_shape(batch, n_q_heads, n_kv_heads, head_dim, max_hist_len, sink_cap, recent_cap) !=
       OSCAR_OK)
     return 0;
-  return make_decode_plan(batch, n_q_heads, n_kv_heads, head_dim, max_hist_len, sink_cap, recent_cap)
-      .total;
+  return sizing_plan(batch, n_q_heads, n_kv_heads, head_dim, max_hist_len, sink_cap, recent_cap).total;
 }
 
 }  // extern "C"
@@ -94,8 +93,10 @@ oscar_status check_decode(const oscar_decode_args* a, void* workspace, size_t wo
     return OSCAR_EINVAL;
   if (a->codebook != OSCAR_CODEBOOK_UNIFORM && a->codebook != OSCAR_CODEBOOK_LLOYD_MAX) return OSCAR_EINVAL;
   if (a->group_channels != 0 && a->group_channels != 64 && a->group_channels != 32) return OSCAR_EINVAL;
+  if (a->prefix_cascade != 0 && a->prefix_cascade != 1) return OSCAR_EINVAL;
   *plan = make_decode_plan(a->batch, a->n_q_heads, a->n_kv_heads, a->head_dim, a->max_hist_len,
-                           a->sink_cap, a->recent_cap, scan_resident_blocks(*a));
+                           a->sink_cap, a->recent_cap, scan_resident_blocks(*a),
+                           decode_cascade(*a) ? kCascadeMaxPagesPerSplit : kMaxPagesPerSplit);
   if (a->batch == 0) return OSCAR_OK;
   if (!a->q || !a->out || !a->sink_len || !a->recent_len || !a->hist_len) return OSCAR_EINVAL;
   if (a->sink_cap > 0 && (!a->sink_k || !a->sink_v)) return OSCAR_EINVAL;
@@ -158,8 +159,8 @@ oscar_status run_phases(const oscar_decode_args* a, void* workspace, size_t work
     if (!a) return OSCAR_EINVAL;
     if (check_decode_shape(a->batch, a->n_q_heads, a->n_kv_heads, a->head_dim, a->max_hist_len, a->sink_cap,
                            a->recent_cap) == OSCAR_OK &&
-        make_decode_plan(a->batch, a->n_q_heads, a->n_kv_heads, a->head_dim, a->max_hist_len, a->sink_cap,
-                         a->recent_cap).total > OSCAR_STATIC_SCRATCH_BYTES)
+        sizing_plan(a->batch, a->n_q_heads, a->n_kv_heads, a->head_dim, a->max_hist_len, a->sink_cap,
+                    a->recent_cap).total > OSCAR_STATIC_SCRATCH_BYTES)
       return OSCAR_ESCRATCH;
     st = check_decode(a, reinterpret_cast<void*>(uintptr_t(256)), OSCAR_STATIC_SCRATCH_BYTES, &plan);
   } else {

@@ -171,10 +171,18 @@ __host__ __device__ constexpr bool kind_is_k(int kind) {
 constexpr int kPartAcc = 4;
 __host__ __device__ constexpr int part_row(int d) { return d + kPartAcc; }
 
-// resident: scan blocks resident at once (the workspace query plans with the
-// largest count, whose splits and workspace bound every other plan's)
+// Shared-prefix cascade blocks read each page of a split for up to 16 requests
+// with every wave covering the whole split, one page id per lane: their splits
+// hold at most 64 pages.
+constexpr int kCascadeMaxPagesPerSplit = 64;
+
+// resident: scan blocks resident at once; max_pps: pages per split at most.
+// The workspace query plans with the largest count and the smallest cap any
+// launch of these sizes can use, so its splits and workspace bound every other
+// plan's.
 inline DecodePlan make_decode_plan(int B, int Hq, int n_kv, int d, int max_hist_len, int sink_cap,
-                                   int recent_cap, long resident = kMaxResidentBlocks) {
+                                   int recent_cap, long resident = kMaxResidentBlocks,
+                                   int max_pps = kMaxPagesPerSplit) {
   DecodePlan p{};
   const int G = Hq / n_kv;
   const int NB = (G + 3) / 4;
@@ -186,7 +194,7 @@ inline DecodePlan make_decode_plan(int B, int Hq, int n_kv, int d, int max_hist_
     long target = resident - units * p.chunks;   // blocks left for history (one BF16 block per chunk)
     if (target < units) target = units;
     long s0 = (target + units - 1) / units;
-    const long s_min = (p.hist_pages + kMaxPagesPerSplit - 1) / kMaxPagesPerSplit;
+    const long s_min = (p.hist_pages + max_pps - 1) / max_pps;
     if (s0 < s_min) s0 = s_min;
     if (s0 > p.hist_pages) s0 = p.hist_pages;
     p.pages_per_split = (int)((p.hist_pages + s0 - 1) / s0);
@@ -247,5 +255,24 @@ hipError_t launch_decode_bf16(const oscar_bf16_decode_args& a, const Bf16Plan& p
 // scan blocks of the variant these (validated) args launch that are resident at
 // once: kResidentBlocks scaled by its blocks per compute unit (two or one)
 long scan_resident_blocks(const oscar_decode_args& a);
+
+// Whether a launch with these (validated) args reads its shared prefix in
+// cascade blocks, and whether any launch of these sizes can (the workspace
+// query's bound): group size 4, head_dim 128, 16 or more requests; the launch
+// also needs the caller's request, the uniform codebook, whole-head groups and
+// a declared prefix of at least one cascade split.
+inline bool cascade_sizes(int batch, int n_q_heads, int n_kv_heads, int head_dim) {
+  return n_kv_heads > 0 && n_q_heads == 4 * n_kv_heads && head_dim == 128 && batch >= 16;
+}
+// the plan of the workspace query: the most splits any launch of these sizes can use
+inline DecodePlan sizing_plan(int B, int Hq, int n_kv, int d, int max_hist_len, int sink_cap, int recent_cap) {
+  return make_decode_plan(B, Hq, n_kv, d, max_hist_len, sink_cap, recent_cap, kMaxResidentBlocks,
+                          cascade_sizes(B, Hq, n_kv, d) ? kCascadeMaxPagesPerSplit : kMaxPagesPerSplit);
+}
+inline bool decode_cascade(const oscar_decode_args& a) {
+  return a.prefix_cascade == 1 && cascade_sizes(a.batch, a.n_q_heads, a.n_kv_heads, a.head_dim) &&
+         a.codebook == OSCAR_CODEBOOK_UNIFORM &&
+         (a.group_channels == 0 || a.group_channels >= a.head_dim) && a.shared_pages >= kCascadeMaxPagesPerSplit;
+}
 
 }  // namespace oscar

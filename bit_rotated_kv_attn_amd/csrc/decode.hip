@@ -69,6 +69,10 @@ struct DecodeDev {
   // (requests pack*i .. pack*i + pack - 1; pack = 2 or 4); the requests past the
   // last whole pack read them on their own
   int n_pref, packs, pack;
+  // cascade (group size 4, four-request packs, 16 or more requests): the prefix
+  // splits run as one block per (split, group of up to four packs, KV head),
+  // each page staged once for the group; pack_units = groups, else packs
+  int casc, pack_units;
   int lm;   // the pools hold Lloyd-Max codes (oscar.h OSCAR_CODEBOOK_LLOYD_MAX)
   int ng;   // (scale, zero) groups per head: 1, 2 (64-channel groups at d = 128, 32 at d = 64) or 4
   float sm_log2;
@@ -491,6 +495,29 @@ __device__ __forceinline__ void stage_page(const DecodeDev& p, size_t blk, uint3
   }
 }
 
+// A quarter of stage_page for the waves of a cascade block (one KV head's page
+// with whole-head groups): part 0 the K codes, 1 the V codes, 2 the K scales
+// and zeros, 3 the V ones.  Every copy lands where stage_page puts it.
+template <int D>
+__device__ __forceinline__ void stage_page_part(const DecodeDev& p, size_t blk, uint32_t stage_lds, StageOffsets o,
+                                                int part) {
+  using S = Stage<D, 1>;
+  stage_lds = __builtin_amdgcn_readfirstlane(stage_lds);
+  if (part == 0) {
+    const uint8_t* kb = p.k_codes + blk * (16 * D);
+    copy16_to_lds(kb, o.k, stage_lds + S::kK);
+    if constexpr (D == 128) copy16_to_lds(kb, o.k + 16, stage_lds + S::kK + 1024);
+  } else if (part == 1) {
+    const uint8_t* vb = p.v_codes + blk * (16 * D);
+    copy16_to_lds(vb, o.v, stage_lds + S::kV);
+    if constexpr (D == 128) copy16_to_lds(vb, o.v + 16 * kPage, stage_lds + S::kV + 1024);
+  } else if (part == 2) {
+    copy4_to_lds(p.k_sz + blk * kPage, o.sz, stage_lds + S::kKsz);
+  } else {
+    copy4_to_lds(p.v_sz + blk * kPage, o.sz, stage_lds + S::kVsz);
+  }
+}
+
 // Softmax weights as PV A operands: one plane per (row block of 8 heads,
 // group), 16 rows x 64 fp16 token slots.  Row 4g + 2e + part holds head
 // 4e + g of the row block (e = head block within it, g = lane group), part 0
@@ -635,10 +662,16 @@ __device__ __forceinline__ uint32_t pack_rtz(float a, float b) {   // two fp16, 
 // holds the page id of page pg_begin + lane, and qo the QK operands; both were
 // loaded by the caller together with the history length, and this wave's
 // vector loads have completed.
-template <int D, int G, bool LM, int NG>
+// CASC: the wave is one of the four of a cascade block, which all scan the
+// same pages (count and pid_lane are the block's): ring is the block's shared
+// two-stage ring, each wave issues its quarter of every page's copies, and a
+// block barrier per page makes the page visible to all; own_planes are the
+// wave's weight planes.  A wave with compute false only stages and keeps step.
+// The fold into mw follows a last block barrier (mw may overlay the ring).
+template <int D, int G, bool LM, int NG, bool CASC = false>
 __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begin, int count, int hl, int pid_lane,
                                           const HistOperands<D, G>& qo, uint8_t* ring, float* mw, bool& poison,
-                                          int lane) {
+                                          int lane, uint8_t* own_planes = nullptr, int wave = 0, bool compute = true) {
   constexpr int NB = (G + 3) / 4;
   constexpr int NCH = D / 64;   // code words per token per K plane; 64-channel chunks of V
   using S = Stage<D, NG>;
@@ -647,6 +680,9 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
   constexpr int NS = RG::kStages;
   constexpr int GC = D / NG;    // channels per (scale, zero) group
   static_assert(NG == 1 || NG == 2 || (NG == 4 && D == 128), "groups of the head, 64 or 32 channels");
+  static_assert(!CASC || (NG == 1 && !LM && NS == 2), "cascade blocks: uniform codebook, whole-head groups");
+  constexpr int kSlotPl = CASC ? 0 : RG::kSlotPlanes;                          // planes in the page slot
+  constexpr int kOwnPlaneBytes = CASC ? PB * NG * kPlaneBytes : RG::kPlaneLds;   // planes of its own
   const int n = lane & 15, grp = lane >> 4;
   const auto& qa = qo.qa;
   const auto& ca = qo.ca;
@@ -692,10 +728,10 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
   float thr = -INFINITY, smax = 0.0f, sthr = 0.0f, kap = 0.0f;
 
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_offset(ring));
-  uint8_t* planes = RG::kPlanesInK ? nullptr : ring + NS * S::kBytes;
-  if constexpr (!RG::kPlanesInK) {   // rows of absent heads are never written
+  uint8_t* planes = CASC ? own_planes : RG::kPlanesInK ? nullptr : ring + NS * S::kBytes;
+  if constexpr (kOwnPlaneBytes > 0) {   // rows of absent heads are never written
 #pragma unroll
-    for (int o = 0; o < RG::kPlaneLds; o += 16 * kWave)
+    for (int o = 0; o < kOwnPlaneBytes; o += 16 * kWave)
       *reinterpret_cast<uint4*>(planes + o + 16 * lane) = make_uint4(0, 0, 0, 0);
   }
   // (page, head) block of each of the wave's pages, one per lane; an invalid
@@ -708,7 +744,11 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
   };
   const StageOffsets soff = stage_offsets<D, NG>(lane);
   const int pre = count < NS - 1 ? count : NS - 1;
-  for (int i = 0; i < pre; ++i) stage_page<D, NG>(p, page_blk(i), ring_lds + i * S::kBytes, soff);
+  if constexpr (CASC) {
+    if (count > 0) stage_page_part<D>(p, page_blk(0), ring_lds, soff, wave);
+  } else {
+    for (int i = 0; i < pre; ++i) stage_page<D, NG>(p, page_blk(i), ring_lds + i * S::kBytes, soff);
+  }
   int slot_use = 0, slot_fill = pre;   // ring slots of page i and of page i + NS - 1
 
   // Issue priority falls with the wave's relative progress through its range
@@ -726,13 +766,24 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
       set_wave_priority(prio);
       prio_next = ((4 - prio) * count + 3) / 4;
     }
-    if (i + NS - 1 < count) {
-      stage_page<D, NG>(p, page_blk(i + NS - 1), ring_lds + slot_fill * S::kBytes, soff);
-      slot_fill = slot_fill == NS - 1 ? 0 : slot_fill + 1;
+    uint8_t* st;
+    if constexpr (CASC) {
+      // page i's copies (every wave's quarter) have landed, and every wave is
+      // done with page i - 1, whose slot now takes page i + 1
+      wait_vmem<0>();
+      __syncthreads();
+      if (i + 1 < count) stage_page_part<D>(p, page_blk(i + 1), ring_lds + ((i + 1) & 1) * S::kBytes, soff, wave);
+      st = ring + (i & 1) * S::kBytes;
+      if (!compute) continue;
+    } else {
+      if (i + NS - 1 < count) {
+        stage_page<D, NG>(p, page_blk(i + NS - 1), ring_lds + slot_fill * S::kBytes, soff);
+        slot_fill = slot_fill == NS - 1 ? 0 : slot_fill + 1;
+      }
+      wait_page<S::kCopies, NS - 1>(count - 1 - i);
+      st = ring + slot_use * S::kBytes;
+      slot_use = slot_use == NS - 1 ? 0 : slot_use + 1;
     }
-    wait_page<S::kCopies, NS - 1>(count - 1 - i);
-    uint8_t* st = ring + slot_use * S::kBytes;
-    slot_use = slot_use == NS - 1 ? 0 : slot_use + 1;
     if (!((page_ok >> i) & 1)) {
       poison = true;
       continue;
@@ -924,7 +975,7 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
     // of the B operands' halves: tokens 0, 2, 1, 3.
     // plane k of (row block, group) index rb*NG + j
     auto plane_at = [&](int k) -> uint8_t* {
-      return k < RG::kSlotPlanes ? st + k * kPlaneBytes : planes + (k - RG::kSlotPlanes) * kPlaneBytes;
+      return k < kSlotPl ? st + k * kPlaneBytes : planes + (k - kSlotPl) * kPlaneBytes;
     };
     float svk[NG][4];
 #pragma unroll
@@ -1021,6 +1072,7 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
     __builtin_amdgcn_wave_barrier();
   }
   wait_vmem<0>();
+  if constexpr (CASC) __syncthreads();   // no wave reads the shared ring or the planes any more
   set_wave_priority(3);   // the block's merge waits for this wave
 
   // ---- reduce the weight sums over the 16 lanes of each head; each head's
@@ -1230,7 +1282,7 @@ __global__ __launch_bounds__(kBlock, (scan_waves_per_simd<G, LM, NG, PACK>())) v
   // KV head), the other history splits (split, request, KV head), the prefix
   // splits of the requests past the last whole pack (split, request, KV head),
   // then the BF16 chunks
-  const int n_packed = p.n_pref * p.packs * p.n_kv;
+  const int n_packed = p.n_pref * p.pack_units * p.n_kv;
   const int n_rest = (p.splits - p.n_pref) * units;
   const int left = p.B - p.packs * p.pack;
   const int n_hist = n_packed + n_rest + p.n_pref * left * p.n_kv;
@@ -1287,6 +1339,71 @@ __global__ __launch_bounds__(kBlock, (scan_waves_per_simd<G, LM, NG, PACK>())) v
     return;
   }
 
+  if constexpr (G == 4 && PACK == 4) {
+    if (p.casc && id < n_packed) {
+      // ---- a cascade block: one split inside the shared prefix, up to four
+      // packs of four requests (wave w takes pack 4*group + w) reading every
+      // page from one staged copy
+      using S1 = Stage<D, 1>;
+      constexpr int kRing = 2 * S1::kBytes, kPlanes = 2 * kPlaneBytes;   // shared ring; each wave's planes
+      constexpr int kSlot = 16 * part_row(D) * 4;                        // each wave's 16-head merge slot
+      static_assert(kRing + 4 * kPlanes <= kSmem && 4 * kSlot <= kSmem, "cascade LDS must fit");
+      const int per_split = p.pack_units * p.n_kv;
+      const int split = id / per_split, grp_id = (id % per_split) / p.n_kv, g = id % p.n_kv;
+      const int pk = 4 * grp_id + wave;                // this wave's pack
+      const bool active = pk < p.packs;
+      const int b = 4 * pk;                            // its first request
+      const int ws0 = split * p.pps, count = p.pps;    // the whole split, inside the prefix
+      const int full = (ws0 + count) * kPage;          // every history of the group must cover it
+      const int32_t* row0 = p.block_table + (size_t)(16 * grp_id) * p.max_pages;   // the staged row
+      const int pid_lane = lane < count ? row0[ws0 + lane] : -1;
+      HistOperands<D, 16> qo;
+      bool bad = false;
+      if (active) {
+        load_pack_operands<D, 4>(p, b, g, lane, qo);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int pr = lane < count ? p.block_table[(size_t)(b + r) * p.max_pages + ws0 + lane] : -1;
+          const int hr = p.hist_len[b + r];
+          bad |= pr != pid_lane || hr < full || hr > p.max_hist_len;
+        }
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          qo.ca[nb] = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) qo.cb[nb][j] = 0.0f;
+#pragma unroll
+          for (int c = 0; c < D / 64; ++c) qo.qa[nb][c] = v4i{0, 0, 0, 0};
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      // a row that differs from the staged one, or a history ending inside the
+      // split, anywhere in the group poisons the whole group
+      const bool wave_bad = __any(bad);
+      if (lane == 0) flags[wave] = wave_bad ? 1 : 0;
+      __syncthreads();
+      poison = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
+      __syncthreads();   // flags are read before anything overlays them
+      const int n_pages = poison ? 0 : count;        // block-uniform
+      float* mw = reinterpret_cast<float*>(smem + wave * kSlot);
+      hist_wave<D, 16, false, 1, true>(p, g, ws0, n_pages, full, pid_lane, qo, smem, mw, poison, lane,
+                                      smem + kRing + wave * kPlanes, wave, active);
+      if (active) {
+        // each request's 4-head partial into its own slot: (m, l, 0, 0, acc)
+        constexpr int R = part_row(D);
+#pragma unroll 4
+        for (int e = lane; e < 16 * R; e += kWave) {
+          const int h = e / R, k = e - h * R;
+          const float v = mw[e];
+          float* dst = p.hpart + (((size_t)(b + h / 4) * p.n_kv + g) * p.splits + split) * (size_t)4 * R +
+                       (size_t)(h % 4) * R + k;
+          *dst = (k == 1) ? (poison ? NAN : v) : (k < kPartAcc && k > 1) ? 0.0f : v;
+        }
+      }
+      return;
+    }
+  }
   if constexpr (G == 4) {
     if (id < n_packed) {
       // ---- a split inside the shared prefix for requests b .. b+PACK-1: one
@@ -1553,13 +1670,13 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(DecodeDev p, int n_merge,
   }
 }
 
-// ---- BF16 paged comparator ---------------------------------------------
-// One (request, KV head) per block, for launches whose heads have at most
-// kUnitRound partials each (large batches, few splits): the R_V rows are
-// loaded once for the unit's G heads rather than once per head, and every
-// partial of every head is requested in one round.  Thread (h, q) owns
-// channels 4q..4q+3 of head h.
+// One (request, KV head) per block, for launches whose heads have few partials
+// each (large batches, few splits): the R_V rows are loaded once for the
+// unit's G heads rather than once per head, and the partials of every head are
+// requested kUnitRound at a time (one round up to 16 partials), the rounds
+// combined online.  Thread (h, q) owns channels 4q..4q+3 of head h.
 constexpr int kUnitRound = 16;
+constexpr int kUnitMaxParts = 4 * kUnitRound;
 
 template <int D, int G>
 __global__ __launch_bounds__(kBlock) void merge_unit_kernel(DecodeDev p, int n_merge, DemoteDev dk, DemoteDev dv) {
@@ -1584,31 +1701,43 @@ __global__ __launch_bounds__(kBlock) void merge_unit_kernel(DecodeDev p, int n_m
   const float* bb = p.bpart + (size_t)unit * p.chunks * stride;
   if (tid < G * QPR) {
     const int h = tid / QPR, q = tid % QPR;
-    float2 ml[kUnitRound];
-    float4 av[kUnitRound];
-#pragma unroll
-    for (int s = 0; s < kUnitRound; ++s) {
-      if (s < nt) {
-        const float* pp = (s < n ? hb + (size_t)s * stride : bb + (size_t)(s - n) * stride) + h * R;
-        ml[s] = *reinterpret_cast<const float2*>(pp);
-        av[s] = *reinterpret_cast<const float4*>(pp + kPartAcc + 4 * q);
-      } else {
-        ml[s] = make_float2(-INFINITY, 0.0f);
-        av[s] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      }
-    }
-    float M = -INFINITY;
-#pragma unroll
-    for (int s = 0; s < kUnitRound; ++s) M = fmaxf(M, ml[s].x);
-    float L = 0.0f;
+    float M = -INFINITY, L = 0.0f;
     float4 ar = make_float4(0.0f, 0.0f, 0.0f, 0.0f), ap = ar;
+    for (int s0 = 0; s0 < nt; s0 += kUnitRound) {
+      float2 ml[kUnitRound];
+      float4 av[kUnitRound];
 #pragma unroll
-    for (int s = 0; s < kUnitRound; ++s) {
-      const float f = exp2_or_zero(ml[s].x, M);
-      const float fr = s < n ? f : 0.0f;   // history partials are still rotated
-      L = fmaf(f, ml[s].y, L);
-      ar = f4_fma(fr, av[s], ar);
-      ap = f4_fma(f - fr, av[s], ap);
+      for (int k = 0; k < kUnitRound; ++k) {
+        const int s = s0 + k;
+        if (s < nt) {
+          const float* pp = (s < n ? hb + (size_t)s * stride : bb + (size_t)(s - n) * stride) + h * R;
+          ml[k] = *reinterpret_cast<const float2*>(pp);
+          av[k] = *reinterpret_cast<const float4*>(pp + kPartAcc + 4 * q);
+        } else {
+          ml[k] = make_float2(-INFINITY, 0.0f);
+          av[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+      }
+      // the round's maximum; the sums so far move to it (on the first round M
+      // is -inf and they are still zero)
+      float Mr = M;
+#pragma unroll
+      for (int k = 0; k < kUnitRound; ++k) Mr = fmaxf(Mr, ml[k].x);
+      if (s0 > 0) {
+        const float c = exp2_or_zero(M, Mr);
+        L *= c;
+        ar = f4_fma(c, ar, make_float4(0.0f, 0.0f, 0.0f, 0.0f));
+        ap = f4_fma(c, ap, make_float4(0.0f, 0.0f, 0.0f, 0.0f));
+      }
+      M = Mr;
+#pragma unroll
+      for (int k = 0; k < kUnitRound; ++k) {
+        const float f = exp2_or_zero(ml[k].x, M);
+        const float fr = s0 + k < n ? f : 0.0f;   // history partials are still rotated
+        L = fmaf(f, ml[k].y, L);
+        ar = f4_fma(fr, av[k], ar);
+        ap = f4_fma(f - fr, av[k], ap);
+      }
     }
     *reinterpret_cast<float4*>(&arot[h][4 * q]) = ar;
     *reinterpret_cast<float4*>(&aplain[h][4 * q]) = ap;
@@ -1635,7 +1764,10 @@ __global__ __launch_bounds__(kBlock) void merge_unit_kernel(DecodeDev p, int n_m
 template <int D>
 bool launch_merge_unit(const DecodeDev& dv, unsigned n_dem, const DemoteDev& mk, const DemoteDev& mv,
                        hipStream_t stream) {
-  if (dv.splits + dv.chunks > kUnitRound || dv.G * (D / 4) > kBlock) return false;
+  // one round, or several when the batch gives every compute unit a block of its own
+  const int parts = dv.splits + dv.chunks;
+  if (dv.G * (D / 4) > kBlock || parts > kUnitMaxParts) return false;
+  if (parts > kUnitRound && (long)dv.B * dv.n_kv < 128) return false;
   const int units = dv.B * dv.n_kv;
   const unsigned grid = (unsigned)units + n_dem;
   switch (dv.G) {
@@ -1660,6 +1792,7 @@ void launch_merge(const DecodeDev& dv, const DemoteDev& mk, const DemoteDev& mv,
   if (n_merge + n_dem > 0) merge_kernel<D><<<(unsigned)n_merge + n_dem, kBlock, 0, stream>>>(dv, n_merge, mk, mv);
 }
 
+// ---- BF16 paged comparator ---------------------------------------------
 template <int D, int G>
 __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : 2)) void bf16_paged_kernel(Bf16Dev p) {
   constexpr int kWaveLds = bf16_lds_bytes<D, G>();
@@ -1723,7 +1856,7 @@ __global__ __launch_bounds__(kBlock) void merge_plain_kernel(Bf16Dev p) {
 template <int D, int G>
 void launch_main(const DecodeDev& dv, hipStream_t stream) {
   const long units = (long)dv.B * dv.n_kv;
-  const long blocks = (long)dv.n_pref * dv.packs * dv.n_kv + (long)(dv.splits - dv.n_pref) * units +
+  const long blocks = (long)dv.n_pref * dv.pack_units * dv.n_kv + (long)(dv.splits - dv.n_pref) * units +
                       (long)dv.n_pref * (dv.B - dv.packs * dv.pack) * dv.n_kv + units * dv.bf_blocks;
   if (blocks == 0) return;
   const dim3 grid((unsigned)blocks);
@@ -1834,6 +1967,9 @@ DecodeDev make_dev(const oscar_decode_args& a, const DecodePlan& plan, char* ws)
   dv.packs = a.batch / dv.pack;
   dv.n_pref = (dv.G == 4 && dv.packs > 0 && plan.splits > 0) ? std::min(plan.splits, a.shared_pages / plan.pages_per_split)
                                                             : 0;
+  // the cascade's plan keeps splits within 64 pages (abi.hip plans with decode_cascade too)
+  dv.casc = quad && decode_cascade(a) && dv.n_pref > 0 && plan.pages_per_split <= kCascadeMaxPagesPerSplit ? 1 : 0;
+  dv.pack_units = dv.casc ? (dv.packs + 3) / 4 : dv.packs;
   dv.sm_log2 = a.sm_scale * kLog2e;
   dv.n_pages = a.n_pages;
   dv.q = a.q; dv.sink_k = a.sink_k; dv.sink_v = a.sink_v; dv.recent_k = a.recent_k; dv.recent_v = a.recent_v;

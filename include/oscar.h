@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define OSCAR_ABI_VERSION 4
+#define OSCAR_ABI_VERSION 5
 #define OSCAR_PAGE_TOKENS 64
 
 #ifndef OSCAR_API
@@ -198,17 +198,29 @@ typedef struct oscar_decode_args {
                                64*shared_pages <= max_hist_len).  A prefix cache makes such
                                tables.  With n_q_heads/n_kv_heads = 4 the scan then reads
                                the history splits that lie inside the prefix once for each
-                               pair of requests (0,1), (2,3), ... (8 query heads per KV
-                               head and page instead of 4); other group sizes ignore it.
-                               For each pair the scan checks the pages it reads for both:
-                               if the two rows' ids differ there, or either history ends
-                               before them, both requests' output rows are NaN.        */
+                               pack of requests: four (4i .. 4i+3; uniform codebook,
+                               whole-head groups, head_dim 128, batch >= 4) or two (2i,
+                               2i+1) per pack.  Other group sizes ignore it.  The scan
+                               checks the pages it reads for every request of a pack (of
+                               a cascade group, below): if a row's ids differ there from
+                               the others', or a history ends before them, every output
+                               row of that pack (group) is NaN.                         */
   int32_t codebook;         /* OSCAR_CODEBOOK_UNIFORM or OSCAR_CODEBOOK_LLOYD_MAX: the
                                codebook the pools were demoted with (a decode step also
                                demotes with it)                                        */
   int32_t group_channels;   /* 0 (a group is the whole head), 64 (OSCAR_GROUPS_64 pools)
                                or 32 (OSCAR_GROUPS_32 pools); a decode step demotes with
                                the same groups                                         */
+  int32_t prefix_cascade;   /* 0 or 1 (else OSCAR_EINVAL).  1: where the packs above
+                               apply with four requests, batch >= 16 and shared_pages >=
+                               64, the splits inside the prefix run as cascade blocks
+                               instead: each page of such a split is read once for a
+                               group of up to four packs (requests 16i .. 16i+15), whose
+                               rows the block's four waves score from that one copy
+                               (splits of at most 64 pages).  Ignored elsewhere.  Same
+                               results as 0 up to rounding order; it cuts the page reads
+                               of the prefix by up to four but makes more history splits
+                               for the merge to combine.                                */
 } oscar_decode_args;
 
 /* Workspace bytes oscar_decode_attn needs for these sizes (0 on invalid sizes).

@@ -61,7 +61,7 @@ def oracle_pools(cfg: dict):
 
 
 def gpu_decode(cfg: dict, pools, *, block_table=None, hist_len=None, sink_len=None, recent_len=None,
-               max_hist_len=None, reps: int = 1, shared_pages: int = 0) -> np.ndarray:
+               max_hist_len=None, reps: int = 1, shared_pages: int = 0, prefix_cascade: bool = False) -> np.ndarray:
     kc, vc, ks, vs = (p if isinstance(p, torch.Tensor) else dev(p) for p in pools)
     q = dev(cfg["q"])
     B, Hq, d = cfg["q"].shape
@@ -80,7 +80,7 @@ def gpu_decode(cfg: dict, pools, *, block_table=None, hist_len=None, sink_len=No
                 block_table=dev(table), r_k=dev(cfg["r_k"]), r_v=dev(cfg["r_v"]), out=out, workspace=ws,
                 sm_scale=float(cfg["sm_scale"]), shared_pages=shared_pages,
                 codebook=CODEBOOK_FLAG[cfg.get("codebook", "uniform")],
-                group_channels=int(cfg.get("group_channels", 0)))
+                group_channels=int(cfg.get("group_channels", 0)), prefix_cascade=prefix_cascade)
     for _ in range(reps):
         hip.oscar_decode_attn(**args)
     torch.cuda.synchronize()

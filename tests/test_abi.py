@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
     L = hip.lib()
     for n in declared_functions():
         assert hasattr(L, n), n
-    assert hip.oscar_abi_version() == hip.ABI_VERSION == 4
+    assert hip.oscar_abi_version() == hip.ABI_VERSION == 5
     # the binding offers a function of the same name for each entry point
     for n in declared_functions():
         assert callable(getattr(hip, n)), n
@@ -100,6 +100,8 @@ def _decode_args(**kw):
     (dict(codebook=1), hip.OSCAR_EINVAL),
     (dict(group_channels=16), hip.OSCAR_EINVAL),
     (dict(group_channels=48), hip.OSCAR_EINVAL),
+    (dict(prefix_cascade=2), hip.OSCAR_EINVAL),
+    (dict(prefix_cascade=-1), hip.OSCAR_EINVAL),
     (dict(batch=0, q=None, out=None), hip.OSCAR_OK),
 ])
 def test_decode_validation(kw, status):

@@ -67,6 +67,29 @@ def test_large_batch_merge(G, d):
     compare_out(got, ref, what=f"large batch G={G} d={d}")
 
 
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_merge_in_rounds(G):
+    """16 requests x 8 KV heads (128 merge units) with a 1024-token recent
+    window: 16 BF16 chunks, one sink chunk and the history splits give every
+    head more partials than one round of the per-unit merge takes, so they are
+    combined in two rounds online (rotated history partials in the first,
+    plain chunk partials in both).  Ragged segments, an empty history and an
+    empty context among them."""
+    rng = np.random.default_rng(95 + G)
+    B = 16
+    hist = [int(x) for x in rng.integers(1, 900, size=B)]
+    sink = [int(x) for x in rng.integers(0, 65, size=B)]
+    recent = [int(x) for x in rng.integers(0, 1025, size=B)]
+    hist[2] = 0
+    sink[7], hist[7], recent[7] = 0, 0, 0
+    cfg, pools = ragged_cache(110 + G, B=B, n_kv=8, G=G, d=128, sink=tuple(sink), hist=tuple(hist),
+                              recent=tuple(recent), recent_cap=1024)
+    ref = oracle.decode_attn_ref(cfg, *pools)
+    got = gpu_decode(cfg, pools)
+    assert not got[7].any()
+    compare_out(got, ref, what=f"merge in rounds G={G}")
+
+
 @pytest.mark.parametrize("log2_scale", [-100, 0, 64])
 def test_query_scale_extremes(log2_scale):
     """q scaled by a power of two far from 1 (exact in bf16): the fixed-point

@@ -9,9 +9,10 @@
   history and the bulk workload), and the 100k layer's decode over
   oracle-quantised grouped pools, every head.
 * The 28-request, 100k-context layer with its 1406-page shared prefix
-  declared to the scan (packs of four requests read each shared split once):
-  all 32 query heads of four requests (the first and the last, and two
-  members of one pack) against the oracle over oracle-quantised pages.  The private
+  declared to the scan (packs of four requests read each shared split once),
+  and the same with the prefix in cascade blocks (groups of 16 requests): all
+  32 query heads of four requests (the first and the last, and two members of
+  one pack) against the oracle over oracle-quantised pages.  The private
   pages of the other requests hold random codes; their rows are checked to
   be finite."""
 import numpy as np
@@ -103,6 +104,8 @@ def test_batch28_shared_prefix_four_requests_all_heads():
         pools.append((c, s))
     pools = (pools[0][0], pools[1][0], pools[0][1], pools[1][1])
     got = gpu_decode(cfg, pools, shared_pages=shared)
+    casc = gpu_decode(cfg, pools, shared_pages=shared, prefix_cascade=True)
     ref = oracle.decode_attn_ref(cfg, *pools, heads=[(b, h) for b in check for h in range(cfg["n_q_heads"])])
     compare_out(got[check], ref[check], what="28 x 100k, four requests, all heads")
-    assert np.all(np.isfinite(got))
+    compare_out(casc[check], ref[check], what="28 x 100k in cascade blocks, four requests, all heads")
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(casc))

@@ -1,11 +1,13 @@
 """Shared-prefix packing of the history scan (group size 4): the splits that
 lie inside a declared shared prefix are read once for each pack of requests,
 four per wave (uniform codebook, whole-head groups, d = 128, batches of four
-or more) or two per wave (otherwise).  Parity with the oracle on ragged
+or more) or two per wave (otherwise); on request (prefix_cascade), with
+sixteen requests or more and a prefix of at least 64 pages, once for each
+group of up to four packs (cascade blocks).  Parity with the oracle on ragged
 private parts, requests past the last whole pack and two split partitions;
 the pack checks (rows that differ inside the prefix, a history shorter than
-the prefix) that turn exactly that pack's rows into NaN; and group sizes that
-ignore the declaration."""
+the prefix) that turn exactly that pack's rows into NaN; and group sizes and
+sizes that ignore the declaration or the request."""
 import numpy as np
 import pytest
 
@@ -131,3 +133,50 @@ def test_short_history_poisons_the_quad():
     got = gpu_decode(cfg, pools, hist_len=hl, shared_pages=13)
     assert np.all(np.isnan(got[:4]))
     compare_out(got[4:], ref[4:], what="request outside the quad")
+
+
+@pytest.mark.parametrize("B", [16, 19, 24])
+def test_prefix_cascade_matches_oracle(B):
+    """Sixteen requests or more with a prefix of at least 64 pages: the splits
+    inside it run as cascade blocks, each page staged once for a group of up
+    to four packs (16 requests).  B = 19 leaves three requests past the last
+    whole pack; B = 24 gives a second group with two packs and two idle waves.
+    Without the request the same launch reads the prefix in packs."""
+    cfg, pools = prefix_cache(50 + B, B, 4, 128, hist_pages=80, shared=70)
+    ref = oracle.decode_attn_ref(cfg, *pools)
+    compare_out(gpu_decode(cfg, pools, shared_pages=70, prefix_cascade=True), ref, what=f"cascade B={B}")
+    compare_out(gpu_decode(cfg, pools, shared_pages=70), ref, what=f"packs B={B}")
+
+
+@pytest.mark.parametrize("B,shared,codebook", [(15, 70, "uniform"), (16, 63, "uniform"), (16, 70, "lloyd_max")])
+def test_cascade_request_ignored_where_it_does_not_apply(B, shared, codebook):
+    """Fewer than 16 requests, a prefix shorter than one cascade split, or the
+    Lloyd-Max codebook: the request changes nothing, bit for bit."""
+    cfg, pools = prefix_cache(70 + B + shared, B, 4, 128, hist_pages=80, shared=shared)
+    if codebook != "uniform":
+        from gpu_util import oracle_pools as pools_of
+        cfg["codebook"] = codebook
+        pools = pools_of(cfg)
+    base = gpu_decode(cfg, pools, shared_pages=shared)
+    compare_out(base, oracle.decode_attn_ref(cfg, *pools), what=f"B={B} shared={shared} {codebook}")
+    assert np.array_equal(gpu_decode(cfg, pools, shared_pages=shared, prefix_cascade=True), base)
+
+
+def test_mismatched_row_poisons_the_cascade_group():
+    cfg, pools = prefix_cache(60, 20, 4, 128, hist_pages=80, shared=70)
+    ref = oracle.decode_attn_ref(cfg, *pools)
+    table = cfg["block_table"].copy()
+    table[6, 30] = table[6, 75]                  # request 6 (group 0) leaves the prefix at page 30
+    got = gpu_decode(cfg, pools, block_table=table, shared_pages=70, prefix_cascade=True)
+    assert np.all(np.isnan(got[:16]))
+    compare_out(got[16:], ref[16:], what="requests outside the poisoned group")
+
+
+def test_short_history_poisons_the_cascade_group():
+    cfg, pools = prefix_cache(61, 20, 4, 128, hist_pages=80, shared=70)
+    ref = oracle.decode_attn_ref(cfg, *pools)
+    hl = cfg["hist_len"].copy()
+    hl[17] = 64 * 70 - 5                         # request 17 (group 1: requests 16-19) ends inside the prefix
+    got = gpu_decode(cfg, pools, hist_len=hl, shared_pages=70, prefix_cascade=True)
+    assert np.all(np.isnan(got[16:]))
+    compare_out(got[:16], ref[:16], what="requests outside the poisoned group")
