@@ -680,7 +680,7 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
   constexpr int NS = RG::kStages;
   constexpr int GC = D / NG;    // channels per (scale, zero) group
   static_assert(NG == 1 || NG == 2 || (NG == 4 && D == 128), "groups of the head, 64 or 32 channels");
-  static_assert(!CASC || (NG == 1 && !LM), "cascade blocks: uniform codebook, whole-head groups");
+  static_assert(!CASC || (NG == 1 && !LM && NS == 2), "cascade blocks: uniform codebook, whole-head groups");
   constexpr int kSlotPl = CASC ? 0 : RG::kSlotPlanes;                          // planes in the page slot
   constexpr int kOwnPlaneBytes = CASC ? PB * NG * kPlaneBytes : RG::kPlaneLds;   // planes of its own
   const int n = lane & 15, grp = lane >> 4;
