@@ -96,7 +96,8 @@ oscar_status check_decode(const oscar_decode_args* a, void* workspace, size_t wo
   if (a->prefix_cascade != 0 && a->prefix_cascade != 1) return OSCAR_EINVAL;
   *plan = make_decode_plan(a->batch, a->n_q_heads, a->n_kv_heads, a->head_dim, a->max_hist_len,
                            a->sink_cap, a->recent_cap, scan_resident_blocks(*a),
-                           decode_cascade(*a) ? kCascadeMaxPagesPerSplit : kMaxPagesPerSplit);
+                           decode_cascade(*a) ? kCascadeMaxPagesPerSplit : kMaxPagesPerSplit,
+                           quad_packs(*a) && a->shared_pages > 0 && !decode_cascade(*a));
   if (a->batch == 0) return OSCAR_OK;
   if (!a->q || !a->out || !a->sink_len || !a->recent_len || !a->hist_len) return OSCAR_EINVAL;
   if (a->sink_cap > 0 && (!a->sink_k || !a->sink_v)) return OSCAR_EINVAL;

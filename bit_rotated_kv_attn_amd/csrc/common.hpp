@@ -176,13 +176,29 @@ __host__ __device__ constexpr int part_row(int d) { return d + kPartAcc; }
 // hold at most 64 pages.
 constexpr int kCascadeMaxPagesPerSplit = 64;
 
-// resident: scan blocks resident at once; max_pps: pages per split at most.
-// The workspace query plans with the largest count and the smallest cap any
-// launch of these sizes can use, so its splits and workspace bound every other
-// plan's.
+// Partials of a head the per-unit merge requests in one round.
+constexpr int kUnitRound = 16;
+
+// Splits a launch that reads its shared prefix in packs of four requests takes
+// at least: enough that the pack blocks of the prefix splits alone come near
+// the resident blocks, so the packed waves, the longest of the launch, spread
+// over every compute unit and end together; at most as many as keep every
+// head's partials (history splits and BF16 chunks) within one merge round.
+inline long pack_min_splits(int B, int n_kv, int chunks, long resident) {
+  const long units = (long)(B / 4) * n_kv;   // pack blocks per prefix split
+  if (units <= 0) return 0;
+  const long want = (resident + units - 1) / units, cap = kUnitRound - chunks;
+  return want < cap ? want : cap;
+}
+
+// resident: scan blocks resident at once; max_pps: pages per split at most;
+// quad_prefix: the launch packs a shared prefix four requests at a time.  The
+// workspace query plans with the largest count, the smallest cap and packing
+// that any launch of these sizes can use, so its splits and workspace bound
+// every other plan's.
 inline DecodePlan make_decode_plan(int B, int Hq, int n_kv, int d, int max_hist_len, int sink_cap,
                                    int recent_cap, long resident = kMaxResidentBlocks,
-                                   int max_pps = kMaxPagesPerSplit) {
+                                   int max_pps = kMaxPagesPerSplit, bool quad_prefix = false) {
   DecodePlan p{};
   const int G = Hq / n_kv;
   const int NB = (G + 3) / 4;
@@ -196,6 +212,7 @@ inline DecodePlan make_decode_plan(int B, int Hq, int n_kv, int d, int max_hist_
     long s0 = (target + units - 1) / units;
     const long s_min = (p.hist_pages + max_pps - 1) / max_pps;
     if (s0 < s_min) s0 = s_min;
+    if (quad_prefix && s0 < pack_min_splits(B, n_kv, p.chunks, resident)) s0 = pack_min_splits(B, n_kv, p.chunks, resident);
     if (s0 > p.hist_pages) s0 = p.hist_pages;
     p.pages_per_split = (int)((p.hist_pages + s0 - 1) / s0);
     p.splits = (p.hist_pages + p.pages_per_split - 1) / p.pages_per_split;
@@ -256,6 +273,14 @@ hipError_t launch_decode_bf16(const oscar_bf16_decode_args& a, const Bf16Plan& p
 // once: kResidentBlocks scaled by its blocks per compute unit (two or one)
 long scan_resident_blocks(const oscar_decode_args& a);
 
+// Whether a launch reads its declared shared prefix in packs of four requests
+// (else two): group size 4, head_dim 128, the uniform codebook, whole-head
+// groups and four or more requests.
+inline bool quad_packs(const oscar_decode_args& a) {
+  return a.batch >= 4 && a.n_kv_heads > 0 && a.n_q_heads == 4 * a.n_kv_heads && a.head_dim == 128 &&
+         a.codebook == OSCAR_CODEBOOK_UNIFORM && (a.group_channels == 0 || a.group_channels >= a.head_dim);
+}
+
 // Whether a launch with these (validated) args reads its shared prefix in
 // cascade blocks, and whether any launch of these sizes can (the workspace
 // query's bound): group size 4, head_dim 128, 16 or more requests; the launch
@@ -266,8 +291,9 @@ inline bool cascade_sizes(int batch, int n_q_heads, int n_kv_heads, int head_dim
 }
 // the plan of the workspace query: the most splits any launch of these sizes can use
 inline DecodePlan sizing_plan(int B, int Hq, int n_kv, int d, int max_hist_len, int sink_cap, int recent_cap) {
+  const bool quad_sizes = B >= 4 && n_kv > 0 && Hq == 4 * n_kv && d == 128;
   return make_decode_plan(B, Hq, n_kv, d, max_hist_len, sink_cap, recent_cap, kMaxResidentBlocks,
-                          cascade_sizes(B, Hq, n_kv, d) ? kCascadeMaxPagesPerSplit : kMaxPagesPerSplit);
+                          cascade_sizes(B, Hq, n_kv, d) ? kCascadeMaxPagesPerSplit : kMaxPagesPerSplit, quad_sizes);
 }
 inline bool decode_cascade(const oscar_decode_args& a) {
   return a.prefix_cascade == 1 && cascade_sizes(a.batch, a.n_q_heads, a.n_kv_heads, a.head_dim) &&

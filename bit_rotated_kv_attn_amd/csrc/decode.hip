@@ -1675,7 +1675,6 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(DecodeDev p, int n_merge,
 // unit's G heads rather than once per head, and the partials of every head are
 // requested kUnitRound at a time (one round up to 16 partials), the rounds
 // combined online.  Thread (h, q) owns channels 4q..4q+3 of head h.
-constexpr int kUnitRound = 16;
 constexpr int kUnitMaxParts = 4 * kUnitRound;
 
 template <int D, int G>
@@ -1962,7 +1961,7 @@ DecodeDev make_dev(const oscar_decode_args& a, const DecodePlan& plan, char* ws)
   // more requests): four requests per wave with the uniform codebook and
   // whole-head groups at d = 128 (the 16-head wave fits two per SIMD there),
   // else two
-  const bool quad = a.batch >= 4 && dv.lm == 0 && dv.ng == 1 && a.head_dim == 128;
+  const bool quad = quad_packs(a);
   dv.pack = quad ? 4 : 2;
   dv.packs = a.batch / dv.pack;
   dv.n_pref = (dv.G == 4 && dv.packs > 0 && plan.splits > 0) ? std::min(plan.splits, a.shared_pages / plan.pages_per_split)

@@ -176,7 +176,7 @@ def test_short_history_poisons_the_cascade_group():
     cfg, pools = prefix_cache(61, 20, 4, 128, hist_pages=80, shared=70)
     ref = oracle.decode_attn_ref(cfg, *pools)
     hl = cfg["hist_len"].copy()
-    hl[17] = 64 * 70 - 5                         # request 17 (group 1: requests 16-19) ends inside the prefix
+    hl[17] = 64 * 30 - 5                         # request 17 (group 1: requests 16-19) ends inside the prefix
     got = gpu_decode(cfg, pools, hist_len=hl, shared_pages=70, prefix_cascade=True)
     assert np.all(np.isnan(got[16:]))
     compare_out(got[:16], ref[:16], what="requests outside the poisoned group")
