@@ -1278,14 +1278,19 @@ __global__ __launch_bounds__(kBlock, (scan_waves_per_simd<G, LM, NG, PACK>())) v
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int units = p.B * p.n_kv;
   const int id = blockIdx.x;
-  // block ids: the shared-prefix splits read for request packs (split, pack,
-  // KV head), the other history splits (split, request, KV head), the prefix
-  // splits of the requests past the last whole pack (split, request, KV head),
-  // then the BF16 chunks
+  // block ids: the history splits past the shared prefix (split, request, KV
+  // head), the prefix splits read for request packs (split, pack, KV head),
+  // the prefix splits of the requests past the last whole pack (split,
+  // request, KV head), then the BF16 chunks.  The per-request splits come
+  // first: they take the first round of resident slots beside pack blocks and
+  // end early, and the pack blocks, the longest of the launch, follow into
+  // their slots (dispatched the other way round, the per-request splits ran
+  // after the pack blocks, at one wave per SIMD)
   const int n_packed = p.n_pref * p.pack_units * p.n_kv;
   const int n_rest = (p.splits - p.n_pref) * units;
   const int left = p.B - p.packs * p.pack;
   const int n_hist = n_packed + n_rest + p.n_pref * left * p.n_kv;
+  const int pid = id - n_rest;   // index among the pack (or cascade) blocks
   bool poison = false;
 
   if (id >= n_hist) {
@@ -1340,7 +1345,7 @@ __global__ __launch_bounds__(kBlock, (scan_waves_per_simd<G, LM, NG, PACK>())) v
   }
 
   if constexpr (G == 4 && PACK == 4) {
-    if (p.casc && id < n_packed) {
+    if (p.casc && id >= n_rest && pid < n_packed) {
       // ---- a cascade block: one split inside the shared prefix, up to four
       // packs of four requests (wave w takes pack 4*group + w) reading every
       // page from one staged copy
@@ -1349,7 +1354,7 @@ __global__ __launch_bounds__(kBlock, (scan_waves_per_simd<G, LM, NG, PACK>())) v
       constexpr int kSlot = 16 * part_row(D) * 4;                        // each wave's 16-head merge slot
       static_assert(kRing + 4 * kPlanes <= kSmem && 4 * kSlot <= kSmem, "cascade LDS must fit");
       const int per_split = p.pack_units * p.n_kv;
-      const int split = id / per_split, grp_id = (id % per_split) / p.n_kv, g = id % p.n_kv;
+      const int split = pid / per_split, grp_id = (pid % per_split) / p.n_kv, g = pid % p.n_kv;
       const int pk = 4 * grp_id + wave;                // this wave's pack
       const bool active = pk < p.packs;
       const int b = 4 * pk;                            // its first request
@@ -1405,14 +1410,14 @@ __global__ __launch_bounds__(kBlock, (scan_waves_per_simd<G, LM, NG, PACK>())) v
     }
   }
   if constexpr (G == 4) {
-    if (id < n_packed) {
+    if (id >= n_rest && pid < n_packed) {
       // ---- a split inside the shared prefix for requests b .. b+PACK-1: one
       // 4*PACK-head wave reads each page once for all of them
       constexpr int GP = 4 * PACK;
       using RP = Ring<D, PACK, NG>;
       static_assert(GP * part_row(D) * 4 <= RP::kWaveBytes, "merge slot must fit in the wave's ring");
       const int per_split = p.packs * p.n_kv;
-      const int split = id / per_split, pk = (id % per_split) / p.n_kv, g = id % p.n_kv;
+      const int split = pid / per_split, pk = (pid % per_split) / p.n_kv, g = pid % p.n_kv;
       const int b = PACK * pk;
       const int per_wave = (p.pps + 3) / 4;
       const int ws0 = split * p.pps + wave * per_wave;
@@ -1452,8 +1457,8 @@ __global__ __launch_bounds__(kBlock, (scan_waves_per_simd<G, LM, NG, PACK>())) v
 
   // ---- INT2 history split of one request: waves take contiguous page ranges
   int b, g, split;
-  if (id < n_packed + n_rest) {
-    const int j = id - n_packed, unit = j % units;
+  if (id < n_rest) {
+    const int j = id, unit = j % units;
     split = p.n_pref + j / units;
     b = unit / p.n_kv;
     g = unit % p.n_kv;
