@@ -31,9 +31,10 @@
 //                           operands
 //   2. decode_main_kernel   one grid: INT2 history splits (those inside a
 //                           declared shared prefix read once per pack of
-//                           two or four requests), then the BF16 sink /
-//                           recent chunks; each
-//                           block writes an (m, l, acc) partial per head
+//                           two or four requests, or on request once per
+//                           group of up to four packs in cascade blocks),
+//                           then the BF16 sink / recent chunks; each block
+//                           writes an (m, l, acc) partial per head
 //   3. merge_kernel         LSE merge of the history partials, * R_V^T, LSE merge
 //      (merge_unit_kernel)  with the BF16 partials, normalise (one block per
 //                           head, or per (request, KV head) in large batches);
