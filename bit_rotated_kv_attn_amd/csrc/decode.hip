@@ -1280,18 +1280,20 @@ __global__ __launch_bounds__(kBlock, (scan_waves_per_simd<G, LM, NG, PACK>())) v
   const int units = p.B * p.n_kv;
   const int id = blockIdx.x;
   // block ids: the history splits past the shared prefix (split, request, KV
-  // head), the prefix splits read for request packs (split, pack, KV head),
-  // the prefix splits of the requests past the last whole pack (split,
+  // head) and the prefix splits read for request packs (split, pack, KV head),
+  // then the prefix splits of the requests past the last whole pack (split,
   // request, KV head), then the BF16 chunks.  The per-request splits come
-  // first: they take the first round of resident slots beside pack blocks and
-  // end early, and the pack blocks, the longest of the launch, follow into
-  // their slots (dispatched the other way round, the per-request splits ran
-  // after the pack blocks, at one wave per SIMD)
+  // before the pack blocks: they take the first round of resident slots
+  // beside pack blocks and end early, and the pack blocks, the longest of the
+  // launch, follow into their slots (dispatched the other way round, the
+  // per-request splits ran after the pack blocks, at one wave per SIMD).
+  // Cascade blocks, fewer and longer still, come first.
   const int n_packed = p.n_pref * p.pack_units * p.n_kv;
   const int n_rest = (p.splits - p.n_pref) * units;
   const int left = p.B - p.packs * p.pack;
   const int n_hist = n_packed + n_rest + p.n_pref * left * p.n_kv;
-  const int pid = id - n_rest;   // index among the pack (or cascade) blocks
+  const int rest0 = p.casc ? n_packed : 0;   // first id of the per-request splits
+  const int pid = id - (p.casc ? 0 : n_rest);   // index among the pack (or cascade) blocks
   bool poison = false;
 
   if (id >= n_hist) {
@@ -1346,7 +1348,7 @@ __global__ __launch_bounds__(kBlock, (scan_waves_per_simd<G, LM, NG, PACK>())) v
   }
 
   if constexpr (G == 4 && PACK == 4) {
-    if (p.casc && id >= n_rest && pid < n_packed) {
+    if (p.casc && id < n_packed) {
       // ---- a cascade block: one split inside the shared prefix, up to four
       // packs of four requests (wave w takes pack 4*group + w) reading every
       // page from one staged copy
@@ -1411,7 +1413,7 @@ __global__ __launch_bounds__(kBlock, (scan_waves_per_simd<G, LM, NG, PACK>())) v
     }
   }
   if constexpr (G == 4) {
-    if (id >= n_rest && pid < n_packed) {
+    if (pid >= 0 && pid < n_packed) {
       // ---- a split inside the shared prefix for requests b .. b+PACK-1: one
       // 4*PACK-head wave reads each page once for all of them
       constexpr int GP = 4 * PACK;
@@ -1458,8 +1460,8 @@ __global__ __launch_bounds__(kBlock, (scan_waves_per_simd<G, LM, NG, PACK>())) v
 
   // ---- INT2 history split of one request: waves take contiguous page ranges
   int b, g, split;
-  if (id < n_rest) {
-    const int j = id, unit = j % units;
+  if (id >= rest0 && id < rest0 + n_rest) {
+    const int j = id - rest0, unit = j % units;
     split = p.n_pref + j / units;
     b = unit / p.n_kv;
     g = unit % p.n_kv;
