@@ -90,6 +90,27 @@ def test_merge_in_rounds(G):
     compare_out(got, ref, what=f"merge in rounds G={G}")
 
 
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("d", [64, 128])
+def test_many_units_every_group_size(G, d):
+    """16 requests x 8 KV heads (128 units, the per-unit merge where its
+    block holds the unit's heads) for every group size and both head dims.
+    Ragged segments, an empty history and an empty context."""
+    rng = np.random.default_rng(130 + G + d)
+    B = 16
+    hist = [int(x) for x in rng.integers(1, 400, size=B)]
+    sink = [int(x) for x in rng.integers(0, 65, size=B)]
+    recent = [int(x) for x in rng.integers(0, 257, size=B)]
+    hist[4] = 0
+    sink[9], hist[9], recent[9] = 0, 0, 0
+    cfg, pools = ragged_cache(140 + G + d, B=B, n_kv=8, G=G, d=d, sink=tuple(sink), hist=tuple(hist),
+                              recent=tuple(recent))
+    ref = oracle.decode_attn_ref(cfg, *pools)
+    got = gpu_decode(cfg, pools)
+    assert not got[9].any()
+    compare_out(got, ref, what=f"128 units G={G} d={d}")
+
+
 @pytest.mark.parametrize("log2_scale", [-100, 0, 64])
 def test_query_scale_extremes(log2_scale):
     """q scaled by a power of two far from 1 (exact in bf16): the fixed-point
