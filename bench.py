@@ -428,7 +428,7 @@ def bulk_demotion(args, tm):
     del g, x, pools
     return {"config": {"workload": cfg["name"], "tokens": n_tok, "n_kv_heads": n_kv, "head_dim": d,
                        "group_channels": args.groups, "tensors": "K and V, one oscar_quantize_pack call each",
-                       "kernel": "quantize_mfma_kernel (certified fast pass) + quantize_exact_kernel (marked tokens)"},
+                       "kernel": "quantize_mfma_kernel (certified fast pass, then each block's marked tokens exactly)"},
             "us_per_tensor": us, "tokens_per_s": n_tok / (2 * us * 1e-6),
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": bytes_per, "kernel_us": us},

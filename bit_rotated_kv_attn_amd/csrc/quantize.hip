@@ -705,6 +705,96 @@ __device__ __forceinline__ void rotate_blocks(const uint8_t* fl, const uint4 (&x
   }
 }
 
+// Exact pass over the tokens t_begin .. t_end - 1 of one block (KV head g)
+// that its fast pass marked: each wave scans its share of them for the mark
+// and recomputes the marked ones sixteen at a time (one column block), with
+// R's A operands in frag and R row-major in rt.
+constexpr int kScanPerLane = 8;   // tokens each lane tests per scan step
+template <int NG>
+__device__ __forceinline__ void exact_pass(int kind, const uint16_t* __restrict__ x, int64_t n_src, int64_t tok_stride,
+                                           int64_t head_stride, const int32_t* __restrict__ src_idx, int n_kv,
+                                           float tau, float nr, const int32_t* __restrict__ dst_slot,
+                                           uint8_t* __restrict__ codes, uint32_t* __restrict__ sz, int64_t n_pages,
+                                           const uint8_t* frag, const float* rt, int g, int64_t t_begin,
+                                           int64_t t_end, int lane, int wave) {
+  const int n = lane & 15, q = lane >> 4;
+  const bool k_layout = kind_is_k(kind);
+  // a batch: lane (n, q) takes the queued token (source row qs, slot qd) when n < count
+  auto batch = [&](int64_t qs, int64_t qd, int count) {
+    const int64_t src = n < count ? qs : -1, slot = n < count ? qd : -1;
+    uint4 xq[1][4];
+    if (src < 0) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) xq[0][kb] = make_uint4(0, 0, 0, 0);
+    } else {
+      const uint4* p = reinterpret_cast<const uint4*>(x + src * tok_stride + (int64_t)g * head_stride + 8 * q);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) xq[0][kb] = p[4 * kb];
+    }
+    v4f_t y[1][8];
+    rotate_blocks<1>(frag + 16 * lane, xq, y);
+    mfma_token<NG, true>(y[0], xq[0], slot, q, g, n_kv, tau, nr, rt, codes, sz, k_layout);
+  };
+
+  // the queue: lanes n < qn (all four of each) hold a marked token's source row and slot
+  int64_t qs = -1, qd = -1;
+  int qn = 0;
+  constexpr int kStep = kWave * kScanPerLane;
+  for (int64_t base = t_begin + (int64_t)wave * kStep; base < t_end; base += (int64_t)kMWaves * kStep) {
+    // all loads of the step in flight together: indices clamped into range, results masked
+    bool marked[kScanPerLane];
+    int64_t slot_k[kScanPerLane], src_k[kScanPerLane];
+#pragma unroll
+    for (int k = 0; k < kScanPerLane; ++k) {
+      const int64_t t = base + k * kWave + lane;
+      const int64_t tc = t < t_end ? t : t_begin;
+      const int64_t sr = src_idx ? (int64_t)src_idx[tc] : tc;
+      const int64_t d = dst_slot[tc];
+      const bool ok = t < t_end && sr >= 0 && sr < n_src && d >= 0 && d < n_pages * kPage;
+      slot_k[k] = ok ? d : 0;
+      src_k[k] = sr;
+      marked[k] = ok;
+    }
+#pragma unroll
+    for (int k = 0; k < kScanPerLane; ++k) {
+      const int64_t page = slot_k[k] / kPage;
+      const uint32_t v = sz[((page * n_kv + g) * NG) * kPage + slot_k[k] % kPage];
+      marked[k] = marked[k] && v == kUnsureMark;
+    }
+    uint32_t mbits = 0;
+#pragma unroll
+    for (int k = 0; k < kScanPerLane; ++k) mbits |= (marked[k] ? 1u : 0u) << k;
+#pragma unroll 1
+    for (int k = 0; k < kScanPerLane; ++k) {   // rolled: one copy of the batch below
+      uint64_t mask = __ballot((mbits >> k) & 1u);
+      int64_t sk = src_k[0], dk = slot_k[0];
+#pragma unroll
+      for (int kk = 1; kk < kScanPerLane; ++kk)
+        if (k == kk) {
+          sk = src_k[kk];
+          dk = slot_k[kk];
+        }
+      while (mask) {   // wave-uniform
+        const int l = __builtin_ctzll(mask);
+        mask &= mask - 1;
+        const int64_t sl = ((int64_t)__builtin_amdgcn_readlane((int)(sk >> 32), l) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)sk, l);
+        const int64_t dl = ((int64_t)__builtin_amdgcn_readlane((int)(dk >> 32), l) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)dk, l);
+        if (n == qn) {
+          qs = sl;
+          qd = dl;
+        }
+        if (++qn == 16) {
+          batch(qs, qd, 16);
+          qn = 0;
+        }
+      }
+    }
+  }
+  if (qn > 0) batch(qs, qd, qn);
+}
+
 // Fast pass.  Block: one KV head and tiles_per_block consecutive 32-token
 // tiles; wave w takes tiles w, w + 8, ... of them.
 template <int NG>
@@ -799,36 +889,17 @@ __global__ __launch_bounds__(kMThreads, 1) void quantize_mfma_kernel(
       slot_n[tb] = slot_f[tb];
     }
   }
-}
 
-// Exact pass over the tokens the fast pass marked, on the same grid: each
-// wave scans its share of the block's tokens for the mark and recomputes the
-// marked ones sixteen at a time (one column block), with R^T in LDS for the
-// exact channels.
-constexpr int kScanPerLane = 8;   // tokens each lane tests per scan step
-template <int NG>
-__global__ __launch_bounds__(kMThreads, 1) void quantize_exact_kernel(
-    int kind, const uint16_t* __restrict__ x, int64_t n_src, int64_t tok_stride, int64_t head_stride,
-    const int32_t* __restrict__ src_idx, int64_t n_tok, int n_kv, const float* __restrict__ rot, float clip,
-    const int32_t* __restrict__ dst_slot, uint8_t* __restrict__ codes, uint32_t* __restrict__ sz,
-    int64_t n_pages, int tiles_per_block) {
-  constexpr int D = 128;
-  __shared__ __attribute__((aligned(16))) uint8_t frag[3 * 32 * kFragBytes];
-  __shared__ __attribute__((aligned(16))) float rt[D * D];   // R, row-major
-  const int g = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-  const int n = lane & 15, q = lane >> 4;
-  const bool k_layout = kind_is_k(kind);
-  const int64_t n_tiles = (n_tok + 31) / 32;
-  const int64_t tile0 = (int64_t)blockIdx.x * tiles_per_block;
-  // block-uniform; with no pages nothing was written (and the clamped scan below reads slot 0)
-  if (tile0 >= n_tiles || n_pages <= 0) return;
-  const int64_t t_begin = tile0 * 32, t_end = min((tile0 + (int64_t)tiles_per_block) * 32, n_tok);
-  const float* R = rot + (size_t)g * D * D;
-  const float nr = max_column_norm(R, rt, tid, lane, wave);
-  build_fragments(R, frag, tid);
+  // ---- the exact pass over this block's marked tokens, as soon as its own
+  // fast pass is done (other blocks may still be in theirs): the barrier
+  // makes every wave's marks visible to the block and frees ystash, which
+  // then holds R row-major for the exact channels
+  if (n_pages <= 0) return;   // block-uniform: nothing was written
+  __syncthreads();
+  float* rt = reinterpret_cast<float*>(&ystash[0][0][0]);
+  static_assert(sizeof(ystash) >= 128 * 128 * sizeof(float), "R must fit where the stash was");
   {
-    constexpr int kPer = D * D / 4 / kMThreads;
+    constexpr int kPer = 128 * 128 / 4 / kMThreads;
     float4 r4[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) r4[k] = reinterpret_cast<const float4*>(R)[tid + k * kMThreads];
@@ -836,82 +907,8 @@ __global__ __launch_bounds__(kMThreads, 1) void quantize_exact_kernel(
     for (int k = 0; k < kPer; ++k) reinterpret_cast<float4*>(rt)[tid + k * kMThreads] = r4[k];
   }
   __syncthreads();
-  const float tau = clip;
-
-  // a batch: lane (n, q) takes the queued token (source row qs, slot qd) when n < count
-  auto batch = [&](int64_t qs, int64_t qd, int count) {
-    const int64_t src = n < count ? qs : -1, slot = n < count ? qd : -1;
-    uint4 xq[1][4];
-    if (src < 0) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) xq[0][kb] = make_uint4(0, 0, 0, 0);
-    } else {
-      const uint4* p = reinterpret_cast<const uint4*>(x + src * tok_stride + (int64_t)g * head_stride + 8 * q);
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) xq[0][kb] = p[4 * kb];
-    }
-    v4f_t y[1][8];
-    rotate_blocks<1>(frag + 16 * lane, xq, y);
-    mfma_token<NG, true>(y[0], xq[0], slot, q, g, n_kv, tau, nr, rt, codes, sz, k_layout);
-  };
-
-  // the queue: lanes n < qn (all four of each) hold a marked token's source row and slot
-  int64_t qs = -1, qd = -1;
-  int qn = 0;
-  constexpr int kStep = kWave * kScanPerLane;
-  for (int64_t base = t_begin + (int64_t)wave * kStep; base < t_end; base += (int64_t)kMWaves * kStep) {
-    // all loads of the step in flight together: indices clamped into range, results masked
-    bool marked[kScanPerLane];
-    int64_t slot_k[kScanPerLane], src_k[kScanPerLane];
-#pragma unroll
-    for (int k = 0; k < kScanPerLane; ++k) {
-      const int64_t t = base + k * kWave + lane;
-      const int64_t tc = t < t_end ? t : t_begin;
-      const int64_t sr = src_idx ? (int64_t)src_idx[tc] : tc;
-      const int64_t d = dst_slot[tc];
-      const bool ok = t < t_end && sr >= 0 && sr < n_src && d >= 0 && d < n_pages * kPage;
-      slot_k[k] = ok ? d : 0;
-      src_k[k] = sr;
-      marked[k] = ok;
-    }
-#pragma unroll
-    for (int k = 0; k < kScanPerLane; ++k) {
-      const int64_t page = slot_k[k] / kPage;
-      const uint32_t v = sz[((page * n_kv + g) * NG) * kPage + slot_k[k] % kPage];
-      marked[k] = marked[k] && v == kUnsureMark;
-    }
-    uint32_t mbits = 0;
-#pragma unroll
-    for (int k = 0; k < kScanPerLane; ++k) mbits |= (marked[k] ? 1u : 0u) << k;
-#pragma unroll 1
-    for (int k = 0; k < kScanPerLane; ++k) {   // rolled: one copy of the batch below
-      uint64_t mask = __ballot((mbits >> k) & 1u);
-      int64_t sk = src_k[0], dk = slot_k[0];
-#pragma unroll
-      for (int kk = 1; kk < kScanPerLane; ++kk)
-        if (k == kk) {
-          sk = src_k[kk];
-          dk = slot_k[kk];
-        }
-      while (mask) {   // wave-uniform
-        const int l = __builtin_ctzll(mask);
-        mask &= mask - 1;
-        const int64_t sl = ((int64_t)__builtin_amdgcn_readlane((int)(sk >> 32), l) << 32) |
-                           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)sk, l);
-        const int64_t dl = ((int64_t)__builtin_amdgcn_readlane((int)(dk >> 32), l) << 32) |
-                           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)dk, l);
-        if (n == qn) {
-          qs = sl;
-          qd = dl;
-        }
-        if (++qn == 16) {
-          batch(qs, qd, 16);
-          qn = 0;
-        }
-      }
-    }
-  }
-  if (qn > 0) batch(qs, qd, qn);
+  exact_pass<NG>(kind, x, n_src, tok_stride, head_stride, src_idx, n_kv, tau, nr, dst_slot, codes, sz, n_pages,
+                 frag, rt, g, tile0 * 32, min(tile_end * 32, n_tok), lane, wave);
 }
 
 // Few tokens (the steady-state step demotes one token per request): one block
@@ -960,23 +957,14 @@ hipError_t launch_quantize_pack(int kind, const uint16_t* x, int64_t n_src, int6
       quantize_mfma_kernel<4><<<fgrid, kMThreads, 0, stream>>>(kind, x, n_src, tok_stride, head_stride, src_idx,
                                                               n_tok, n_kv, rot, clip, dst_slot, codes, sz,
                                                               n_pages, (int)tiles);
-      quantize_exact_kernel<4><<<fgrid, kMThreads, 0, stream>>>(kind, x, n_src, tok_stride, head_stride, src_idx,
-                                                               n_tok, n_kv, rot, clip, dst_slot, codes, sz,
-                                                               n_pages, (int)tiles);
     } else if (kind_groups(kind, d) == 2) {
       quantize_mfma_kernel<2><<<fgrid, kMThreads, 0, stream>>>(kind, x, n_src, tok_stride, head_stride, src_idx,
                                                               n_tok, n_kv, rot, clip, dst_slot, codes, sz,
                                                               n_pages, (int)tiles);
-      quantize_exact_kernel<2><<<fgrid, kMThreads, 0, stream>>>(kind, x, n_src, tok_stride, head_stride, src_idx,
-                                                               n_tok, n_kv, rot, clip, dst_slot, codes, sz,
-                                                               n_pages, (int)tiles);
     } else {
       quantize_mfma_kernel<1><<<fgrid, kMThreads, 0, stream>>>(kind, x, n_src, tok_stride, head_stride, src_idx,
                                                               n_tok, n_kv, rot, clip, dst_slot, codes, sz,
                                                               n_pages, (int)tiles);
-      quantize_exact_kernel<1><<<fgrid, kMThreads, 0, stream>>>(kind, x, n_src, tok_stride, head_stride, src_idx,
-                                                               n_tok, n_kv, rot, clip, dst_slot, codes, sz,
-                                                               n_pages, (int)tiles);
     }
     return hipGetLastError();
   }
