@@ -64,7 +64,8 @@ constexpr int kBf16WaveTokens = 16;       // tokens of a BF16 chunk per wave (4 
 
 struct DecodeDev {
   int B, Hq, n_kv, G, NB, sink_cap, recent_cap, max_hist_len, max_pages;
-  int splits, pps, chunks, sink_chunks, bf_blocks;   // bf_blocks: BF16 blocks per unit (one per chunk)
+  // bf_blocks: BF16 blocks (and partials) per unit, each taking bf_cpb consecutive chunks
+  int splits, pps, chunks, sink_chunks, bf_blocks, bf_cpb;
   // shared-prefix packing (G = 4 only): the first n_pref splits lie inside the
   // prefix and are read once for each of the `packs` packs of `pack` requests
   // (requests pack*i .. pack*i + pack - 1; pack = 2 or 4); the requests past the
@@ -1297,45 +1298,49 @@ __global__ __launch_bounds__(kBlock, (scan_waves_per_simd<G, LM, NG, PACK>())) v
   bool poison = false;
 
   if (id >= n_hist) {
-    // ---- BF16 sink / recent chunk (block-uniform), after every history block:
-    // one chunk per block, 16 tokens per wave.  Spread this thin, a block's
-    // loads stay small next to the history block that shares its CU.
+    // ---- BF16 sink / recent chunks (block-uniform), after every history block:
+    // bf_cpb consecutive chunks per block, 16 tokens of each per wave.  With
+    // one chunk per block, spread this thin, a block's loads stay small next
+    // to the history block that shares its CU; with many units, a block takes
+    // all of its unit's chunks, so the launch's tail has fewer, fuller blocks.
     const int cid = id - n_hist;
-    const int unit = cid % units, c = cid / units;
+    const int unit = cid % units, bc = cid / units;
     const int b = unit / p.n_kv, g = unit % p.n_kv;
     WaveAcc<D, G> st;
     acc_init(st);
-    const uint16_t *kb, *vb;
-    int nv;
-    if (c < p.sink_chunks) {
-      int sl = p.sink_len[b];
-      if (sl < 0 || sl > p.sink_cap) {
-        poison = true;
-        sl = 0;
-      }
-      const int t0 = c * kPage + kBf16WaveTokens * wave;
-      nv = min(kBf16WaveTokens, sl - t0);
-      const size_t off = (((size_t)b * p.n_kv + g) * p.sink_cap + t0) * D;
-      kb = p.sink_k + off;
-      vb = p.sink_v + off;
-    } else {
-      int rl = p.recent_len[b];
-      if (rl < 0 || rl > p.recent_cap) {
-        poison = true;
-        rl = 0;
-      }
-      const int t0 = (c - p.sink_chunks) * kPage + kBf16WaveTokens * wave;
-      nv = min(kBf16WaveTokens, rl - t0);
-      const size_t off = (((size_t)b * p.n_kv + g) * p.recent_cap + t0) * D;
-      kb = p.recent_k + off;
-      vb = p.recent_v + off;
+    int sl = p.sink_len[b], rl = p.recent_len[b];
+    if (sl < 0 || sl > p.sink_cap) {
+      poison = true;
+      sl = 0;
     }
-    if (nv > 0) {
-      bf16x8 qa[D / 32];
-      bf16_q_operands<D, G>(qa, p.q + ((size_t)b * p.Hq + g * G) * D, lane);
-      Bf16Tile<D> tile;
-      bf16_load<D>(tile, kb, vb, nv, lane);
-      bf16_compute<D, G>(st, tile, qa, p.sm_log2, nv, smem + wave * bf16_lds_bytes<D, G>(), lane);
+    if (rl < 0 || rl > p.recent_cap) {
+      poison = true;
+      rl = 0;
+    }
+    bf16x8 qa[D / 32];
+    bf16_q_operands<D, G>(qa, p.q + ((size_t)b * p.Hq + g * G) * D, lane);
+    const int c_end = min(p.chunks, (bc + 1) * p.bf_cpb);
+    for (int c = bc * p.bf_cpb; c < c_end; ++c) {   // block-uniform
+      const uint16_t *kb, *vb;
+      int nv;
+      if (c < p.sink_chunks) {
+        const int t0 = c * kPage + kBf16WaveTokens * wave;
+        nv = min(kBf16WaveTokens, sl - t0);
+        const size_t off = (((size_t)b * p.n_kv + g) * p.sink_cap + t0) * D;
+        kb = p.sink_k + off;
+        vb = p.sink_v + off;
+      } else {
+        const int t0 = (c - p.sink_chunks) * kPage + kBf16WaveTokens * wave;
+        nv = min(kBf16WaveTokens, rl - t0);
+        const size_t off = (((size_t)b * p.n_kv + g) * p.recent_cap + t0) * D;
+        kb = p.recent_k + off;
+        vb = p.recent_v + off;
+      }
+      if (nv > 0) {
+        Bf16Tile<D> tile;
+        bf16_load<D>(tile, kb, vb, nv, lane);
+        bf16_compute<D, G>(st, tile, qa, p.sm_log2, nv, smem + wave * bf16_lds_bytes<D, G>(), lane);
+      }
     }
     __syncthreads();   // the merge slots overlay the tiles' LDS
     float* mrg = reinterpret_cast<float*>(smem);
@@ -1343,7 +1348,7 @@ __global__ __launch_bounds__(kBlock, (scan_waves_per_simd<G, LM, NG, PACK>())) v
     if (lane == 0) flags[wave] = poison ? 1 : 0;
     __syncthreads();
     combine_block<G, D>(mrg, G * part_row(D), flags,
-                        p.bpart + (((size_t)b * p.n_kv + g) * p.chunks + c) * (size_t)G * part_row(D), tid);
+                        p.bpart + (((size_t)b * p.n_kv + g) * p.bf_blocks + bc) * (size_t)G * part_row(D), tid);
     return;
   }
 
@@ -1660,8 +1665,8 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(DecodeDev p, int n_merge,
   const int tid = threadIdx.x;
   const size_t stride = (size_t)p.G * part_row(D);
   const float* hp = p.hpart + ((size_t)b * p.n_kv + g) * p.splits * stride + (size_t)kh * part_row(D);
-  const float* bp = p.bpart + ((size_t)b * p.n_kv + g) * p.chunks * stride + (size_t)kh * part_row(D);
-  const int n = p.splits, nt = p.splits + p.chunks;
+  const float* bp = p.bpart + ((size_t)b * p.n_kv + g) * p.bf_blocks * stride + (size_t)kh * part_row(D);
+  const int n = p.splits, nt = p.splits + p.bf_blocks;
   RV rv;
   load_rv_rows<D, NR>(rv, p.r_v + ((size_t)g * D + (size_t)half * NR) * D, tid);
   const float2 ML = merge_head<D>(
@@ -1703,9 +1708,9 @@ __global__ __launch_bounds__(kBlock) void merge_unit_kernel(DecodeDev p, int n_m
   RvRows<D, D> rv;
   load_rv_rows<D, D>(rv, p.r_v + (size_t)g * D * D, tid);
   const size_t stride = (size_t)G * R;
-  const int n = p.splits, nt = p.splits + p.chunks;
+  const int n = p.splits, nt = p.splits + p.bf_blocks;
   const float* hb = p.hpart + (size_t)unit * n * stride;
-  const float* bb = p.bpart + (size_t)unit * p.chunks * stride;
+  const float* bb = p.bpart + (size_t)unit * p.bf_blocks * stride;
   if (tid < G * QPR) {
     const int h = tid / QPR, q = tid % QPR;
     float M = -INFINITY, L = 0.0f;
@@ -1772,7 +1777,7 @@ template <int D>
 bool launch_merge_unit(const DecodeDev& dv, unsigned n_dem, const DemoteDev& mk, const DemoteDev& mv,
                        hipStream_t stream) {
   // one round, or several when the batch gives every compute unit a block of its own
-  const int parts = dv.splits + dv.chunks;
+  const int parts = dv.splits + dv.bf_blocks;
   if (dv.G * (D / 4) > kBlock || parts > kUnitMaxParts) return false;
   if (parts > kUnitRound && (long)dv.B * dv.n_kv < 128) return false;
   const int units = dv.B * dv.n_kv;
@@ -1962,7 +1967,9 @@ DecodeDev make_dev(const oscar_decode_args& a, const DecodePlan& plan, char* ws)
   dv.max_hist_len = a.max_hist_len; dv.max_pages = a.max_pages;
   dv.splits = plan.splits; dv.pps = plan.pages_per_split;
   dv.chunks = plan.chunks; dv.sink_chunks = plan.sink_chunks;
-  dv.bf_blocks = plan.chunks;
+  // with many units a BF16 block takes all of its unit's chunks, else one
+  dv.bf_cpb = (long)a.batch * a.n_kv_heads >= 128 && plan.chunks > 0 ? plan.chunks : 1;
+  dv.bf_blocks = (plan.chunks + dv.bf_cpb - 1) / dv.bf_cpb;
   dv.lm = a.codebook == OSCAR_CODEBOOK_LLOYD_MAX ? 1 : 0;
   dv.ng = decode_groups(a);
   // pack the splits that lie wholly inside a shared prefix (group size 4, two or
