@@ -212,7 +212,10 @@ inline DecodePlan make_decode_plan(int B, int Hq, int n_kv, int d, int max_hist_
     long s0 = (target + units - 1) / units;
     const long s_min = (p.hist_pages + max_pps - 1) / max_pps;
     if (s0 < s_min) s0 = s_min;
-    if (quad_prefix && s0 < pack_min_splits(B, n_kv, p.chunks, resident)) s0 = pack_min_splits(B, n_kv, p.chunks, resident);
+    if (quad_prefix) {
+      const long s_pack = pack_min_splits(B, n_kv, p.chunks, resident);
+      if (s0 < s_pack) s0 = s_pack;
+    }
     if (s0 > p.hist_pages) s0 = p.hist_pages;
     p.pages_per_split = (int)((p.hist_pages + s0 - 1) / s0);
     p.splits = (p.hist_pages + p.pages_per_split - 1) / p.pages_per_split;
