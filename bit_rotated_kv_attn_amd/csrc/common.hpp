@@ -150,8 +150,8 @@ constexpr int kResidentBlocks = OSCAR_RESIDENT_BLOCKS;
 // per CU; a variant holds at most OSCAR_SCAN_WAVES_PER_SIMD): the workspace
 // query plans with it, so its splits and workspace bound every launch's
 constexpr long kMaxResidentBlocks = (long)kResidentBlocks * OSCAR_SCAN_WAVES_PER_SIMD / 2;
-// at most 64 pages per wave (one page id per lane), which also keeps the int32
-// PV accumulators far from overflow
+// at most 64 pages per wave (one page id per lane), which also bounds the
+// rounding of the fp32 PV sums a wave accumulates
 constexpr int kMaxPagesPerSplit = 4 * 64;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }

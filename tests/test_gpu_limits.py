@@ -1,14 +1,15 @@
-"""The integer history path at its design limits.
+"""The history path at its design limits.
 
 With 88 (request, KV head) units and 256 history pages, the split policy
 gives one split of 256 pages per unit, so every history wave scans the
-maximum of 64 pages.  The cache is built so that the int32 PV accumulators
-are never folded and grow as large as the design allows: every V code is 2
-or 3 (the largest operands), the V scales are equal (no scale-driven
+maximum of 64 pages.  The cache is built so that no rescale ever fires and
+the PV operands and sums grow as large as the design allows: every V code is
+2 or 3 (the largest operands), the V scales are equal (no scale-driven
 rescale), and from the second page on every logit sits 11.5 log2-units above
 the first page's maximum, just under the lazy-rescale threshold of 12, so
-every weight is near the top of its 30-bit fixed point.  The oracle's fp64
-attention over the same cache is the reference."""
+every weight p*scale_V*kap is near the 2^14 top of its fp16 pair and the
+fp32 sums run over 4096 such tokens unscaled.  The oracle's fp64 attention
+over the same cache is the reference."""
 import numpy as np
 import pytest
 
