@@ -412,13 +412,27 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 
 // address = scalar base + 32-bit lane offset (the global SADDR form).  No
 // instruction offset: on these copies it also moves the LDS destination.
+// STREAM marks the copy non-temporal (nt).  The per-request splits use it;
+// pack and cascade blocks, whose prefix pages several packs read, keep the
+// default cache policy.
+template <bool STREAM>
 __device__ __forceinline__ void copy16_to_lds(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
-               : "memory");
+  if constexpr (STREAM)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "s"(lds_base)
+                 : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
+                 : "memory");
 }
 
+template <bool STREAM>
 __device__ __forceinline__ void copy4_to_lds(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base) : "memory");
+  if constexpr (STREAM)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1 nt" ::"v"(voff), "s"(sbase), "s"(lds_base)
+                 : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
+                 : "memory");
 }
 
 // s_waitcnt immediate for vmcnt(0) with expcnt / lgkmcnt left at their maxima
@@ -478,7 +492,7 @@ __device__ __forceinline__ StageOffsets stage_offsets(int lane) {
 // blk (the (page, head) block index) is wave-uniform, so the block addresses
 // stay in scalar registers; the second K / V copies of d = 128 differ only in
 // their lane offsets
-template <int D, int NG>
+template <int D, int NG, bool STREAM>
 __device__ __forceinline__ void stage_page(const DecodeDev& p, size_t blk, uint32_t stage_lds, StageOffsets o) {
   using S = Stage<D, NG>;
   // the stage address is wave-uniform (ring base and slot index); say so, so that
@@ -486,14 +500,14 @@ __device__ __forceinline__ void stage_page(const DecodeDev& p, size_t blk, uint3
   stage_lds = __builtin_amdgcn_readfirstlane(stage_lds);
   const uint8_t* kb = p.k_codes + blk * (16 * D);
   const uint8_t* vb = p.v_codes + blk * (16 * D);
-  copy16_to_lds(kb, o.k, stage_lds + S::kK);
-  if constexpr (D == 128) copy16_to_lds(kb, o.k + 16, stage_lds + S::kK + 1024);
-  copy16_to_lds(vb, o.v, stage_lds + S::kV);
-  if constexpr (D == 128) copy16_to_lds(vb, o.v + 16 * kPage, stage_lds + S::kV + 1024);
+  copy16_to_lds<STREAM>(kb, o.k, stage_lds + S::kK);
+  if constexpr (D == 128) copy16_to_lds<STREAM>(kb, o.k + 16, stage_lds + S::kK + 1024);
+  copy16_to_lds<STREAM>(vb, o.v, stage_lds + S::kV);
+  if constexpr (D == 128) copy16_to_lds<STREAM>(vb, o.v + 16 * kPage, stage_lds + S::kV + 1024);
 #pragma unroll
   for (int j = 0; j < NG; ++j) {
-    copy4_to_lds(p.k_sz + (blk * NG + j) * kPage, o.sz, stage_lds + S::kKsz + 256 * j);
-    copy4_to_lds(p.v_sz + (blk * NG + j) * kPage, o.sz, stage_lds + S::kVsz + 256 * j);
+    copy4_to_lds<STREAM>(p.k_sz + (blk * NG + j) * kPage, o.sz, stage_lds + S::kKsz + 256 * j);
+    copy4_to_lds<STREAM>(p.v_sz + (blk * NG + j) * kPage, o.sz, stage_lds + S::kVsz + 256 * j);
   }
 }
 
@@ -507,16 +521,16 @@ __device__ __forceinline__ void stage_page_part(const DecodeDev& p, size_t blk, 
   stage_lds = __builtin_amdgcn_readfirstlane(stage_lds);
   if (part == 0) {
     const uint8_t* kb = p.k_codes + blk * (16 * D);
-    copy16_to_lds(kb, o.k, stage_lds + S::kK);
-    if constexpr (D == 128) copy16_to_lds(kb, o.k + 16, stage_lds + S::kK + 1024);
+    copy16_to_lds<false>(kb, o.k, stage_lds + S::kK);
+    if constexpr (D == 128) copy16_to_lds<false>(kb, o.k + 16, stage_lds + S::kK + 1024);
   } else if (part == 1) {
     const uint8_t* vb = p.v_codes + blk * (16 * D);
-    copy16_to_lds(vb, o.v, stage_lds + S::kV);
-    if constexpr (D == 128) copy16_to_lds(vb, o.v + 16 * kPage, stage_lds + S::kV + 1024);
+    copy16_to_lds<false>(vb, o.v, stage_lds + S::kV);
+    if constexpr (D == 128) copy16_to_lds<false>(vb, o.v + 16 * kPage, stage_lds + S::kV + 1024);
   } else if (part == 2) {
-    copy4_to_lds(p.k_sz + blk * kPage, o.sz, stage_lds + S::kKsz);
+    copy4_to_lds<false>(p.k_sz + blk * kPage, o.sz, stage_lds + S::kKsz);
   } else {
-    copy4_to_lds(p.v_sz + blk * kPage, o.sz, stage_lds + S::kVsz);
+    copy4_to_lds<false>(p.v_sz + blk * kPage, o.sz, stage_lds + S::kVsz);
   }
 }
 
@@ -670,7 +684,7 @@ __device__ __forceinline__ uint32_t pack_rtz(float a, float b) {   // two fp16, 
 // block barrier per page makes the page visible to all; own_planes are the
 // wave's weight planes.  A wave with compute false only stages and keeps step.
 // The fold into mw follows a last block barrier (mw may overlay the ring).
-template <int D, int G, bool LM, int NG, bool CASC = false>
+template <int D, int G, bool LM, int NG, bool CASC = false, bool STREAM = false>
 __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begin, int count, int hl, int pid_lane,
                                           const HistOperands<D, G>& qo, uint8_t* ring, float* mw, bool& poison,
                                           int lane, uint8_t* own_planes = nullptr, int wave = 0, bool compute = true) {
@@ -749,7 +763,7 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
   if constexpr (CASC) {
     if (count > 0) stage_page_part<D>(p, page_blk(0), ring_lds, soff, wave);
   } else {
-    for (int i = 0; i < pre; ++i) stage_page<D, NG>(p, page_blk(i), ring_lds + i * S::kBytes, soff);
+    for (int i = 0; i < pre; ++i) stage_page<D, NG, STREAM>(p, page_blk(i), ring_lds + i * S::kBytes, soff);
   }
   int slot_use = 0, slot_fill = pre;   // ring slots of page i and of page i + NS - 1
 
@@ -779,7 +793,7 @@ __device__ __forceinline__ void hist_wave(const DecodeDev& p, int g, int pg_begi
       if (!compute) continue;
     } else {
       if (i + NS - 1 < count) {
-        stage_page<D, NG>(p, page_blk(i + NS - 1), ring_lds + slot_fill * S::kBytes, soff);
+        stage_page<D, NG, STREAM>(p, page_blk(i + NS - 1), ring_lds + slot_fill * S::kBytes, soff);
         slot_fill = slot_fill == NS - 1 ? 0 : slot_fill + 1;
       }
       wait_page<S::kCopies, NS - 1>(count - 1 - i);
@@ -1500,7 +1514,8 @@ __global__ __launch_bounds__(kBlock, (scan_waves_per_simd<G, LM, NG, PACK>())) v
   const int count = max(0, min(ws0 + per_wave, pe) - ws0);
   uint8_t* ring = smem + wave * RG::kWaveBytes;
   // the wave's merge slot [G][D+2] = (m, l, acc) overlays its own ring once the scan is done
-  hist_wave<D, G, LM, NG>(p, g, ws0, count, hl, pid_lane, qo, ring, reinterpret_cast<float*>(ring), poison, lane);
+  hist_wave<D, G, LM, NG, false, true>(p, g, ws0, count, hl, pid_lane, qo, ring, reinterpret_cast<float*>(ring), poison,
+                                       lane);
   if (lane == 0) flags[wave] = poison ? 1 : 0;
   __syncthreads();
   combine_block<G, D>(reinterpret_cast<const float*>(smem), RG::kWaveBytes / 4, flags,
