@@ -225,6 +225,12 @@ __device__ __forceinline__ void bf16_q_operands(bf16x8* qa, const uint16_t* __re
   }
 }
 
+// a 16-byte non-temporal load: BF16 window and comparator tiles are read once
+__device__ __forceinline__ uint4 ld_nt16(const uint16_t* ptr) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Tokens at or past nv are neither read nor used.
 template <int D>
 __device__ __forceinline__ void bf16_load(Bf16Tile<D>& t, const uint16_t* __restrict__ kbase,
@@ -235,13 +241,13 @@ __device__ __forceinline__ void bf16_load(Bf16Tile<D>& t, const uint16_t* __rest
     const int tok = 16 * tb + r;
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk)
-      t.k[tb][kk] = tok < nv ? *reinterpret_cast<const uint4*>(kbase + (size_t)tok * D + 32 * kk + 8 * kg)
+      t.k[tb][kk] = tok < nv ? ld_nt16(kbase + (size_t)tok * D + 32 * kk + 8 * kg)
                              : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
   for (int j = 0; j < D / 8; ++j) {
     const int ch = lane + kWave * j, tok = ch / (D / 8);
-    t.v[j] = tok < nv ? *reinterpret_cast<const uint4*>(vbase + (size_t)tok * D + 8 * (ch % (D / 8)))
+    t.v[j] = tok < nv ? ld_nt16(vbase + (size_t)tok * D + 8 * (ch % (D / 8)))
                       : make_uint4(0, 0, 0, 0);
   }
 }
