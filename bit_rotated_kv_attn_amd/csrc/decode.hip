@@ -225,14 +225,21 @@ __device__ __forceinline__ void bf16_q_operands(bf16x8* qa, const uint16_t* __re
   }
 }
 
-// a 16-byte non-temporal load: BF16 window and comparator tiles are read once
-__device__ __forceinline__ uint4 ld_nt16(const uint16_t* ptr) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
-  return make_uint4(v.x, v.y, v.z, v.w);
+// a 16-byte load, non-temporal when STREAM: the sink and recent windows are
+// read once per call, while the comparator's pages of a shared prefix are read
+// for every request that holds them
+template <bool STREAM>
+__device__ __forceinline__ uint4 ld16(const uint16_t* ptr) {
+  if constexpr (STREAM) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    return *reinterpret_cast<const uint4*>(ptr);
+  }
 }
 
 // Tokens at or past nv are neither read nor used.
-template <int D>
+template <int D, bool STREAM>
 __device__ __forceinline__ void bf16_load(Bf16Tile<D>& t, const uint16_t* __restrict__ kbase,
                                           const uint16_t* __restrict__ vbase, int nv, int lane) {
   const int r = lane & 15, kg = lane >> 4;
@@ -241,13 +248,13 @@ __device__ __forceinline__ void bf16_load(Bf16Tile<D>& t, const uint16_t* __rest
     const int tok = 16 * tb + r;
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk)
-      t.k[tb][kk] = tok < nv ? ld_nt16(kbase + (size_t)tok * D + 32 * kk + 8 * kg)
+      t.k[tb][kk] = tok < nv ? ld16<STREAM>(kbase + (size_t)tok * D + 32 * kk + 8 * kg)
                              : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
   for (int j = 0; j < D / 8; ++j) {
     const int ch = lane + kWave * j, tok = ch / (D / 8);
-    t.v[j] = tok < nv ? ld_nt16(vbase + (size_t)tok * D + 8 * (ch % (D / 8)))
+    t.v[j] = tok < nv ? ld16<STREAM>(vbase + (size_t)tok * D + 8 * (ch % (D / 8)))
                       : make_uint4(0, 0, 0, 0);
   }
 }
@@ -1358,7 +1365,7 @@ __global__ __launch_bounds__(kBlock, (scan_waves_per_simd<G, LM, NG, PACK>())) v
       }
       if (nv > 0) {
         Bf16Tile<D> tile;
-        bf16_load<D>(tile, kb, vb, nv, lane);
+        bf16_load<D, true>(tile, kb, vb, nv, lane);
         bf16_compute<D, G>(st, tile, qa, p.sm_log2, nv, smem + wave * bf16_lds_bytes<D, G>(), lane);
       }
     }
@@ -1856,7 +1863,7 @@ __global__ __launch_bounds__(kBlock, (G > 8 ? 1 : 2)) void bf16_paged_kernel(Bf1
     const size_t off = ((size_t)pid * p.n_kv + g) * kPage * D;
     const int nv = min(kPage, cl - pg * kPage);
     Bf16Tile<D> tile;
-    bf16_load<D>(tile, p.k_pages + off, p.v_pages + off, nv, lane);
+    bf16_load<D, false>(tile, p.k_pages + off, p.v_pages + off, nv, lane);
     bf16_compute<D, G>(st, tile, qa, p.sm_log2, nv, smem + wave * kWaveLds, lane);
   }
   __syncthreads();   // the merge area overlays the tiles' LDS
