@@ -264,7 +264,7 @@ hipError_t launch_quantize_pack(int kind, const uint16_t* x, int64_t n_src, int6
 
 // decode phases: rotate the query, scan history and BF16 windows, merge
 constexpr int kPhaseRotate = 0, kPhaseScan = 1, kPhaseMerge = 2;
-// demote_k / demote_v (or NULL): a decode step's demotions, run in the rotate phase
+// demote_k / demote_v (or NULL): a decode step's demotions, run in the merge phase
 hipError_t launch_decode_phase(int phase, const oscar_decode_args& a, const DecodePlan& plan, char* ws,
                                hipStream_t stream, const oscar_demote_args* demote_k = nullptr,
                                const oscar_demote_args* demote_v = nullptr);
