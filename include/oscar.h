@@ -242,11 +242,15 @@ OSCAR_API oscar_status oscar_decode_attn(const oscar_decode_args* args, void* wo
  * workspace must be passed to all three.
  *   oscar_decode_rotate_query  q_rot = q R_K (and its channel sum) per query head
  *   oscar_decode_scan          INT2 history split-K scan and BF16 sink/recent
- *                              tiles; one online-softmax partial per split/tile
+ *                              tiles; one online-softmax partial per history
+ *                              split and per BF16 block (a 64-token tile, or
+ *                              all of a (request, KV head)'s tiles when the
+ *                              call has 128 or more of those)
  *   oscar_decode_merge         log-sum-exp merge of the history partials, times
  *                              R_V^T, merge with the BF16 partials, normalise
  *                              (one block per query head, or per (request, KV
- *                              head) when each head has at most 16 partials)
+ *                              head) when each head has at most 16 partials, or
+ *                              at most 64 with 128 or more (request, KV head)s)
  * Same validation and status codes as oscar_decode_attn.
  */
 OSCAR_API oscar_status oscar_decode_rotate_query(const oscar_decode_args* args, void* workspace,
