@@ -1,7 +1,8 @@
 """GPU parity of oscar_decode_step: the step's K and V demotions run in the
 decode's last launch.  The decode must equal the oracle decode of the cache
 as given (the demoted slots lie past hist_len), and the demoted slots must
-equal the oracle quantiser's output for the demoted tokens."""
+equal the oracle quantiser's output for the demoted tokens, also in batches
+whose merge and demotion blocks take more than one round of resident blocks."""
 import numpy as np
 import pytest
 import torch
@@ -37,10 +38,29 @@ def _pools_with_room(cfg):
     return kc, vc, ks, vs
 
 
+# large batches: 29 x 8 and 41 x 8 (request, KV head) units (the per-unit
+# merge, 464 and 656 demotion blocks), and group size 16 (the per-head merge)
+MANY = [
+    synth.DecodeShape("step-b29-h32kv8-d128-L700", 29, 32, 8, 128, 700),
+    synth.DecodeShape("step-b41-h32kv8-d128-L520", 41, 32, 8, 128, 520),
+    synth.DecodeShape("step-b9-h128kv8-d128-L600", 9, 128, 8, 128, 600),
+]
+
+
 @pytest.mark.parametrize("groups", [0, 64, 32])
 @pytest.mark.parametrize("codebook", ["uniform", "lloyd_max"])
 @pytest.mark.parametrize("shape", SHAPES, ids=[s.name for s in SHAPES])
 def test_decode_step_matches_separate_oracle_steps(shape, codebook, groups):
+    _check_step(shape, codebook, groups)
+
+
+@pytest.mark.parametrize("codebook,groups", [("uniform", 0), ("lloyd_max", 32)])
+@pytest.mark.parametrize("shape", MANY, ids=[s.name for s in MANY])
+def test_decode_step_large_batches(shape, codebook, groups):
+    _check_step(shape, codebook, groups)
+
+
+def _check_step(shape, codebook, groups):
     cfg, slot = _with_free_slots(synth.make_decode_config(0, shape=shape, seed_index=7))
     cfg["codebook"] = codebook
     cfg["group_channels"] = groups
